@@ -1,0 +1,166 @@
+"""Benchmark: paged decode attention on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--partition P]
+
+A step is one pass of the hot path over one batch: the KV append when the
+workload has one, then paged_attention_decode (split-KV partitions plus the
+log-sum-exp merge when the workload is split).  Inputs are seeded synthetic
+tensors already resident in HBM.  Prints ONE JSON line with seq-steps/s, the
+roofline of the decode call (algorithmic bytes / event-timed duration against
+the 8 TB/s HBM peak) and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workload  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "seq-steps/s and achieved HBM GB/s (% of peak) for paged decode attention"
+DEFAULT_WORKLOAD = "llama8b_prefix_share"
+
+
+def live_slots(w):
+    """Number of distinct (physical block, slot) pairs attention reads."""
+    live = np.zeros((w.N_blocks, w.block_size), dtype=bool)
+    for b in range(w.B):
+        L = int(w.context_lens[b])
+        nfull, rem = divmod(L, w.block_size)
+        live[w.block_tables[b, :nfull], :] = True
+        if rem:
+            live[w.block_tables[b, nfull], :rem] = True
+    return int(live.sum())
+
+
+def algorithmic_bytes(w):
+    """Bytes the decode call must move (unique), and the logical KV bytes (each sequence in full)."""
+    e = w.elem_bytes
+    row = w.Hkv * w.D * e                      # one token, all KV heads, K or V
+    kv_unique = 2 * row * live_slots(w)
+    kv_logical = 2 * row * int(w.context_lens.sum())
+    qo = 2 * w.B * w.T * w.Hq * w.D * e        # q read + out written
+    tables = 4 * int(np.sum(-(-w.context_lens // w.block_size))) + 4 * w.B
+    append = 2 * 2 * w.B * w.T * row if w.lens_pre is not None else 0   # k_new+v_new read and written
+    return dict(decode=kv_unique + qo + tables, logical=kv_logical + qo + tables, append=append,
+                kv_unique=kv_unique, kv_logical=kv_logical)
+
+
+def cpu_baseline(w, budget_s):
+    """The fp64 oracle, untuned, on the first n sequences (n sized to ~budget_s of work), one BLAS thread."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    def run(n):
+        q = w.values(w.q[:n])
+        t0 = time.perf_counter()
+        oracle.paged_attention(q, w.values(w.k_pool), w.values(w.v_pool), w.block_tables[:n], w.context_lens[:n],
+                               w.scale, w.block_size)
+        return time.perf_counter() - t0
+
+    with threadpool_limits(limits=1):
+        t1 = run(1)
+        n = int(max(1, min(w.B, budget_s / max(t1, 1e-3))))
+        t = run(n)
+    return {"value": n / t, "unit": "seq-steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} of {w.B} sequences of {w.name} (fp64 NumPy, 1 BLAS thread, {t:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(workload.WORKLOADS))
+    ap.add_argument("--partition", type=int, default=None, help="split-KV partition size (tokens); 0 = single pass")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_attention_amd as pkv
+
+    t_gen = time.time()
+    w = workload.WORKLOADS[args.workload](poison=False)
+    part = w.partition_size if args.partition is None else args.partition
+    print(f"# generated {w.name} in {time.time() - t_gen:.1f}s; partition {part}", file=sys.stderr, flush=True)
+
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if w.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    q, kp, vp = up(w.q), up(w.k_pool), up(w.v_pool)
+    tables = torch.from_numpy(w.block_tables).to(dev)
+    lens = torch.from_numpy(w.context_lens).to(dev)
+    has_append = w.lens_pre is not None
+    if has_append:
+        k_new, v_new = up(w.k_new), up(w.v_new)
+        lens_pre = torch.from_numpy(w.lens_pre).to(dev)
+    out = torch.empty_like(q)
+    need = pkv.pkv_decode_workspace_bytes(w.B, w.T, w.Hq, w.D, w.max_blocks, w.block_size, part)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    scale = float(w.scale)
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    def step(i=None):
+        if has_append:
+            pkv.paged_kv_append(k_new, v_new, kp, vp, tables, lens_pre, stream=stream)
+        if i is not None:
+            ev[i][0].record(stream)
+        pkv.paged_attention_decode(q, kp, vp, tables, lens, out=out, scale=scale, partition_size=part,
+                                   workspace=ws, stream=stream)
+        if i is not None:
+            ev[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    decode_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    nb = algorithmic_bytes(w)
+    achieved = nb["decode"] / (decode_ms * 1e-3) / 1e9
+    seq_steps = w.B / (ms_step * 1e-3)
+    result = {
+        "metric": METRIC, "value": round(seq_steps, 1), "unit": "seq-steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+                   "block_size": w.block_size, "partition_size": part, "total_tokens": int(w.context_lens.sum()),
+                   "append": has_append},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "paged_attention_decode call (partition kernel + lse merge)",
+                     "bytes_per_launch": nb["decode"], "launch_ms": round(decode_ms, 5),
+                     "logical_GBps": round(nb["logical"] / (decode_ms * 1e-3) / 1e9, 1)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

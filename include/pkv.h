@@ -1,0 +1,169 @@
+/*
+ * pkv.h -- C ABI of the paged KV-cache decode-attention library (libpkv.so).
+ *
+ * One decode step of causal attention over a paged KV cache on an AMD
+ * Instinct MI355X (gfx950).  Each sequence's new query token(s) attend to
+ * every cached key/value row of that sequence.  The cache lives in a pool
+ * of fixed-size physical blocks; a per-sequence block table maps logical
+ * block i of a sequence to a physical block of the pool ("Inference From
+ * Scratch", chapter table, ch. 10 "Paged attention, block tables"; "The
+ * Project: Serve Your Own LLM", M13, mini-vLLM with a paged KV cache).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every array argument is a DEVICE pointer to dense, row-major memory
+ *    owned by the caller.  The library never allocates, frees or keeps any
+ *    caller memory.  Scalars are passed by value.
+ *  - Layouts (element type given by `dtype`):
+ *      q, out         [B, T, Hq, D]
+ *      k_pool, v_pool [N_blocks, block_size, Hkv, D]
+ *      k_new, v_new   [B, T, Hkv, D]
+ *      block_tables   int32 [B, max_blocks]
+ *      context_lens   int32 [B]
+ *      lse_out        float32 [B, T, Hq] (natural log), optional (NULL)
+ *    Logical token j of sequence b is slot j % block_size of physical block
+ *    block_tables[b][j / block_size].  Table entries past the last block a
+ *    sequence needs are never read.
+ *  - Grouped-query attention: query head h reads KV head h / (Hq / Hkv)
+ *    ("The Project", M2: MHA/GQA/MQA chosen from the KV-cache budget).
+ *  - Query token t of T sits at position L - T + t of its sequence (L =
+ *    context_lens[b], which counts the T query tokens) and attends to
+ *    positions 0 .. L - T + t: T = 1 is plain decode, T > 1 is the
+ *    speculative-decoding verify step ("LLM Inference from Scratch", M7).
+ *  - `stream` is a hipStream_t passed as void*; NULL is the null stream.
+ *    Every launch is asynchronous on that stream; no call synchronises,
+ *    except that PKV_DEBUG=1 in the environment adds a device-side check of
+ *    table entries and lengths, followed by a stream synchronisation.
+ *  - Errors: argument errors are detected on the host before any launch and
+ *    return a status; nothing is launched then.  Launch failures return
+ *    PKV_EHIP.  pkv_last_error() gives a message for the last non-OK status
+ *    of the calling thread.  No C++ exception crosses this interface.
+ *  - Device-side contract, not checked unless PKV_DEBUG=1: T <= L <=
+ *    max_blocks * block_size for every sequence and every table entry a
+ *    sequence needs lies in [0, N_blocks).  Violations read or write outside
+ *    the pool.
+ *  - Supported shapes: block_size 16; D 64 or 128; Hq a multiple of Hkv and
+ *    of 4; Hq / Hkv in {1, 2, 4, 8}; 1 <= T <= 16.  Others return
+ *    PKV_EUNSUPPORTED rather than taking a slow path.  B = 0 is a no-op.
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_EINVAL = 1,        /* bad argument (null pointer, bad size, workspace too small) */
+  PKV_EUNSUPPORTED = 2,  /* valid but outside the supported shape set */
+  PKV_EWORKSPACE = 3,    /* workspace missing or smaller than pkv_decode_workspace_bytes */
+  PKV_EHIP = 4           /* a HIP runtime call or kernel launch failed */
+} pkv_status;
+
+typedef enum {
+  PKV_FP32 = 0, /* float32 storage; accumulation in float32 */
+  PKV_BF16 = 1  /* bfloat16 storage; accumulation in float32, output rounded to nearest even */
+} pkv_dtype;
+
+/*
+ * paged_kv_append -- write this step's new key/value rows into the cache.
+ *
+ * For every sequence b and t < T the row k_new[b][t] (and v_new[b][t]) is
+ * copied to position p = context_lens_pre[b] + t, i.e. to slot p % block_size
+ * of physical block block_tables[b][p / block_size].  This is the KV-cache
+ * update of a decode step ("LLM Inference from Scratch", M1: past keys and
+ * values are kept so decode only adds the new token's rows).  Only those
+ * slots are written; the copy is exact (bytes are moved, not converted).
+ *
+ * context_lens_pre counts the tokens cached BEFORE the append; the library
+ * does not update it (the caller passes context_lens_pre + T to attention).
+ * The caller's allocator must already have put the target blocks in the
+ * table.  Two (b, t) pairs must not address the same slot.
+ */
+pkv_status paged_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                           const int32_t* block_tables, const int32_t* context_lens_pre,
+                           int B, int T, int Hkv, int D, int block_size, int max_blocks, int N_blocks,
+                           pkv_dtype dtype, void* stream);
+
+/*
+ * paged_kv_gather -- diagnostic copy of each sequence's cached rows into a
+ * contiguous buffer: out[b][j] = pool row of logical token j for j <
+ * context_lens[b], zero for context_lens[b] <= j < max_len.  out is
+ * [B, max_len, Hkv, D] for K and V each (k_out, v_out); the copy is exact.
+ * This is the block-table gather that attention performs internally, exposed
+ * so that its indexing can be checked bit for bit ("The Project", M10: a
+ * paged_gather kernel).  Requires context_lens[b] <= max_len.
+ */
+pkv_status paged_kv_gather(const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                           const int32_t* context_lens, void* k_out, void* v_out,
+                           int B, int max_len, int Hkv, int D, int block_size, int max_blocks, int N_blocks,
+                           pkv_dtype dtype, void* stream);
+
+/*
+ * pkv_decode_workspace_bytes -- bytes of device workspace paged_attention_decode
+ * needs for these sizes and this partition size (0 when partition_size == 0).
+ * The split-KV partials use B*T*Hq*P_max*(D+1) float32 values, where
+ * P_max = ceil(max_blocks * block_size / partition_size).  Returns 0 for
+ * invalid sizes.
+ */
+size_t pkv_decode_workspace_bytes(int B, int T, int Hq, int D, int max_blocks, int block_size,
+                                  int partition_size);
+
+/*
+ * paged_attention_decode -- out = softmax(scale * q K^T + causal mask) V per
+ * (sequence, query token, query head), with K and V read through the block
+ * table ("Inference From Scratch", ch. 8 online softmax / flash attention and
+ * ch. 10 paged attention; the result equals recomputing attention over the
+ * full contiguous prefix).
+ *
+ * scale is normally 1/sqrt(D).  lse_out, when not NULL, receives the natural
+ * log of the softmax denominator, log sum_j exp(scale * q.k_j).
+ *
+ * partition_size = 0 evaluates each (sequence, head group) in one pass.
+ * partition_size > 0 (a multiple of block_size) splits every sequence into
+ * partitions of that many tokens starting at position 0; each partition
+ * emits a normalised partial output and its log-sum-exp into `workspace`,
+ * and a second kernel merges them as lse_reduce does.  Sequences that fit in
+ * one partition are written straight to `out`.  After a split call, the
+ * workspace holds, for every (b, t, h) whose sequence has P_b =
+ * ceil(L / partition_size) > 1 partitions, part_out [B, T, Hq, P_max, D]
+ * float32 at offset 0 followed by part_lse [B, T, Hq, P_max] float32, valid
+ * for p < P_b; everything else in it is unspecified.  A partition with no
+ * visible token for a query row has part_lse = -inf and part_out = 0.
+ *
+ * out must not alias any input.  workspace is ignored when partition_size is 0.
+ */
+pkv_status paged_attention_decode(const void* q, const void* k_pool, const void* v_pool,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  void* out, float* lse_out,
+                                  int B, int T, int Hq, int Hkv, int D, int block_size, int max_blocks,
+                                  int N_blocks, float scale, int partition_size,
+                                  void* workspace, size_t workspace_bytes, pkv_dtype dtype, void* stream);
+
+/*
+ * lse_reduce -- merge P_max normalised partial attention results per row by
+ * their log-sum-exp ("Inference From Scratch", ch. 8: softmax pieces over
+ * disjoint key ranges combine through their running max and sum):
+ *   M = max_p lse_p,  w_p = exp(lse_p - M),
+ *   out = sum_p w_p part_out_p / sum_p w_p,  lse = M + log sum_p w_p.
+ * part_out is float32 [B, T, Hq, P_max, D], part_lse float32 [B, T, Hq, P_max];
+ * a partition with part_lse = -inf is empty and its part_out is never read.
+ * A row whose partitions are all empty gets out = 0 and lse = -inf.  The
+ * order of the sum over p is fixed, so results are deterministic.
+ * out is [B, T, Hq, D] in out_dtype; lse_out (float32 [B, T, Hq]) may be NULL.
+ */
+pkv_status lse_reduce(const float* part_out, const float* part_lse, void* out, float* lse_out,
+                      int B, int T, int Hq, int D, int P_max, pkv_dtype out_dtype, void* stream);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char* pkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

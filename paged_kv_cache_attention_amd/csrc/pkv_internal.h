@@ -1,0 +1,55 @@
+// Internal launcher interface between the C ABI (pkv_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Arguments of one paged-attention launch, already validated by the host.
+struct DecodeArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  void* out;
+  float* lse_out;
+  float* part_out;  // [B, T, Hq, P_max, D] or nullptr when not split
+  float* part_lse;  // [B, T, Hq, P_max]
+  int B, T, Hq, Hkv, D, block_size, max_blocks, N_blocks;
+  int part_tokens;  // tokens per partition (max_blocks * block_size when not split)
+  int P_max;        // partitions per sequence upper bound (1 when not split)
+  float scale;
+  bool bf16;
+};
+
+// VALU decode kernel: any T (one query token per work item), Hq/Hkv in {1,2,4,8}.
+hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
+
+// MFMA verify kernel for bf16 when T * (Hq/Hkv) == 16 (e.g. T=4 with 4 query heads per KV head).
+bool verify_mfma_supported(const DecodeArgs& a);
+hipError_t launch_verify_mfma(const DecodeArgs& a, hipStream_t stream);
+
+// Log-sum-exp merge of split partials.  When `lens` is given, rows whose
+// sequence has a single partition are skipped (the decode kernel wrote them).
+hipError_t launch_lse_reduce(const float* part_out, const float* part_lse, void* out, float* lse_out,
+                             int B, int T, int Hq, int D, int P_max, bool bf16, const int32_t* lens,
+                             int part_tokens, hipStream_t stream);
+
+hipError_t launch_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                         const int32_t* block_tables, const int32_t* lens_pre, int B, int T, int Hkv, int D,
+                         int block_size, int max_blocks, int N_blocks, int elem_bytes, hipStream_t stream);
+
+hipError_t launch_gather(const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                         const int32_t* lens, void* k_out, void* v_out, int B, int max_len, int Hkv, int D,
+                         int block_size, int max_blocks, int N_blocks, int elem_bytes, hipStream_t stream);
+
+// Device-side contract check (PKV_DEBUG): with L = lens[b] + len_add, sets
+// *bad = 1 unless T <= L <= max_blocks*block_size and every table entry of the
+// first ceil(L/block_size) blocks lies in [0, N_blocks).
+hipError_t launch_validate(const int32_t* block_tables, const int32_t* lens, int B, int T, int len_add,
+                           int block_size, int max_blocks, int N_blocks, int* bad, hipStream_t stream);
+
+}  // namespace pkv
