@@ -75,6 +75,23 @@ def cpu_baseline(w, budget_s):
             "sample": f"first {n} of {w.B} sequences of {w.name} (fp64 NumPy, 1 BLAS thread, {t:.1f} s)"}
 
 
+def copy_ceiling(torch, dev, nbytes=1 << 30, reps=20):
+    """Read+write bandwidth of a plain device copy of nbytes (torch's copy kernel)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "ms": round(ms, 4),
+            "GBps_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -84,6 +101,8 @@ def main():
     ap.add_argument("--partition", type=int, default=None, help="split-KV partition size (tokens); 0 = single pass")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="also time a plain 1 GiB device copy (torch) as the practical bandwidth reference")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -157,6 +176,8 @@ def main():
                      "bytes_per_launch": nb["decode"], "launch_ms": round(decode_ms, 5),
                      "logical_GBps": round(nb["logical"] / (decode_ms * 1e-3) / 1e9, 1)},
     }
+    if args.ceiling:
+        result["copy_ceiling"] = copy_ceiling(torch, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -125,8 +125,9 @@ def paged_attention_decode(q, k_pool, v_pool, block_tables, context_lens, out=No
                            partition_size=0, workspace=None, stream=None):
     """Attention of q [B,T,Hq,D] over the paged cache; returns out [B,T,Hq,D].
 
-    When partition_size > 0 and no workspace is given, one is allocated with
-    torch (device memory only; all computation is in the library)."""
+    When the library needs workspace (pkv_decode_workspace_bytes > 0) and none
+    is given, one is allocated with torch (device memory only; all computation
+    is in the library)."""
     torch = _torch()
     lib = load_library()
     B, T, Hq, D = q.shape
@@ -137,8 +138,8 @@ def paged_attention_decode(q, k_pool, v_pool, block_tables, context_lens, out=No
     if scale is None:
         scale = 1.0 / D ** 0.5
     need = pkv_decode_workspace_bytes(B, T, Hq, D, max_blocks, bs, partition_size)
-    if partition_size and workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.paged_attention_decode(_ptr(q), _ptr(k_pool), _ptr(v_pool), _i32(block_tables, "block_tables"),
                                       _i32(context_lens, "context_lens"), _ptr(out), _ptr(lse_out), B, T, Hq, Hkv, D,

@@ -19,7 +19,7 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 LIB = PKG / "libpkv.so"
-SOURCES = ["pkv_api.hip", "pkv_decode.hip", "pkv_verify.hip", "pkv_reduce.hip", "pkv_copy.hip"]
+SOURCES = ["pkv_api.hip", "pkv_decode.hip", "pkv_stream.hip", "pkv_verify.hip", "pkv_reduce.hip", "pkv_copy.hip"]
 ARCH = "gfx950"
 
 

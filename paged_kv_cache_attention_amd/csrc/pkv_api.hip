@@ -91,8 +91,8 @@ extern "C" {
 const char* pkv_last_error(void) { return g_last_error.c_str(); }
 
 size_t pkv_decode_workspace_bytes(int B, int T, int Hq, int D, int max_blocks, int block_size, int partition_size) {
-  if (partition_size == 0) return 0;
   if (B < 0 || T < 1 || Hq < 1 || D < 1 || max_blocks < 1 || block_size < 1 || partition_size < 0) return 0;
+  if (partition_size == 0) return pkv::stream_workspace_bytes(B, T, Hq, D);
   const unsigned long long P = (unsigned long long)partitions_max(max_blocks, block_size, partition_size);
   const unsigned long long rows = (unsigned long long)B * T * Hq;
   return (size_t)(rows * P * (unsigned long long)(D + 1) * 4ull);
@@ -160,16 +160,22 @@ pkv_status paged_attention_decode(const void* q, const void* k_pool, const void*
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out) return fail(PKV_EINVAL, "null pointer argument");
   if (out == q || out == k_pool || out == v_pool) return fail(PKV_EINVAL, "out must not alias an input");
 
-  const bool split = partition_size > 0 && partition_size < max_blocks * block_size;
   pkv::DecodeArgs a{};
   a.q = q; a.k_pool = k_pool; a.v_pool = v_pool; a.block_tables = block_tables; a.context_lens = context_lens;
   a.out = out; a.lse_out = lse_out;
   a.B = B; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.block_size = block_size; a.max_blocks = max_blocks;
   a.N_blocks = N_blocks; a.scale = scale; a.bf16 = dtype == PKV_BF16;
-  if (split) {
-    const size_t need = pkv_decode_workspace_bytes(B, T, Hq, D, max_blocks, block_size, partition_size);
-    if (!workspace || workspace_bytes < need)
-      return fail(PKV_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+  const size_t need = pkv_decode_workspace_bytes(B, T, Hq, D, max_blocks, block_size, partition_size);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(PKV_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug_enabled() && (st = debug_validate(block_tables, context_lens, B, T, 0, block_size, max_blocks, N_blocks, s)) !=
+                             PKV_OK)
+    return st;
+  const bool fixed_split = partition_size > 0 && partition_size < max_blocks * block_size;
+  if (partition_size == 0 && !pkv::verify_mfma_supported(a) && pkv::stream_supported(a))
+    return from_hip(pkv::launch_decode_stream(a, workspace, s), "paged_attention_decode launch");
+  if (fixed_split) {
     a.part_tokens = partition_size;
     a.P_max = partitions_max(max_blocks, block_size, partition_size);
     a.part_out = static_cast<float*>(workspace);
@@ -180,15 +186,11 @@ pkv_status paged_attention_decode(const void* q, const void* k_pool, const void*
   }
   if ((unsigned long long)a.P_max * T * (Hq / 4) * B > (1ull << 31) - 256)
     return fail(PKV_EINVAL, "too many work items");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (debug_enabled() && (st = debug_validate(block_tables, context_lens, B, T, 0, block_size, max_blocks, N_blocks, s)) !=
-                             PKV_OK)
-    return st;
   if (pkv::verify_mfma_supported(a))
     st = from_hip(pkv::launch_verify_mfma(a, s), "paged_attention_decode verify launch");
   else
     st = from_hip(pkv::launch_decode_valu(a, s), "paged_attention_decode launch");
-  if (st != PKV_OK || !split) return st;
+  if (st != PKV_OK || !fixed_split) return st;
   return from_hip(pkv::launch_lse_reduce(a.part_out, a.part_lse, out, lse_out, B, T, Hq, D, a.P_max, a.bf16,
                                          context_lens, partition_size, s),
                   "lse_reduce launch");

@@ -84,6 +84,11 @@ template <> __device__ __forceinline__ void chunk_widen<float>(u32x4_t v, float*
   f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y); f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
 }
 
+#ifndef PKV_PD
+#define PKV_PD 2
+#endif
+constexpr int PD = PKV_PD;   // blocks in flight per wave
+
 template <typename ET, int D, int GW, int NW>
 __global__ __launch_bounds__(64 * NW) void decode_valu_kernel(DecodeArgs a, float scale_log2e, uint32_t n_items) {
   using G = Geo<ET, D, GW, NW>;
@@ -159,32 +164,33 @@ __global__ __launch_bounds__(64 * NW) void decode_valu_kernel(DecodeArgs a, floa
 #pragma unroll
     for (int e = 0; e < G::EC; ++e) acc[g][e] = 0.f;
 
-  // Software pipeline: while block i is processed, K and V of block i+1 are in
-  // flight (V double-buffered; the loop is unrolled by two so the buffers swap
-  // roles without register copies).  The last prefetch re-reads the current
-  // block, which hits in L2, so no load is conditional.
+  // Software pipeline of depth PD: while block i is processed, K and V of
+  // blocks i+1 .. i+PD are in flight in registers.  The loop is unrolled by
+  // PD so the buffers rotate without copies; prefetches past the last block
+  // re-read the current block (an L2 hit) so no load is conditional, and the
+  // trip count is padded to a multiple of PD with fully masked steps.
   u32x4_t* ktile16 = reinterpret_cast<u32x4_t*>(ktile);
-  u32x4_t kreg[G::LOADS], vA[G::LOADS], vB[G::LOADS];
-  int tbl = 0, ph_cur = 0, cn = 0;
+  u32x4_t kbuf[PD][G::LOADS], vbuf[PD][G::LOADS];
+  int tbl = 0, cn = 0;
   auto load_block = [&](u32x4_t (&dst)[G::LOADS], const unsigned char* pool, int ph) {
     const unsigned char* base = pool + (size_t)ph * block_bytes;
 #pragma unroll
     for (int l = 0; l < G::LOADS; ++l) dst[l] = load16(base + l * load_step);
   };
-  auto body = [&](u32x4_t (&vcur)[G::LOADS], u32x4_t (&vnxt)[G::LOADS], int c0, int i) {
+  auto phys = [&](int i) { return __builtin_amdgcn_readlane(tbl, i < cn ? i : cn - 1); };
+
+  auto body = [&](u32x4_t (&kcur)[G::LOADS], u32x4_t (&vcur)[G::LOADS], int c0, int i) {
     const int kb = lo / kBS + wv + NW * (c0 + i);   // logical block
-    const int ph_next = i + 1 < cn ? __builtin_amdgcn_readlane(tbl, i + 1) : ph_cur;
-    // 1. K rows of this block -> LDS
+    const int ph_ahead = phys(i + PD);
+    // 1. K rows of this block -> LDS, then refill the slot with block i+PD
 #pragma unroll
     for (int l = 0; l < G::LOADS; ++l) {
       const int row = l * (64 / G::NC) + grp;
-      ktile16[row * G::NC + swz<G::NC, G::ROWS_PER_LINE>(c, row)] = kreg[l];
+      ktile16[row * G::NC + swz<G::NC, G::ROWS_PER_LINE>(c, row)] = kcur[l];
     }
-    // 2. prefetch K and V of the next block
-    load_block(kreg, kpool, ph_next);
-    load_block(vnxt, vpool, ph_next);
+    load_block(kcur, kpool, ph_ahead);
     lds_order();
-    // 3. scores: lane (hl, tq) dots its query row with key row tq
+    // 2. scores: lane (hl, tq) dots its query row with key row tq
     float dot = 0.f;
 #pragma unroll
     for (int cc = 0; cc < G::NC; ++cc)
@@ -210,7 +216,7 @@ __global__ __launch_bounds__(64 * NW) void decode_valu_kernel(DecodeArgs a, floa
     l_part += pr;
     pbuf[tq * kHeadsPerWave + hl] = pr;
     lds_order();
-    // 4. acc += p * V
+    // 3. acc += p * V, then refill the V slot with block i+PD
     const bool partial = (kb + 1) * kBS > hi;
 #pragma unroll
     for (int l = 0; l < G::LOADS; ++l) {
@@ -227,21 +233,21 @@ __global__ __launch_bounds__(64 * NW) void decode_valu_kernel(DecodeArgs a, floa
 #pragma unroll
         for (int e = 0; e < G::EC; ++e) acc[g][e] = fmaf(pv[g], vf[e], acc[g][e]);
     }
+    load_block(vcur, vpool, ph_ahead);
     lds_order();
-    ph_cur = ph_next;
   };
 
   for (int c0 = 0; c0 < nb; c0 += 64) {
     cn = min(64, nb - c0);
     tbl = lane < cn ? clampi(trow[NW * (c0 + lane)], 0, nmax) : 0;
-    ph_cur = __builtin_amdgcn_readfirstlane(tbl);
-    load_block(kreg, kpool, ph_cur);
-    load_block(vA, vpool, ph_cur);
-    // Pairs of blocks; an odd count ends with one pad step past the last
-    // block, whose tokens are all masked (it reads the current block again).
-    for (int i = 0; i < cn; i += 2) {
-      body(vA, vB, c0, i);
-      body(vB, vA, c0, i + 1);
+#pragma unroll
+    for (int s = 0; s < PD; ++s) {
+      load_block(kbuf[s], kpool, phys(s));
+      load_block(vbuf[s], vpool, phys(s));
+    }
+    for (int i = 0; i < cn; i += PD) {
+#pragma unroll
+      for (int s = 0; s < PD; ++s) body(kbuf[s], vbuf[s], c0, i + s);
     }
   }
 

@@ -25,6 +25,15 @@ struct DecodeArgs {
   bool bf16;
 };
 
+// Balanced persistent VALU path: a fixed grid of kStreamWaves waves splits
+// the flattened block list of all (head group, query token, sequence) units
+// evenly; pieces of units cut by wave ranges are merged by a second kernel.
+constexpr int kStreamWaves = 2048;
+constexpr int kStreamMaxTB = 8192;   // B * T limit of the planning kernel
+bool stream_supported(const DecodeArgs& a);
+size_t stream_workspace_bytes(int B, int T, int Hq, int D);
+hipError_t launch_decode_stream(const DecodeArgs& a, void* workspace, hipStream_t stream);
+
 // VALU decode kernel: any T (one query token per work item), Hq/Hkv in {1,2,4,8}.
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
 

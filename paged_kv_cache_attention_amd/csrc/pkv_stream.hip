@@ -1,0 +1,527 @@
+// Paged decode attention, balanced persistent VALU path (gfx950).
+//
+// Work is the flattened list of 16-token KV blocks over all work units
+// (query-head group u of 4 heads, query token t, sequence b), unit-major:
+//   flat = u * TBtot + prefix[t*B + b] + j,  j < ceil(visible(b,t) / 16).
+// A fixed grid of persistent waves splits that list into equal contiguous
+// ranges, so every wave streams the same number of blocks whatever the mix of
+// sequence lengths.  A unit that lies inside one wave's range is finished by
+// that wave; a unit cut by range boundaries leaves one normalised partial
+// (o, lse) per piece, merged afterwards by log-sum-exp weights ("Inference
+// From Scratch", ch. 8: softmax pieces combine through their max and sum).
+//
+// Inside a wave everything stays in registers:
+//   * lane (c, kl, tg) loads 16-byte chunk c of token rows of KV head kl; a
+//     block of K (or V) is LOADS such loads per lane;
+//   * each lane dots its K chunk with the matching q chunk of the GW query
+//     heads of that KV head (v_dot2 on bf16 pairs), and a DPP reduce-scatter
+//     over the NC lanes of a row leaves one complete score per lane;
+//   * online softmax per query head with a lazily raised running maximum
+//     (exponents stay <= 2^8; a rescale happens only when a score exceeds the
+//     maximum by more than 8 in base-2 units, detected with one ballot);
+//   * p is broadcast back along the row with DPP and multiplies the lane's
+//     own V chunk into fp32 accumulators;
+//   * K and V of the next PD blocks are in flight while a block is processed.
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kBS = 16;
+constexpr int kHPW = 4;              // query heads per work unit
+constexpr int kWaves = kStreamWaves;
+constexpr int kWavesPerGroup = 4;
+constexpr int kMinBlocksPerWave = 16;
+constexpr float kSlack = 8.f;
+
+struct StreamArgs {
+  DecodeArgs a;
+  const int* hdr;      // [total, per, tbtot]
+  const int* prefix;   // [TB + 1]
+  const int* first;    // [kWaves] first unit of each wave, -1 if idle
+  float* part;         // partial slots [(kWaves + G)][kHPW][D + 1]
+  int TB;
+};
+
+template <typename ET, int D, int GW>
+struct SGeo {
+  static constexpr int EB = Storage<ET>::bytes;
+  static constexpr int EC = 16 / EB;
+  static constexpr int RB = D * EB;
+  static constexpr int NC = RB / 16;              // lanes per token row (8 or 16)
+  static constexpr int KW = kHPW / GW;            // KV heads per unit
+  static constexpr int LOADS = KW * NC / 4;       // 16-byte loads per lane per block
+  static constexpr int RPL = 64 / (NC * KW);      // tokens per load and KV head
+  static constexpr int NCOMB = LOADS * GW;        // (load, head) score combos per row group
+  static_assert(NCOMB == NC, "one score per lane after the reduce-scatter");
+  static_assert(NC == 8 || NC == 16, "rows of 8 or 16 lanes");
+};
+
+template <int CTRL> __device__ __forceinline__ float dppf(float x) {
+  return __builtin_amdgcn_update_dpp(0.0f, x, CTRL, 0xf, 0xf, false);
+}
+
+// One reduce-scatter stage: lanes whose `bit` is clear keep the lower half of
+// v[0..2n), the others the upper half, each adding its partner's copy.
+template <int CTRL, int N>
+__device__ __forceinline__ void rs_stage(float* v, bool upper) {
+#pragma unroll
+  for (int m = 0; m < N; ++m) {
+    const float mine = upper ? v[m + N] : v[m];
+    const float theirs = upper ? v[m] : v[m + N];
+    v[m] = mine + dppf<CTRL>(theirs);
+  }
+}
+
+// Reduce-scatter of NC partial sums over a group of NC lanes (a 16-lane row
+// or an 8-lane half row): afterwards v[0] of lane c holds the group sum of
+// combo c.  Partners: c^8 (row rotate by 8), c^7 (half-row mirror), c^2, c^1.
+template <int NC>
+__device__ __forceinline__ float reduce_scatter(float* v, int c) {
+  if constexpr (NC == 16) rs_stage<0x128, 8>(v, c & 8);   // row_ror:8
+  rs_stage<0x141, 4>(v, c & 4);                            // row_half_mirror (c^7): split on bit 2
+  rs_stage<0x4E, 2>(v, c & 2);                             // quad_perm [2,3,0,1]
+  rs_stage<0xB1, 1>(v, c & 1);                             // quad_perm [1,0,3,2]
+  return v[0];
+}
+
+// p of combo k from lane k of the lane's own group.
+template <int NC>
+__device__ __forceinline__ float group_bcast(float p, int k, bool upper_half) {
+  if constexpr (NC == 16) {
+    switch (k) {
+      case 0: return dppf<0x150>(p); case 1: return dppf<0x151>(p); case 2: return dppf<0x152>(p);
+      case 3: return dppf<0x153>(p); case 4: return dppf<0x154>(p); case 5: return dppf<0x155>(p);
+      case 6: return dppf<0x156>(p); case 7: return dppf<0x157>(p); case 8: return dppf<0x158>(p);
+      case 9: return dppf<0x159>(p); case 10: return dppf<0x15A>(p); case 11: return dppf<0x15B>(p);
+      case 12: return dppf<0x15C>(p); case 13: return dppf<0x15D>(p); case 14: return dppf<0x15E>(p);
+      default: return dppf<0x15F>(p);
+    }
+  } else {
+    float lo, hi;
+    switch (k) {
+      case 0: lo = dppf<0x150>(p); hi = dppf<0x158>(p); break;
+      case 1: lo = dppf<0x151>(p); hi = dppf<0x159>(p); break;
+      case 2: lo = dppf<0x152>(p); hi = dppf<0x15A>(p); break;
+      case 3: lo = dppf<0x153>(p); hi = dppf<0x15B>(p); break;
+      case 4: lo = dppf<0x154>(p); hi = dppf<0x15C>(p); break;
+      case 5: lo = dppf<0x155>(p); hi = dppf<0x15D>(p); break;
+      case 6: lo = dppf<0x156>(p); hi = dppf<0x15E>(p); break;
+      default: lo = dppf<0x157>(p); hi = dppf<0x15F>(p); break;
+    }
+    return upper_half ? hi : lo;
+  }
+}
+
+// Reduce over all lanes that hold the same query head: every lane bit except
+// the head-selecting ones (the low log2(GW) bits of c and the kl bits).
+template <int NC, int GW, int KW, bool MAX>
+__device__ __forceinline__ float head_reduce(float x) {
+#pragma unroll
+  for (int bit = 0; bit < 6; ++bit) {
+    const int m = 1 << bit;
+    const bool head_bit = (m < GW) || (m >= NC && m < NC * KW);
+    if (head_bit) continue;
+    const float y = __shfl_xor(x, m);
+    x = MAX ? fmaxf(x, y) : x + y;
+  }
+  return x;
+}
+
+template <typename ET> __device__ __forceinline__ float chunk_dot4(u32x4_t k, u32x4_t q, float acc);
+template <> __device__ __forceinline__ float chunk_dot4<Bf16>(u32x4_t k, u32x4_t q, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(k.x), as_bf16x2(q.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(k.y), as_bf16x2(q.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(k.z), as_bf16x2(q.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(k.w), as_bf16x2(q.w), acc, false);
+  return acc;
+}
+template <> __device__ __forceinline__ float chunk_dot4<float>(u32x4_t k, u32x4_t q, float acc) {
+  acc = fmaf(__uint_as_float(k.x), __uint_as_float(q.x), acc);
+  acc = fmaf(__uint_as_float(k.y), __uint_as_float(q.y), acc);
+  acc = fmaf(__uint_as_float(k.z), __uint_as_float(q.z), acc);
+  acc = fmaf(__uint_as_float(k.w), __uint_as_float(q.w), acc);
+  return acc;
+}
+
+template <typename ET> __device__ __forceinline__ void widen(u32x4_t v, float* f);
+template <> __device__ __forceinline__ void widen<Bf16>(u32x4_t v, float* f) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+template <> __device__ __forceinline__ void widen<float>(u32x4_t v, float* f) {
+  f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y); f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+}
+
+template <typename ET> __device__ __forceinline__ void store_chunk(void* dst, const float* v);
+template <> __device__ __forceinline__ void store_chunk<Bf16>(void* dst, const float* v) {
+  u32x4_t w;
+  w.x = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+  w.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+  w.z = (uint32_t)f32_to_bf16_rne(v[4]) | ((uint32_t)f32_to_bf16_rne(v[5]) << 16);
+  w.w = (uint32_t)f32_to_bf16_rne(v[6]) | ((uint32_t)f32_to_bf16_rne(v[7]) << 16);
+  store16(dst, w);
+}
+template <> __device__ __forceinline__ void store_chunk<float>(void* dst, const float* v) {
+  store16(dst, u32x4_t{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
+}
+
+// ---------------------------------------------------------------------------
+// Planning: blocks per (t, b), their prefix sums, and each wave's first unit.
+// ---------------------------------------------------------------------------
+constexpr int kPlanThreads = 1024;
+
+__device__ __forceinline__ int unit_blocks(const int32_t* lens, int tb, int B, int T, int max_tokens) {
+  const int t = tb / B, b = tb - t * B;
+  const int L = clampi(lens[b], 0, max_tokens);
+  const int vis = L - T + t + 1;
+  return vis > 0 ? (vis + kBS - 1) / kBS : 0;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ lens, int B, int T, int U,
+                                                            int max_tokens, int TB, int* __restrict__ hdr,
+                                                            int* __restrict__ prefix, int* __restrict__ first) {
+  __shared__ int part[kPlanThreads];
+  __shared__ int spref[kStreamMaxTB + 1];
+  const int tid = threadIdx.x;
+  const int per_t = (TB + kPlanThreads - 1) / kPlanThreads;
+  const int s0 = min(TB, tid * per_t), s1 = min(TB, s0 + per_t);
+  int sum = 0;
+  for (int i = s0; i < s1; ++i) sum += unit_blocks(lens, i, B, T, max_tokens);
+  part[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = tid ? part[tid - 1] : 0;
+  for (int i = s0; i < s1; ++i) {
+    spref[i] = run;
+    prefix[i] = run;
+    run += unit_blocks(lens, i, B, T, max_tokens);
+  }
+  const int tbtot = part[kPlanThreads - 1];
+  if (tid == 0) {
+    spref[TB] = tbtot;
+    prefix[TB] = tbtot;
+  }
+  __syncthreads();
+  const long long total = (long long)U * tbtot;
+  const int per = (int)max((long long)kMinBlocksPerWave, (total + kWaves - 1) / kWaves);
+  if (tid == 0) {
+    hdr[0] = (int)total;
+    hdr[1] = per;
+    hdr[2] = tbtot;
+  }
+  for (int w = tid; w < kWaves; w += kPlanThreads) {
+    const long long F0 = (long long)w * per;
+    if (F0 >= total) {
+      first[w] = -1;
+      continue;
+    }
+    const int u = (int)(F0 / tbtot);
+    const int r = (int)(F0 - (long long)u * tbtot);
+    // largest i with spref[i] <= r (skips empty units)
+    int lo = 0, hi = TB;   // spref[lo] <= r < spref[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (spref[mid] <= r) lo = mid; else hi = mid;
+    }
+    first[w] = u * TB + lo;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The persistent decode kernel.
+// ---------------------------------------------------------------------------
+template <typename ET, int D, int GW, int PD>
+__global__ __launch_bounds__(64 * kWavesPerGroup, 2) void stream_decode_kernel(StreamArgs sa, float scale_log2e) {
+  using G = SGeo<ET, D, GW>;
+  using ST = typename Storage<ET>::T;
+  const DecodeArgs& a = sa.a;
+  const int lane = threadIdx.x & 63;
+  const int wid = xcd_logical_id(blockIdx.x, gridDim.x / 8) * kWavesPerGroup +
+                  __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int total = sa.hdr[0], per = sa.hdr[1], tbtot = sa.hdr[2];
+  const int F0 = wid * per;
+  if (F0 >= total) return;
+  const int F1 = min(total, F0 + per);
+  int gidx = sa.first[wid];
+
+  const int c = lane % G::NC;
+  const int grp = lane / G::NC;
+  const int kl = grp % G::KW;
+  const int tg = grp / G::KW;
+  const bool upper_half = (lane & 8) != 0;
+  const int lc = c / GW;            // load index of this lane's score combo
+  const int gc = c % GW;            // head (within the KV group) of that combo
+  const int G_ratio = a.Hq / a.Hkv;
+  const size_t block_bytes = (size_t)kBS * a.Hkv * G::RB;
+  const uint32_t load_step = (uint32_t)(G::RPL * a.Hkv * G::RB);
+  const int nmax = a.N_blocks - 1;
+  const int max_tokens = a.max_blocks * kBS;
+
+  while (true) {
+    const int u = gidx / sa.TB;
+    const int tb = gidx - u * sa.TB;
+    const int t = tb / a.B, b = tb - t * a.B;
+    const int pstart = sa.prefix[tb], plen = sa.prefix[tb + 1] - pstart;
+    const int ustart = u * tbtot + pstart;
+    const int js = max(F0, ustart) - ustart;
+    const int je = min(F1, ustart + plen) - ustart;
+    const bool direct = ustart >= F0 && ustart + plen <= F1;
+
+    if (je > js) {
+      const int L = clampi(a.context_lens[b], 0, max_tokens);
+      // visible tokens of the unit, cut at the end of this wave's piece
+      const int hi = min(L - a.T + t + 1, je * kBS);
+      const int h0 = u * kHPW;
+      const int kv0 = h0 / G_ratio;
+      const uint32_t lane_off = (uint32_t)(((tg * a.Hkv) + kv0 + kl) * G::RB + c * 16);
+      const unsigned char* kpool = static_cast<const unsigned char*>(a.k_pool) + lane_off;
+      const unsigned char* vpool = static_cast<const unsigned char*>(a.v_pool) + lane_off;
+      const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks;
+
+      u32x4_t qreg[GW];
+      {
+        const unsigned char* qp = reinterpret_cast<const unsigned char*>(static_cast<const ST*>(a.q)) +
+                                  (((size_t)(b * a.T + t) * a.Hq + h0 + kl * GW) * D) * G::EB + c * 16;
+#pragma unroll
+        for (int g = 0; g < GW; ++g) qreg[g] = load16(qp + (size_t)g * G::RB);
+      }
+
+      float m_lane = kNegInf;   // running max of this lane's head (base 2)
+      float l_part = 0.f;
+      float acc[GW][G::EC];
+#pragma unroll
+      for (int g = 0; g < GW; ++g)
+#pragma unroll
+        for (int e = 0; e < G::EC; ++e) acc[g][e] = 0.f;
+
+      const int nb = je - js;
+      u32x4_t kbuf[PD][G::LOADS], vbuf[PD][G::LOADS];
+      int tbl = 0, cn = 0;
+      // Loads are fenced from the scheduler: left alone it sinks them next to
+      // their use to shorten register live ranges, which undoes the prefetch.
+      auto load_block = [&](u32x4_t (&dst)[G::LOADS], const unsigned char* pool, int ph) {
+        const unsigned char* base = pool + (size_t)ph * block_bytes;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int l = 0; l < G::LOADS; ++l) dst[l] = load16(base + l * load_step);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      auto phys = [&](int i) { return __builtin_amdgcn_readlane(tbl, i < cn ? i : cn - 1); };
+
+      auto body = [&](u32x4_t (&kcur)[G::LOADS], u32x4_t (&vcur)[G::LOADS], int kb, int i) {
+        const int ph_ahead = phys(i + PD);
+        // scores: partial dots of this lane's chunk, then reduce-scatter along the row
+        float part[G::NCOMB];
+#pragma unroll
+        for (int l = 0; l < G::LOADS; ++l)
+#pragma unroll
+          for (int g = 0; g < GW; ++g) part[l * GW + g] = chunk_dot4<ET>(kcur[l], qreg[g], 0.f);
+        load_block(kcur, kpool, ph_ahead);
+        const float sc = reduce_scatter<G::NC>(part, c);
+        const int tok = kb * kBS + lc * G::RPL + tg;
+        const bool valid = tok < hi;
+        const float s2 = valid ? sc * scale_log2e : kNegInf;
+        if (__builtin_amdgcn_ballot_w64(s2 > m_lane + kSlack)) {
+          const float m_new = fmaxf(m_lane, head_reduce<G::NC, GW, G::KW, true>(s2));
+          const float alpha = __builtin_amdgcn_exp2f(m_lane - m_new);   // 0 when m_lane = -inf
+          l_part *= alpha;
+          m_lane = m_new;
+#pragma unroll
+          for (int g = 0; g < GW; ++g) {
+            const float ag = __shfl(alpha, grp * G::NC + g);
+#pragma unroll
+            for (int e = 0; e < G::EC; ++e) acc[g][e] *= ag;
+          }
+        }
+        const float p = valid ? __builtin_amdgcn_exp2f(s2 - m_lane) : 0.f;
+        l_part += p;
+        // acc += p * V; V of tokens past the end is zeroed (never multiply poison by 0)
+#pragma unroll
+        for (int l = 0; l < G::LOADS; ++l) {
+          const bool vvalid = kb * kBS + l * G::RPL + tg < hi;
+          const u32x4_t vz{0u, 0u, 0u, 0u};
+          float vf[G::EC];
+          widen<ET>(vvalid ? vcur[l] : vz, vf);
+#pragma unroll
+          for (int g = 0; g < GW; ++g) {
+            const float pb = group_bcast<G::NC>(p, l * GW + g, upper_half);
+#pragma unroll
+            for (int e = 0; e < G::EC; ++e) acc[g][e] = fmaf(pb, vf[e], acc[g][e]);
+          }
+        }
+        load_block(vcur, vpool, ph_ahead);
+      };
+
+      for (int c0 = 0; c0 < nb; c0 += 64) {
+        cn = min(64, nb - c0);
+        tbl = lane < cn ? clampi(trow[js + c0 + lane], 0, nmax) : 0;
+#pragma unroll
+        for (int s = 0; s < PD; ++s) {
+          load_block(kbuf[s], kpool, phys(s));
+          load_block(vbuf[s], vpool, phys(s));
+        }
+        for (int i = 0; i < cn; i += PD) {
+#pragma unroll
+          for (int s = 0; s < PD; ++s) body(kbuf[s], vbuf[s], js + c0 + i + s, i + s);
+        }
+      }
+
+      // ---- finish the piece: combine token groups and lanes of each head ----
+      const float l_head = head_reduce<G::NC, GW, G::KW, false>(l_part);
+#pragma unroll
+      for (int bit = 0; bit < 6; ++bit) {
+        const int m = 1 << bit;
+        if (m < G::NC * G::KW) continue;       // tg bits only
+#pragma unroll
+        for (int g = 0; g < GW; ++g)
+#pragma unroll
+          for (int e = 0; e < G::EC; ++e) acc[g][e] += __shfl_xor(acc[g][e], m);
+      }
+      if (tg == 0) {
+        const size_t row0 = ((size_t)b * a.T + t) * a.Hq + h0;
+        float* slot = sa.part + (size_t)(wid + gidx) * kHPW * (D + 1);
+#pragma unroll
+        for (int g = 0; g < GW; ++g) {
+          const int hh = kl * GW + g;            // head within the unit
+          const float lh = __shfl(l_head, grp * G::NC + g);
+          const float mh = __shfl(m_lane, grp * G::NC + g);
+          float o[G::EC];
+#pragma unroll
+          for (int e = 0; e < G::EC; ++e) o[e] = lh != 0.f ? acc[g][e] / lh : 0.f;
+          const float lse = lh != 0.f ? (mh + log2f(lh)) * kLn2 : kNegInf;
+          if (direct) {
+            store_chunk<ET>(static_cast<unsigned char*>(a.out) + ((row0 + hh) * D + c * G::EC) * G::EB, o);
+            if (c == 0 && a.lse_out) a.lse_out[row0 + hh] = lse;
+          } else {
+            float* od = slot + hh * D + c * G::EC;
+#pragma unroll
+            for (int e = 0; e < G::EC; e += 4) store16(od + e, u32x4_t{__float_as_uint(o[e]), __float_as_uint(o[e + 1]),
+                                                                        __float_as_uint(o[e + 2]), __float_as_uint(o[e + 3])});
+            if (c == 0) slot[kHPW * D + hh] = lse;
+          }
+        }
+      }
+    }
+    if (ustart + plen >= F1) break;
+    ++gidx;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge the pieces of units cut by wave ranges.
+// ---------------------------------------------------------------------------
+template <typename ET, int D>
+__global__ __launch_bounds__(256) void stream_merge_kernel(StreamArgs sa) {
+  constexpr int DPL = D / 64;
+  using OT = typename Storage<ET>::T;
+  const DecodeArgs& a = sa.a;
+  const int lane = threadIdx.x & 63;
+  const int gidx = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int U = a.Hq / kHPW;
+  if (gidx >= U * sa.TB) return;
+  const int per = sa.hdr[1], tbtot = sa.hdr[2];
+  const int u = gidx / sa.TB, tb = gidx - u * sa.TB;
+  const int t = tb / a.B, b = tb - t * a.B;
+  const int pstart = sa.prefix[tb], plen = sa.prefix[tb + 1] - pstart;
+  const long long ustart = (long long)u * tbtot + pstart;
+  const size_t row0 = ((size_t)b * a.T + t) * a.Hq + u * kHPW;
+  if (plen == 0) {   // nothing visible: out = 0, lse = -inf
+    for (int h = 0; h < kHPW; ++h) {
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) store_out<ET>(static_cast<OT*>(a.out) + (row0 + h) * D + lane * DPL + k, 0.f);
+      if (a.lse_out && lane == 0) a.lse_out[row0 + h] = kNegInf;
+    }
+    return;
+  }
+  const int w0 = (int)(ustart / per), w1 = (int)((ustart + plen - 1) / per);
+  if (w0 == w1) return;   // finished by one wave
+  for (int h = 0; h < kHPW; ++h) {
+    float M = kNegInf;
+    for (int w = w0; w <= w1; ++w) M = fmaxf(M, sa.part[(size_t)(w + gidx) * kHPW * (D + 1) + kHPW * D + h]);
+    float acc[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
+    float wsum = 0.f;
+    for (int w = w0; w <= w1; ++w) {
+      const float* slot = sa.part + (size_t)(w + gidx) * kHPW * (D + 1);
+      const float l = slot[kHPW * D + h];
+      if (l == kNegInf) continue;
+      const float wt = __builtin_amdgcn_exp2f((l - M) * kLog2e);
+      wsum += wt;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) acc[k] = fmaf(wt, slot[h * D + lane * DPL + k], acc[k]);
+    }
+    const float inv = wsum != 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) store_out<ET>(static_cast<OT*>(a.out) + (row0 + h) * D + lane * DPL + k, acc[k] * inv);
+    if (a.lse_out && lane == 0) a.lse_out[row0 + h] = wsum != 0.f ? M + logf(wsum) : kNegInf;
+  }
+}
+
+template <typename ET, int D, int GW>
+hipError_t launch_s(const StreamArgs& sa, hipStream_t stream) {
+  constexpr int LOADS = SGeo<ET, D, GW>::LOADS;
+  constexpr int PD = LOADS >= 16 ? 1 : (LOADS >= 8 ? 2 : 4);   // about 16-32 KB of K+V in flight per wave
+  const float sl2 = sa.a.scale * kLog2e;
+  hipLaunchKernelGGL((stream_decode_kernel<ET, D, GW, PD>), dim3(kWaves / kWavesPerGroup), dim3(64 * kWavesPerGroup), 0,
+                     stream, sa, sl2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int G = (sa.a.Hq / kHPW) * sa.TB;
+  hipLaunchKernelGGL((stream_merge_kernel<ET, D>), dim3((G + 3) / 4), dim3(256), 0, stream, sa);
+  return hipGetLastError();
+}
+
+template <typename ET, int D>
+hipError_t launch_sd(const StreamArgs& sa, hipStream_t stream) {
+  const int G = sa.a.Hq / sa.a.Hkv;
+  if (G >= 4) return launch_s<ET, D, 4>(sa, stream);
+  if (G == 2) return launch_s<ET, D, 2>(sa, stream);
+  return launch_s<ET, D, 1>(sa, stream);
+}
+
+}  // namespace
+
+size_t stream_workspace_bytes(int B, int T, int Hq, int D) {
+  const size_t TB = (size_t)B * T;
+  const size_t G = (size_t)(Hq / kHPW) * TB;
+  size_t off = 256;                                       // header
+  off += ((TB + 1) * 4 + 255) / 256 * 256;                // prefix
+  off += ((size_t)kWaves * 4 + 255) / 256 * 256;          // first unit per wave
+  off += ((size_t)kWaves + G) * kHPW * (D + 1) * 4;       // partial slots
+  return off;
+}
+
+bool stream_supported(const DecodeArgs& a) {
+  // rows of 8 or 16 lanes: bf16 D in {64,128}, fp32 D = 64
+  const bool rows_ok = a.bf16 || a.D == 64;
+  return rows_ok && (long long)a.B * a.T <= kStreamMaxTB &&
+         (long long)(a.Hq / kHPW) * a.B * a.T * a.max_blocks < (1ll << 30);
+}
+
+hipError_t launch_decode_stream(const DecodeArgs& a, void* workspace, hipStream_t stream) {
+  StreamArgs sa{};
+  sa.a = a;
+  sa.TB = a.B * a.T;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  int* hdr = reinterpret_cast<int*>(ws);
+  int* prefix = reinterpret_cast<int*>(ws + 256);
+  int* first = reinterpret_cast<int*>(ws + 256 + ((size_t)(sa.TB + 1) * 4 + 255) / 256 * 256);
+  float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(first) + ((size_t)kWaves * 4 + 255) / 256 * 256);
+  sa.hdr = hdr; sa.prefix = prefix; sa.first = first; sa.part = part;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.context_lens, a.B, a.T, a.Hq / kHPW,
+                     a.max_blocks * kBS, sa.TB, hdr, prefix, first);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.bf16) return a.D == 64 ? launch_sd<Bf16, 64>(sa, stream) : launch_sd<Bf16, 128>(sa, stream);
+  return launch_sd<float, 64>(sa, stream);
+}
+
+}  // namespace pkv

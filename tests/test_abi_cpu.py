@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_workspace_sizing():
     f = pkv.pkv_decode_workspace_bytes
-    assert f(4, 1, 32, 128, 64, 16, 0) == 0
+    assert f(4, 1, 32, 128, 64, 16, 0) > 0          # balanced split needs its own workspace
     # P_max = ceil(64*16/256) = 4 partitions
     assert f(4, 1, 32, 128, 64, 16, 256) == 4 * 1 * 32 * 4 * 129 * 4
     assert f(16, 4, 32, 128, 4096, 16, 512) == 16 * 4 * 32 * 128 * 129 * 4
@@ -66,6 +66,7 @@ def _decode(**kw):
     (dict(Hq=6, Hkv=6), pkv.PKV_EUNSUPPORTED),      # Hq not a multiple of 4
     (dict(Hq=8, Hkv=8, D=128, dt=pkv.PKV_FP32), pkv.PKV_EUNSUPPORTED),
     (dict(part=16), pkv.PKV_EWORKSPACE),
+    (dict(part=0), pkv.PKV_EWORKSPACE),
     (dict(part=16, ws=P, wsb=100), pkv.PKV_EWORKSPACE),
 ])
 def test_decode_argument_errors(kw, status):
