@@ -56,23 +56,55 @@ def algorithmic_bytes(w):
 
 
 def cpu_baseline(w, budget_s):
-    """The fp64 oracle, untuned, on the first n sequences (n sized to ~budget_s of work), one BLAS thread."""
+    """The fp64 oracle, untuned, one BLAS thread, on a bounded sample of the same batch.
+
+    Sequences are evaluated one call at a time, cycling through the batch,
+    until budget_s seconds of oracle time have been spent."""
     import oracle
     from threadpoolctl import threadpool_limits
 
-    def run(n):
-        q = w.values(w.q[:n])
-        t0 = time.perf_counter()
-        oracle.paged_attention(q, w.values(w.k_pool), w.values(w.v_pool), w.block_tables[:n], w.context_lens[:n],
-                               w.scale, w.block_size)
-        return time.perf_counter() - t0
-
+    q_all, kp, vp = w.values(w.q), w.values(w.k_pool), w.values(w.v_pool)
+    done, spent = 0, 0.0
     with threadpool_limits(limits=1):
-        t1 = run(1)
-        n = int(max(1, min(w.B, budget_s / max(t1, 1e-3))))
-        t = run(n)
-    return {"value": n / t, "unit": "seq-steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} of {w.B} sequences of {w.name} (fp64 NumPy, 1 BLAS thread, {t:.1f} s)"}
+        while spent < budget_s:
+            b = done % w.B
+            t0 = time.perf_counter()
+            oracle.paged_attention(q_all[b:b + 1], kp, vp, w.block_tables[b:b + 1], w.context_lens[b:b + 1],
+                                   w.scale, w.block_size)
+            spent += time.perf_counter() - t0
+            done += 1
+    return {"value": round(done / spent, 2), "unit": "seq-steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} sequence-steps of {w.name} taken in batch order ({min(done, w.B)} distinct "
+                      f"sequences), fp64 NumPy oracle, 1 BLAS thread, {spent:.1f} s"}
+
+
+def read_ceiling(torch, dev, nbytes=2 << 30, reps=10):
+    """Read bandwidth of the diagnostic probe: random 32 KB blocks of a 2 GiB pool, read as
+    4 KB head slices (the KV-pool pattern), no compute; 8 and 16 waves per CU."""
+    import ctypes
+    from paged_kv_cache_attention_amd import build as pkv_build
+    lib = ctypes.CDLL(str(pkv_build.PROBE_LIB))
+    nblocks = nbytes // 32768
+    pool = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    g = torch.Generator().manual_seed(0)
+    order = torch.randperm(nblocks, generator=g).to(torch.int32).to(dev)
+    res = {}
+    for grid in (512, 1024):
+        sink = torch.empty(grid * 256, dtype=torch.int32, device=dev)
+        call = lambda: lib.pkv_probe_slice_read(ctypes.c_void_p(pool.data_ptr()), ctypes.c_void_p(order.data_ptr()),
+                                                nblocks, grid, ctypes.c_void_p(sink.data_ptr()), None)
+        for _ in range(2):
+            assert call() == 0
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        res[f"GBps_{grid * 4 // 256}_waves_per_cu"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    return res
 
 
 def copy_ceiling(torch, dev, nbytes=1 << 30, reps=20):
@@ -102,7 +134,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ceiling", action="store_true",
-                    help="also time a plain 1 GiB device copy (torch) as the practical bandwidth reference")
+                    help="also time a plain 1 GiB device copy (torch) and the random-slice read probe")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -178,6 +210,7 @@ def main():
     }
     if args.ceiling:
         result["copy_ceiling"] = copy_ceiling(torch, dev)
+        result["read_ceiling"] = read_ceiling(torch, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -19,6 +19,7 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 LIB = PKG / "libpkv.so"
+PROBE_LIB = PKG / "libpkv_probe.so"      # diagnostic read-bandwidth probe, not part of the pkv ABI
 SOURCES = ["pkv_api.hip", "pkv_decode.hip", "pkv_stream.hip", "pkv_verify.hip", "pkv_reduce.hip", "pkv_copy.hip"]
 ARCH = "gfx950"
 
@@ -37,10 +38,7 @@ def command(out: pathlib.Path = LIB, extra=()) -> list:
             f"-I{INCLUDE}", f"-I{CSRC}", *extra, "-o", str(out), *[str(CSRC / s) for s in SOURCES]]
 
 
-def build(verbose: bool = False) -> pathlib.Path:
-    """Always recompiles; writes libpkv.so next to this file atomically."""
-    tmp = LIB.with_suffix(".so.tmp")
-    cmd = command(tmp)
+def _compile(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,6 +48,18 @@ def build(verbose: bool = False) -> pathlib.Path:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> pathlib.Path:
+    """Always recompiles; writes libpkv.so (and the probe library) next to this file atomically."""
+    ptmp = PROBE_LIB.with_suffix(".so.tmp")
+    _compile([hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument",
+              "-o", str(ptmp), str(CSRC / "probe_read.hip")], verbose)
+    os.replace(ptmp, PROBE_LIB)
+    tmp = LIB.with_suffix(".so.tmp")
+    cmd = command(tmp)
+    _compile(cmd, verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -28,7 +28,10 @@ struct DecodeArgs {
 // Balanced persistent VALU path: a fixed grid of kStreamWaves waves splits
 // the flattened block list of all (head group, query token, sequence) units
 // evenly; pieces of units cut by wave ranges are merged by a second kernel.
-constexpr int kStreamWaves = 2048;
+#ifndef PKV_STREAM_WAVES
+#define PKV_STREAM_WAVES 2048
+#endif
+constexpr int kStreamWaves = PKV_STREAM_WAVES;
 constexpr int kStreamMaxTB = 8192;   // B * T limit of the planning kernel
 bool stream_supported(const DecodeArgs& a);
 size_t stream_workspace_bytes(int B, int T, int Hq, int D);

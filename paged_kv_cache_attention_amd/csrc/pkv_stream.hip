@@ -1,14 +1,16 @@
 // Paged decode attention, balanced persistent VALU path (gfx950).
 //
-// Work is the flattened list of 16-token KV blocks over all work units
-// (query-head group u of 4 heads, query token t, sequence b), unit-major:
-//   flat = u * TBtot + prefix[t*B + b] + j,  j < ceil(visible(b,t) / 16).
-// A fixed grid of persistent waves splits that list into equal contiguous
-// ranges, so every wave streams the same number of blocks whatever the mix of
-// sequence lengths.  A unit that lies inside one wave's range is finished by
-// that wave; a unit cut by range boundaries leaves one normalised partial
-// (o, lse) per piece, merged afterwards by log-sum-exp weights ("Inference
-// From Scratch", ch. 8: softmax pieces combine through their max and sum).
+// Work is the flattened list of 16-token KV blocks of all (query token t,
+// sequence b) pairs:  flat = prefix[t*B + b] + j,  j < ceil(visible(b,t)/16).
+// A fixed grid of persistent workgroups splits that list into equal
+// contiguous ranges, so every workgroup streams the same number of blocks
+// whatever the mix of sequence lengths.  A workgroup has one wave per group of
+// 4 query heads (U = Hq/4 waves); its waves walk the same blocks together, so
+// each CU reads whole physical blocks (all KV heads, contiguous) at once.
+// A (t, b) pair that lies inside one range is finished by its workgroup; a
+// pair cut by range boundaries leaves one normalised partial (o, lse) per
+// piece and head, merged afterwards by log-sum-exp weights ("Inference From
+// Scratch", ch. 8: softmax pieces combine through their max and sum).
 //
 // Inside a wave everything stays in registers:
 //   * lane (c, kl, tg) loads 16-byte chunk c of token rows of KV head kl; a
@@ -30,18 +32,22 @@ namespace {
 
 constexpr int kBS = 16;
 constexpr int kHPW = 4;              // query heads per work unit
-constexpr int kWaves = kStreamWaves;
-constexpr int kWavesPerGroup = 4;
-constexpr int kMinBlocksPerWave = 16;
+constexpr int kWaves = kStreamWaves;   // about 8 waves per CU
+#ifndef PKV_STREAM_WPG
+#define PKV_STREAM_WPG 8
+#endif
+constexpr int kMaxU = PKV_STREAM_WPG;  // head groups (waves) per workgroup
+constexpr int kMinBlocksPerRange = 16;
 constexpr float kSlack = 8.f;
 
 struct StreamArgs {
   DecodeArgs a;
   const int* hdr;      // [total, per, tbtot]
   const int* prefix;   // [TB + 1]
-  const int* first;    // [kWaves] first unit of each wave, -1 if idle
-  float* part;         // partial slots [(kWaves + G)][kHPW][D + 1]
+  const int* first;    // [ranges] first (t, b) pair of each range, -1 if idle
+  float* part;         // partial slots [(ranges + TB)][Hq][D + 1]
   int TB;
+  int ranges;          // workgroups splitting the block list
 };
 
 template <typename ET, int D, int GW>
@@ -179,8 +185,8 @@ __device__ __forceinline__ int unit_blocks(const int32_t* lens, int tb, int B, i
   return vis > 0 ? (vis + kBS - 1) / kBS : 0;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ lens, int B, int T, int U,
-                                                            int max_tokens, int TB, int* __restrict__ hdr,
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ lens, int B, int T,
+                                                            int ranges, int max_tokens, int TB, int* __restrict__ hdr,
                                                             int* __restrict__ prefix, int* __restrict__ first) {
   __shared__ int part[kPlanThreads];
   __shared__ int spref[kStreamMaxTB + 1];
@@ -209,28 +215,26 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     prefix[TB] = tbtot;
   }
   __syncthreads();
-  const long long total = (long long)U * tbtot;
-  const int per = (int)max((long long)kMinBlocksPerWave, (total + kWaves - 1) / kWaves);
+  const int per = max(kMinBlocksPerRange, (tbtot + ranges - 1) / ranges);
   if (tid == 0) {
-    hdr[0] = (int)total;
+    hdr[0] = tbtot;
     hdr[1] = per;
     hdr[2] = tbtot;
   }
-  for (int w = tid; w < kWaves; w += kPlanThreads) {
+  for (int w = tid; w < ranges; w += kPlanThreads) {
     const long long F0 = (long long)w * per;
-    if (F0 >= total) {
+    if (F0 >= tbtot) {
       first[w] = -1;
       continue;
     }
-    const int u = (int)(F0 / tbtot);
-    const int r = (int)(F0 - (long long)u * tbtot);
-    // largest i with spref[i] <= r (skips empty units)
+    const int r = (int)F0;
+    // largest i with spref[i] <= r (skips empty pairs)
     int lo = 0, hi = TB;   // spref[lo] <= r < spref[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (spref[mid] <= r) lo = mid; else hi = mid;
     }
-    first[w] = u * TB + lo;
+    first[w] = lo;
   }
 }
 
@@ -238,18 +242,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 // The persistent decode kernel.
 // ---------------------------------------------------------------------------
 template <typename ET, int D, int GW, int PD>
-__global__ __launch_bounds__(64 * kWavesPerGroup, 2) void stream_decode_kernel(StreamArgs sa, float scale_log2e) {
+__global__ __launch_bounds__(64 * kMaxU) void stream_decode_kernel(StreamArgs sa, float scale_log2e) {
   using G = SGeo<ET, D, GW>;
   using ST = typename Storage<ET>::T;
   const DecodeArgs& a = sa.a;
   const int lane = threadIdx.x & 63;
-  const int wid = xcd_logical_id(blockIdx.x, gridDim.x / 8) * kWavesPerGroup +
-                  __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int total = sa.hdr[0], per = sa.hdr[1], tbtot = sa.hdr[2];
-  const int F0 = wid * per;
+  const int U = a.Hq / kHPW;
+  const int wpg = blockDim.x >> 6;                      // waves per workgroup
+  const int rng = blockIdx.x / (U / wpg);               // block range of this workgroup
+  const int u = (blockIdx.x % (U / wpg)) * wpg + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int total = sa.hdr[0], per = sa.hdr[1];
+  const int F0 = rng * per;
   if (F0 >= total) return;
   const int F1 = min(total, F0 + per);
-  int gidx = sa.first[wid];
+  int tb = sa.first[rng];
 
   const int c = lane % G::NC;
   const int grp = lane / G::NC;
@@ -265,11 +271,9 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, 2) void stream_decode_kernel(S
   const int max_tokens = a.max_blocks * kBS;
 
   while (true) {
-    const int u = gidx / sa.TB;
-    const int tb = gidx - u * sa.TB;
     const int t = tb / a.B, b = tb - t * a.B;
     const int pstart = sa.prefix[tb], plen = sa.prefix[tb + 1] - pstart;
-    const int ustart = u * tbtot + pstart;
+    const int ustart = pstart;
     const int js = max(F0, ustart) - ustart;
     const int je = min(F1, ustart + plen) - ustart;
     const bool direct = ustart >= F0 && ustart + plen <= F1;
@@ -310,7 +314,13 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, 2) void stream_decode_kernel(S
         const unsigned char* base = pool + (size_t)ph * block_bytes;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int l = 0; l < G::LOADS; ++l) dst[l] = load16(base + l * load_step);
+        for (int l = 0; l < G::LOADS; ++l) {
+#ifdef PKV_NT_LOADS
+          dst[l] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(base + l * load_step));
+#else
+          dst[l] = load16(base + l * load_step);
+#endif
+        }
         __builtin_amdgcn_sched_barrier(0);
       };
       auto phys = [&](int i) { return __builtin_amdgcn_readlane(tbl, i < cn ? i : cn - 1); };
@@ -386,7 +396,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, 2) void stream_decode_kernel(S
       }
       if (tg == 0) {
         const size_t row0 = ((size_t)b * a.T + t) * a.Hq + h0;
-        float* slot = sa.part + (size_t)(wid + gidx) * kHPW * (D + 1);
+        float* slot = sa.part + ((size_t)(rng + tb) * a.Hq + h0) * (D + 1);
 #pragma unroll
         for (int g = 0; g < GW; ++g) {
           const int hh = kl * GW + g;            // head within the unit
@@ -400,17 +410,17 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, 2) void stream_decode_kernel(S
             store_chunk<ET>(static_cast<unsigned char*>(a.out) + ((row0 + hh) * D + c * G::EC) * G::EB, o);
             if (c == 0 && a.lse_out) a.lse_out[row0 + hh] = lse;
           } else {
-            float* od = slot + hh * D + c * G::EC;
+            float* od = slot + hh * (D + 1) + c * G::EC;
 #pragma unroll
             for (int e = 0; e < G::EC; e += 4) store16(od + e, u32x4_t{__float_as_uint(o[e]), __float_as_uint(o[e + 1]),
                                                                         __float_as_uint(o[e + 2]), __float_as_uint(o[e + 3])});
-            if (c == 0) slot[kHPW * D + hh] = lse;
+            if (c == 0) slot[hh * (D + 1) + D] = lse;
           }
         }
       }
     }
     if (ustart + plen >= F1) break;
-    ++gidx;
+    ++tb;
   }
 }
 
@@ -419,59 +429,82 @@ __global__ __launch_bounds__(64 * kWavesPerGroup, 2) void stream_decode_kernel(S
 // ---------------------------------------------------------------------------
 template <typename ET, int D>
 __global__ __launch_bounds__(256) void stream_merge_kernel(StreamArgs sa) {
-  constexpr int DPL = D / 64;
+  // One wave per unit: lanes 16h .. 16h+15 hold head h, EPL elements each.
+  // The pieces' (o, lse) are loaded in batches of 8 with all loads issued
+  // together, and merged online: running max, rescaled sum and accumulator.
+  constexpr int EPL = D / 16;
+  constexpr int BATCH = 8;
   using OT = typename Storage<ET>::T;
   const DecodeArgs& a = sa.a;
   const int lane = threadIdx.x & 63;
-  const int gidx = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int gidx = blockIdx.x * 4 + (threadIdx.x >> 6);   // (t, b) pair and head group
   const int U = a.Hq / kHPW;
   if (gidx >= U * sa.TB) return;
-  const int per = sa.hdr[1], tbtot = sa.hdr[2];
-  const int u = gidx / sa.TB, tb = gidx - u * sa.TB;
+  const int per = sa.hdr[1];
+  const int tb = gidx / U, u = gidx - tb * U;
   const int t = tb / a.B, b = tb - t * a.B;
   const int pstart = sa.prefix[tb], plen = sa.prefix[tb + 1] - pstart;
-  const long long ustart = (long long)u * tbtot + pstart;
-  const size_t row0 = ((size_t)b * a.T + t) * a.Hq + u * kHPW;
+  const long long ustart = pstart;
+  const int h = lane >> 4, d0 = (lane & 15) * EPL;
+  const size_t orow = (((size_t)b * a.T + t) * a.Hq + u * kHPW + h) * D + d0;
+  OT* out = static_cast<OT*>(a.out) + orow;
+  float* lse_out = a.lse_out ? a.lse_out + ((size_t)b * a.T + t) * a.Hq + u * kHPW + h : nullptr;
   if (plen == 0) {   // nothing visible: out = 0, lse = -inf
-    for (int h = 0; h < kHPW; ++h) {
 #pragma unroll
-      for (int k = 0; k < DPL; ++k) store_out<ET>(static_cast<OT*>(a.out) + (row0 + h) * D + lane * DPL + k, 0.f);
-      if (a.lse_out && lane == 0) a.lse_out[row0 + h] = kNegInf;
-    }
+    for (int e = 0; e < EPL; ++e) store_out<ET>(out + e, 0.f);
+    if (lse_out && (lane & 15) == 0) *lse_out = kNegInf;
     return;
   }
   const int w0 = (int)(ustart / per), w1 = (int)((ustart + plen - 1) / per);
   if (w0 == w1) return;   // finished by one wave
-  for (int h = 0; h < kHPW; ++h) {
-    float M = kNegInf;
-    for (int w = w0; w <= w1; ++w) M = fmaxf(M, sa.part[(size_t)(w + gidx) * kHPW * (D + 1) + kHPW * D + h]);
-    float acc[DPL];
+  float m = kNegInf, ssum = 0.f, acc[EPL];
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
-    float wsum = 0.f;
-    for (int w = w0; w <= w1; ++w) {
-      const float* slot = sa.part + (size_t)(w + gidx) * kHPW * (D + 1);
-      const float l = slot[kHPW * D + h];
-      if (l == kNegInf) continue;
-      const float wt = __builtin_amdgcn_exp2f((l - M) * kLog2e);
-      wsum += wt;
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int w = w0; w <= w1; w += BATCH) {
+    float lv[BATCH], ov[BATCH][EPL];
 #pragma unroll
-      for (int k = 0; k < DPL; ++k) acc[k] = fmaf(wt, slot[h * D + lane * DPL + k], acc[k]);
+    for (int k = 0; k < BATCH; ++k) {
+      lv[k] = kNegInf;
+      if (w + k <= w1) {
+        const float* slot = sa.part + ((size_t)(w + k + tb) * a.Hq + u * kHPW + h) * (D + 1);
+        lv[k] = slot[D];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) ov[k][e] = slot[d0 + e];
+      }
     }
-    const float inv = wsum != 0.f ? 1.f / wsum : 0.f;
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) store_out<ET>(static_cast<OT*>(a.out) + (row0 + h) * D + lane * DPL + k, acc[k] * inv);
-    if (a.lse_out && lane == 0) a.lse_out[row0 + h] = wsum != 0.f ? M + logf(wsum) : kNegInf;
+    for (int k = 0; k < BATCH; ++k) {
+      if (lv[k] == kNegInf) continue;   // absent or empty piece: its o is not read
+      const float nm = fmaxf(m, lv[k]);
+      const float sa_ = __builtin_amdgcn_exp2f((m - nm) * kLog2e);
+      const float sb = __builtin_amdgcn_exp2f((lv[k] - nm) * kLog2e);
+      ssum = ssum * sa_ + sb;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = acc[e] * sa_ + sb * ov[k][e];
+      m = nm;
+    }
   }
+  const float inv = ssum != 0.f ? 1.f / ssum : 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) store_out<ET>(out + e, acc[e] * inv);
+  if (lse_out && (lane & 15) == 0) *lse_out = ssum != 0.f ? m + logf(ssum) : kNegInf;
 }
 
 template <typename ET, int D, int GW>
 hipError_t launch_s(const StreamArgs& sa, hipStream_t stream) {
   constexpr int LOADS = SGeo<ET, D, GW>::LOADS;
-  constexpr int PD = LOADS >= 16 ? 1 : (LOADS >= 8 ? 2 : 4);   // about 16-32 KB of K+V in flight per wave
+#ifdef PKV_STREAM_PD
+  constexpr int PD = PKV_STREAM_PD;
+#else
+  // Two blocks in flight per wave: measured as fast as four on the 8B-shaped
+  // batch (deeper prefetch only lengthens memory queues) and half the VGPRs.
+  constexpr int PD = LOADS >= 16 ? 1 : 2;
+#endif
   const float sl2 = sa.a.scale * kLog2e;
-  hipLaunchKernelGGL((stream_decode_kernel<ET, D, GW, PD>), dim3(kWaves / kWavesPerGroup), dim3(64 * kWavesPerGroup), 0,
-                     stream, sa, sl2);
+  const int U = sa.a.Hq / kHPW;
+  const int wpg = U < kMaxU ? U : kMaxU;
+  hipLaunchKernelGGL((stream_decode_kernel<ET, D, GW, PD>), dim3(sa.ranges * (U / wpg)), dim3(64 * wpg), 0, stream,
+                     sa, sl2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int G = (sa.a.Hq / kHPW) * sa.TB;
@@ -489,34 +522,39 @@ hipError_t launch_sd(const StreamArgs& sa, hipStream_t stream) {
 
 }  // namespace
 
+int stream_ranges(int Hq) { return kWaves / (Hq >= kHPW ? Hq / kHPW : 1); }
+
 size_t stream_workspace_bytes(int B, int T, int Hq, int D) {
   const size_t TB = (size_t)B * T;
-  const size_t G = (size_t)(Hq / kHPW) * TB;
+  const size_t R = (size_t)stream_ranges(Hq);
   size_t off = 256;                                       // header
   off += ((TB + 1) * 4 + 255) / 256 * 256;                // prefix
-  off += ((size_t)kWaves * 4 + 255) / 256 * 256;          // first unit per wave
-  off += ((size_t)kWaves + G) * kHPW * (D + 1) * 4;       // partial slots
+  off += (R * 4 + 255) / 256 * 256;                       // first pair per range
+  off += (R + TB) * Hq * (D + 1) * 4;                     // partial slots
   return off;
 }
 
 bool stream_supported(const DecodeArgs& a) {
   // rows of 8 or 16 lanes: bf16 D in {64,128}, fp32 D = 64
   const bool rows_ok = a.bf16 || a.D == 64;
-  return rows_ok && (long long)a.B * a.T <= kStreamMaxTB &&
-         (long long)(a.Hq / kHPW) * a.B * a.T * a.max_blocks < (1ll << 30);
+  const int U = a.Hq / kHPW;
+  return rows_ok && (U <= kMaxU || U % kMaxU == 0) && (long long)a.B * a.T <= kStreamMaxTB &&
+         (long long)a.B * a.T * a.max_blocks < (1ll << 30);
 }
 
 hipError_t launch_decode_stream(const DecodeArgs& a, void* workspace, hipStream_t stream) {
   StreamArgs sa{};
   sa.a = a;
   sa.TB = a.B * a.T;
+  sa.ranges = stream_ranges(a.Hq);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   int* hdr = reinterpret_cast<int*>(ws);
   int* prefix = reinterpret_cast<int*>(ws + 256);
   int* first = reinterpret_cast<int*>(ws + 256 + ((size_t)(sa.TB + 1) * 4 + 255) / 256 * 256);
-  float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(first) + ((size_t)kWaves * 4 + 255) / 256 * 256);
+  float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(first) +
+                                         ((size_t)sa.ranges * 4 + 255) / 256 * 256);
   sa.hdr = hdr; sa.prefix = prefix; sa.first = first; sa.part = part;
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.context_lens, a.B, a.T, a.Hq / kHPW,
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.context_lens, a.B, a.T, sa.ranges,
                      a.max_blocks * kBS, sa.TB, hdr, prefix, first);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -233,7 +233,7 @@ def tinylm_mha_bf16(poison=True, structure_only=False):
                    poison=poison, append=False, structure_only=structure_only)
 
 
-def llama1b_gqa_append(poison=True, partition_size=512, structure_only=False):
+def llama1b_gqa_append(poison=True, partition_size=0, structure_only=False):
     """B=64, GQA 32/8, D=64, pre-append lengths ~ U[128,4096], 1 token appended."""
     rng = np.random.Generator(np.random.PCG64(3))
     lens_pre = rng.integers(128, 4096, size=64, endpoint=True)
@@ -256,7 +256,7 @@ def llama8b_prefix_lens(rng):
     return np.clip(np.rint(1024.0 * np.exp(0.8 * z)), 16, 8192).astype(np.int64)
 
 
-def llama8b_prefix_share(poison=True, partition_size=1024, structure_only=False):
+def llama8b_prefix_share(poison=True, partition_size=0, structure_only=False):
     """B=256, GQA 32/8, D=128, lognormal lengths; groups of 16 share a 512-token prefix.
 
     A member with L < 512 points at the first ceil(L/16) blocks of its group's
