@@ -92,7 +92,10 @@ const char* pkv_last_error(void) { return g_last_error.c_str(); }
 
 size_t pkv_decode_workspace_bytes(int B, int T, int Hq, int D, int max_blocks, int block_size, int partition_size) {
   if (B < 0 || T < 1 || Hq < 1 || D < 1 || max_blocks < 1 || block_size < 1 || partition_size < 0) return 0;
-  if (partition_size == 0) return pkv::stream_workspace_bytes(B, T, Hq, D);
+  if (partition_size == 0) {
+    const size_t a = pkv::stream_workspace_bytes(B, T, Hq, D), b = pkv::verify_workspace_bytes(B, T, Hq, D);
+    return a > b ? a : b;
+  }
   const unsigned long long P = (unsigned long long)partitions_max(max_blocks, block_size, partition_size);
   const unsigned long long rows = (unsigned long long)B * T * Hq;
   return (size_t)(rows * P * (unsigned long long)(D + 1) * 4ull);
@@ -173,7 +176,9 @@ pkv_status paged_attention_decode(const void* q, const void* k_pool, const void*
                              PKV_OK)
     return st;
   const bool fixed_split = partition_size > 0 && partition_size < max_blocks * block_size;
-  if (partition_size == 0 && !pkv::verify_mfma_supported(a) && pkv::stream_supported(a))
+  if (partition_size == 0 && pkv::verify_mfma_supported(a))
+    return from_hip(pkv::launch_verify_mfma(a, workspace, s), "paged_attention_decode verify launch");
+  if (partition_size == 0 && pkv::stream_supported(a))
     return from_hip(pkv::launch_decode_stream(a, workspace, s), "paged_attention_decode launch");
   if (fixed_split) {
     a.part_tokens = partition_size;
@@ -186,10 +191,7 @@ pkv_status paged_attention_decode(const void* q, const void* k_pool, const void*
   }
   if ((unsigned long long)a.P_max * T * (Hq / 4) * B > (1ull << 31) - 256)
     return fail(PKV_EINVAL, "too many work items");
-  if (pkv::verify_mfma_supported(a))
-    st = from_hip(pkv::launch_verify_mfma(a, s), "paged_attention_decode verify launch");
-  else
-    st = from_hip(pkv::launch_decode_valu(a, s), "paged_attention_decode launch");
+  st = from_hip(pkv::launch_decode_valu(a, s), "paged_attention_decode launch");
   if (st != PKV_OK || !fixed_split) return st;
   return from_hip(pkv::launch_lse_reduce(a.part_out, a.part_lse, out, lse_out, B, T, Hq, D, a.P_max, a.bf16,
                                          context_lens, partition_size, s),

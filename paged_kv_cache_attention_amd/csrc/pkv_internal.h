@@ -40,9 +40,17 @@ hipError_t launch_decode_stream(const DecodeArgs& a, void* workspace, hipStream_
 // VALU decode kernel: any T (one query token per work item), Hq/Hkv in {1,2,4,8}.
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
 
-// MFMA verify kernel for bf16 when T * (Hq/Hkv) == 16 (e.g. T=4 with 4 query heads per KV head).
+// Planning kernel shared by the balanced paths: blocks per (t, b) pair with
+// the causal limit of query token t, their prefix sums, the range length and
+// each range's first pair (B*T <= kStreamMaxTB).
+hipError_t launch_plan(const int32_t* lens, int B, int T, int ranges, int max_tokens, int* hdr, int* prefix, int* first,
+                       hipStream_t stream);
+
+// MFMA verify tile for bf16 with 2 <= T and T * (Hq/Hkv) <= 16 query rows per
+// KV head; balanced like the VALU path, with its own workspace layout.
 bool verify_mfma_supported(const DecodeArgs& a);
-hipError_t launch_verify_mfma(const DecodeArgs& a, hipStream_t stream);
+size_t verify_workspace_bytes(int B, int T, int Hq, int D);
+hipError_t launch_verify_mfma(const DecodeArgs& a, void* workspace, hipStream_t stream);
 
 // Log-sum-exp merge of split partials.  When `lens` is given, rows whose
 // sequence has a single partition are skipped (the decode kernel wrote them).

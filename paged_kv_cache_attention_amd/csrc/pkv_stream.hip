@@ -340,7 +340,8 @@ __global__ __launch_bounds__(64 * kMaxU) void stream_decode_kernel(StreamArgs sa
         const float s2 = valid ? sc * scale_log2e : kNegInf;
         if (__builtin_amdgcn_ballot_w64(s2 > m_lane + kSlack)) {
           const float m_new = fmaxf(m_lane, head_reduce<G::NC, GW, G::KW, true>(s2));
-          const float alpha = __builtin_amdgcn_exp2f(m_lane - m_new);   // 0 when m_lane = -inf
+          // 1 while a head is still empty (both -inf), 0 on its first key
+          const float alpha = m_lane == m_new ? 1.f : __builtin_amdgcn_exp2f(m_lane - m_new);
           l_part *= alpha;
           m_lane = m_new;
 #pragma unroll
@@ -522,6 +523,13 @@ hipError_t launch_sd(const StreamArgs& sa, hipStream_t stream) {
 
 }  // namespace
 
+hipError_t launch_plan(const int32_t* lens, int B, int T, int ranges, int max_tokens, int* hdr, int* prefix, int* first,
+                       hipStream_t stream) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, lens, B, T, ranges, max_tokens, B * T, hdr,
+                     prefix, first);
+  return hipGetLastError();
+}
+
 int stream_ranges(int Hq) { return kWaves / (Hq >= kHPW ? Hq / kHPW : 1); }
 
 size_t stream_workspace_bytes(int B, int T, int Hq, int D) {
@@ -554,9 +562,7 @@ hipError_t launch_decode_stream(const DecodeArgs& a, void* workspace, hipStream_
   float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(first) +
                                          ((size_t)sa.ranges * 4 + 255) / 256 * 256);
   sa.hdr = hdr; sa.prefix = prefix; sa.first = first; sa.part = part;
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.context_lens, a.B, a.T, sa.ranges,
-                     a.max_blocks * kBS, sa.TB, hdr, prefix, first);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_plan(a.context_lens, a.B, a.T, sa.ranges, a.max_blocks * kBS, hdr, prefix, first, stream);
   if (e != hipSuccess) return e;
   if (a.bf16) return a.D == 64 ? launch_sd<Bf16, 64>(sa, stream) : launch_sd<Bf16, 128>(sa, stream);
   return launch_sd<float, 64>(sa, stream);

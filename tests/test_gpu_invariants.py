@@ -123,6 +123,19 @@ def test_verify_rows_equal_decode_chain():
         oracle_check(w, o4, l4, f"verify part={part}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_verify_piece_visible_only_to_later_rows(D):
+    """Balanced split with pieces of 16 blocks: a piece that is the last block alone, visible only to the
+    later query tokens (L in 257..259, T=4), must leave the earlier rows empty, not NaN."""
+    T = 4
+    lens = [257, 258, 259, 300, 16 * 33 + 2]
+    w = workload.uniform_batch("late_rows", seed=12, B=len(lens), T=T, Hq=16, Hkv=4, D=D, dtype="bf16", lens=lens)
+    d = upload(w)
+    say("late rows", D)
+    out, lse = decode(w, d, 0)
+    oracle_check(w, out, lse, f"late rows D={D}")
+
+
 def test_fully_masked_partition_rows():
     """T=4 and L mod 512 in {1,2,3}: the last partition is empty for the first rows (lse -inf, o 0)."""
     T = 4

@@ -285,7 +285,7 @@ def llama8b_prefix_share(poison=True, partition_size=0, structure_only=False):
                    handout=handout, note=f"{len(handout)} unique blocks", structure_only=structure_only)
 
 
-def longctx_verify(poison=True, partition_size=512, structure_only=False):
+def longctx_verify(poison=True, partition_size=0, structure_only=False):
     """B=16, GQA 32/8, D=128, lengths ~ U[16384,65536], T=4 causal verify queries."""
     rng = np.random.Generator(np.random.PCG64(5))
     lens = rng.integers(16384, 65536, size=16, endpoint=True)
