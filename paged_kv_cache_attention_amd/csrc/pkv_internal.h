@@ -2,6 +2,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <mutex>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -37,14 +39,62 @@ bool stream_supported(const DecodeArgs& a);
 size_t stream_workspace_bytes(int B, int T, int Hq, int D);
 hipError_t launch_decode_stream(const DecodeArgs& a, void* workspace, hipStream_t stream);
 
+// Shared-prefix groups (single-token decode, bf16): runs of consecutive
+// sequences whose tables start with the same physical block, cut into groups
+// of at most group_members(G) members inside aligned windows of kGroupWindow
+// sequences.  The blocks a member has in common with the group's longest
+// member are attended once per group on MFMA (all members' query rows
+// together); the rest goes through the balanced path and the two are merged.
+constexpr int kGroupWindow = 16;
+constexpr int kGroupChunks = 4;      // partials per member (chunks of a group's prefix)
+constexpr int kGroupMinShare = 4;    // blocks in common before a group pays off
+inline int group_members(int G) { return 64 / G < kGroupWindow ? 64 / G : kGroupWindow; }   // G <= 32
+__host__ __device__ inline int group_chunk_blocks(int d) {
+  const int c = (d + kGroupChunks - 1) / kGroupChunks;
+  return c > 8 ? c : 8;
+}
+
+struct GroupPlan {
+  int* sfx;        // [B] blocks of the sequence attended by its group (0: not grouped)
+  int* nch;        // [B] chunk partials of the sequence's group (0: not grouped)
+  int* cnt;        // [B] chunks of the group led by this sequence (0 unless leader)
+  int4* desc;      // [B] leader: {canonical, members, shared blocks, V row limit}
+  int* clist;      // [B * kGroupChunks / 2] leader * kGroupChunks + chunk
+  float* part;     // [B][kGroupChunks][Hq][D + 1] normalised partials and lse
+};
+bool groups_supported(const DecodeArgs& a);
+size_t group_workspace_bytes(int B, int Hq, int D);
+GroupPlan group_plan_layout(void* base, int B, int Hq, int D);
+hipError_t launch_group_detect(const DecodeArgs& a, const GroupPlan& gp, hipStream_t stream);
+hipError_t launch_group_prefix(const DecodeArgs& a, const GroupPlan& gp, const int* hdr, int grid, hipStream_t stream);
+
+// Per-device side stream (default priority, created on first use and kept
+// for the life of the process) with a fork and a join event, and the
+// device's CU count.  Record fork -> side waits -> side work -> record join ->
+// main waits, all under group_side_mutex(), so that calls from several host
+// threads never interleave their records and waits.
+struct GroupSide {
+  hipStream_t stream;
+  hipEvent_t fork, join;
+  int cus;
+};
+hipError_t group_side(GroupSide* out);
+std::mutex& group_side_mutex();
+
 // VALU decode kernel: any T (one query token per work item), Hq/Hkv in {1,2,4,8}.
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
 
 // Planning kernel shared by the balanced paths: blocks per (t, b) pair with
-// the causal limit of query token t, their prefix sums, the range length and
-// each range's first pair (B*T <= kStreamMaxTB).
-hipError_t launch_plan(const int32_t* lens, int B, int T, int ranges, int max_tokens, int* hdr, int* prefix, int* first,
-                       hipStream_t stream);
+// the causal limit of query token t, their prefix sums, the range length, the
+// compact list of non-empty pairs (udesc, nu + 1 entries with a sentinel) and
+// each range's first non-empty pair as an index into that list
+// (B*T <= kStreamMaxTB).  hdr = {total, per range, total, group chunks, nu}.
+// With `sfx` (T = 1 only) the first sfx[b] blocks of sequence b are left out
+// of its unit, and the chunks of every group leader (cnt) are listed in clist;
+// hdr[3] receives the number of listed chunks.
+hipError_t launch_plan(const int32_t* lens, int B, int T, int ranges, int max_blocks, int* hdr, int* prefix, int* first,
+                       int4* udesc, hipStream_t stream, const int* sfx = nullptr, const int* nch = nullptr,
+                       const int* cnt = nullptr, int* clist = nullptr);
 
 // MFMA verify tile for bf16 with 2 <= T and T * (Hq/Hkv) <= 16 query rows per
 // KV head; balanced like the VALU path, with its own workspace layout.

@@ -24,6 +24,8 @@
 //   * p is broadcast back along the row with DPP and multiplies the lane's
 //     own V chunk into fp32 accumulators;
 //   * K and V of the next PD blocks are in flight while a block is processed.
+#include <mutex>
+
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -44,8 +46,12 @@ struct StreamArgs {
   DecodeArgs a;
   const int* hdr;      // [total, per, tbtot]
   const int* prefix;   // [TB + 1]
-  const int* first;    // [ranges] first (t, b) pair of each range, -1 if idle
+  const int* first;    // [ranges] first non-empty unit (compact index) of each range, -1 if idle
+  const int4* udesc;   // [nu + 1] non-empty units: {tb, flat start, table offset, visible tokens}
   float* part;         // partial slots [(ranges + TB)][Hq][D + 1]
+  const int* gsfx;     // [B] leading blocks attended by the sequence's group, or null
+  const int* gnch;     // [B] group partials to merge (0: not grouped), or null
+  const float* gpart;  // [B][kGroupChunks][Hq][D + 1]
   int TB;
   int ranges;          // workgroups splitting the block list
 };
@@ -174,45 +180,86 @@ template <> __device__ __forceinline__ void store_chunk<float>(void* dst, const 
 }
 
 // ---------------------------------------------------------------------------
-// Planning: blocks per (t, b), their prefix sums, and each wave's first unit.
+// Planning: blocks per (t, b) unit, their prefix sums, the compact list of
+// non-empty units with everything a wave needs to walk them, and each range's
+// first non-empty unit.
 // ---------------------------------------------------------------------------
 constexpr int kPlanThreads = 1024;
 
-__device__ __forceinline__ int unit_blocks(const int32_t* lens, int tb, int B, int T, int max_tokens) {
+__device__ __forceinline__ int unit_visible(const int32_t* lens, int tb, int B, int T, int max_tokens) {
   const int t = tb / B, b = tb - t * B;
   const int L = clampi(lens[b], 0, max_tokens);
-  const int vis = L - T + t + 1;
-  return vis > 0 ? (vis + kBS - 1) / kBS : 0;
+  return max(0, L - T + t + 1);
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ lens, int B, int T,
-                                                            int ranges, int max_tokens, int TB, int* __restrict__ hdr,
-                                                            int* __restrict__ prefix, int* __restrict__ first) {
+                                                            int ranges, int max_blocks, int TB, int* __restrict__ hdr,
+                                                            int* __restrict__ prefix, int* __restrict__ first,
+                                                            int4* __restrict__ udesc, const int* __restrict__ sfx,
+                                                            const int* __restrict__ nch, const int* __restrict__ cnt,
+                                                            int* __restrict__ clist) {
   __shared__ int part[kPlanThreads];
-  __shared__ int spref[kStreamMaxTB + 1];
+  __shared__ int npart[kPlanThreads];
+  __shared__ int cpart[kPlanThreads];
+  __shared__ int spref[kStreamMaxTB + 1];   // flat start of each non-empty unit
   const int tid = threadIdx.x;
+  const int max_tokens = max_blocks * kBS;
   const int per_t = (TB + kPlanThreads - 1) / kPlanThreads;
   const int s0 = min(TB, tid * per_t), s1 = min(TB, s0 + per_t);
-  int sum = 0;
-  for (int i = s0; i < s1; ++i) sum += unit_blocks(lens, i, B, T, max_tokens);
+  auto blocks_of = [&](int i, int vis) {
+    const int nb = (vis + kBS - 1) / kBS;
+    return sfx ? nb - sfx[i] : nb;   // sfx only with T = 1 (i = b)
+  };
+  int sum = 0, ne = 0, csum = 0;
+  for (int i = s0; i < s1; ++i) {
+    const int nb = blocks_of(i, unit_visible(lens, i, B, T, max_tokens));
+    sum += nb;
+    ne += nb > 0;
+    if (cnt) csum += cnt[i];
+  }
   part[tid] = sum;
+  npart[tid] = ne;
+  cpart[tid] = csum;
   __syncthreads();
   for (int off = 1; off < kPlanThreads; off <<= 1) {
     const int v = tid >= off ? part[tid - off] : 0;
+    const int nv = tid >= off ? npart[tid - off] : 0;
+    const int cv = tid >= off ? cpart[tid - off] : 0;
     __syncthreads();
     part[tid] += v;
+    npart[tid] += nv;
+    cpart[tid] += cv;
     __syncthreads();
   }
   int run = tid ? part[tid - 1] : 0;
+  int krun = tid ? npart[tid - 1] : 0;
+  int crun = tid ? cpart[tid - 1] : 0;
   for (int i = s0; i < s1; ++i) {
-    spref[i] = run;
     prefix[i] = run;
-    run += unit_blocks(lens, i, B, T, max_tokens);
+    const int vis = unit_visible(lens, i, B, T, max_tokens);
+    const int nb = blocks_of(i, vis);
+    if (nb > 0) {
+      const int b = i % B;
+      const int sb = sfx ? sfx[i] : 0;
+      const bool grouped = nch && nch[i] > 0;
+      // {unit, flat start, table offset of its first block, visible tokens (negative: merged with a group)}
+      udesc[krun] = make_int4(i, run, b * max_blocks + sb, grouped ? -vis : vis);
+      spref[krun] = run;
+      ++krun;
+    }
+    run += nb;
+    if (cnt) {
+      const int c = cnt[i];
+      for (int k = 0; k < c; ++k) clist[crun + k] = i * kGroupChunks + k;
+      crun += c;
+    }
   }
   const int tbtot = part[kPlanThreads - 1];
+  const int nu = npart[kPlanThreads - 1];
   if (tid == 0) {
-    spref[TB] = tbtot;
     prefix[TB] = tbtot;
+    spref[nu] = tbtot;
+    udesc[nu] = make_int4(0, tbtot, 0, 0);   // sentinel: start of "unit nu" = end of the list
   }
   __syncthreads();
   const int per = max(kMinBlocksPerRange, (tbtot + ranges - 1) / ranges);
@@ -220,6 +267,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     hdr[0] = tbtot;
     hdr[1] = per;
     hdr[2] = tbtot;
+    hdr[3] = cpart[kPlanThreads - 1];
+    hdr[4] = nu;
   }
   for (int w = tid; w < ranges; w += kPlanThreads) {
     const long long F0 = (long long)w * per;
@@ -228,8 +277,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
       continue;
     }
     const int r = (int)F0;
-    // largest i with spref[i] <= r (skips empty pairs)
-    int lo = 0, hi = TB;   // spref[lo] <= r < spref[hi]
+    int lo = 0, hi = nu;   // spref[lo] <= r < spref[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (spref[mid] <= r) lo = mid; else hi = mid;
@@ -240,9 +288,27 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 
 // ---------------------------------------------------------------------------
 // The persistent decode kernel.
+//
+// A wave walks the flat blocks [F0, F1) of its range as one continuous
+// stream.  Per chunk of 64 flat blocks each lane resolves one block: its unit
+// (binary search over the starts of a window of 64 consecutive non-empty
+// units), its physical id (table gather) and whether a unit starts or ends
+// there.  The next chunk is resolved while the current one is processed, the
+// descriptor and query of the next unit are loaded while the current unit
+// runs, and the K/V prefetch runs across unit and chunk boundaries, so the
+// memory pipeline only drains at the end of the range.
 // ---------------------------------------------------------------------------
+constexpr int kResolveAt = 4;   // step of a full chunk at which the next chunk is resolved
+
+// The chunk loop is laid out so that every value loaded ahead is consumed at
+// a fixed distance (in issued loads) from its load: the first kResolveAt steps
+// of a full chunk are unrolled before the next chunk is resolved, the middle
+// steps run a loop of constant trip count and the last PD steps, which
+// prefetch from the next chunk, are unrolled after it.  The compiler's wait
+// counts are then exact instead of draining the prefetch queue.
 template <typename ET, int D, int GW, int PD>
-__global__ __launch_bounds__(64 * kMaxU) void stream_decode_kernel(StreamArgs sa, float scale_log2e) {
+__global__ __launch_bounds__(64 * kMaxU) void stream_decode_kernel(StreamArgs sa, const int4* __restrict__ udesc,
+                                                                 float scale_log2e) {
   using G = SGeo<ET, D, GW>;
   using ST = typename Storage<ET>::T;
   const DecodeArgs& a = sa.a;
@@ -251,11 +317,10 @@ __global__ __launch_bounds__(64 * kMaxU) void stream_decode_kernel(StreamArgs sa
   const int wpg = blockDim.x >> 6;                      // waves per workgroup
   const int rng = blockIdx.x / (U / wpg);               // block range of this workgroup
   const int u = (blockIdx.x % (U / wpg)) * wpg + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int total = sa.hdr[0], per = sa.hdr[1];
+  const int total = sa.hdr[0], per = sa.hdr[1], nu = sa.hdr[4];
   const int F0 = rng * per;
   if (F0 >= total) return;
   const int F1 = min(total, F0 + per);
-  int tb = sa.first[rng];
 
   const int c = lane % G::NC;
   const int grp = lane / G::NC;
@@ -263,165 +328,255 @@ __global__ __launch_bounds__(64 * kMaxU) void stream_decode_kernel(StreamArgs sa
   const int tg = grp / G::KW;
   const bool upper_half = (lane & 8) != 0;
   const int lc = c / GW;            // load index of this lane's score combo
-  const int gc = c % GW;            // head (within the KV group) of that combo
   const int G_ratio = a.Hq / a.Hkv;
   const size_t block_bytes = (size_t)kBS * a.Hkv * G::RB;
   const uint32_t load_step = (uint32_t)(G::RPL * a.Hkv * G::RB);
   const int nmax = a.N_blocks - 1;
-  const int max_tokens = a.max_blocks * kBS;
+  const int h0 = u * kHPW;
+  const int kv0 = h0 / G_ratio;
+  const uint32_t lane_off = (uint32_t)(((tg * a.Hkv) + kv0 + kl) * G::RB + c * 16);
+  const unsigned char* kpool = static_cast<const unsigned char*>(a.k_pool) + lane_off;
+  const unsigned char* vpool = static_cast<const unsigned char*>(a.v_pool) + lane_off;
 
-  while (true) {
-    const int t = tb / a.B, b = tb - t * a.B;
-    const int pstart = sa.prefix[tb], plen = sa.prefix[tb + 1] - pstart;
-    const int ustart = pstart;
-    const int js = max(F0, ustart) - ustart;
-    const int je = min(F1, ustart + plen) - ustart;
-    const bool direct = ustart >= F0 && ustart + plen <= F1;
-
-    if (je > js) {
-      const int L = clampi(a.context_lens[b], 0, max_tokens);
-      // visible tokens of the unit, cut at the end of this wave's piece
-      const int hi = min(L - a.T + t + 1, je * kBS);
-      const int h0 = u * kHPW;
-      const int kv0 = h0 / G_ratio;
-      const uint32_t lane_off = (uint32_t)(((tg * a.Hkv) + kv0 + kl) * G::RB + c * 16);
-      const unsigned char* kpool = static_cast<const unsigned char*>(a.k_pool) + lane_off;
-      const unsigned char* vpool = static_cast<const unsigned char*>(a.v_pool) + lane_off;
-      const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks;
-
-      u32x4_t qreg[GW];
-      {
-        const unsigned char* qp = reinterpret_cast<const unsigned char*>(static_cast<const ST*>(a.q)) +
-                                  (((size_t)(b * a.T + t) * a.Hq + h0 + kl * GW) * D) * G::EB + c * 16;
+  // ---- chunk resolution ----
+  auto window = [&](int kc, int4& w, int& ue) {
+    w = udesc[min(kc + lane, nu)];
+    ue = udesc[min(kc + lane + 1, nu)].y;
+  };
+  // Resolves flat blocks Fc + lane against the window of units starting at
+  // wbase; returns the first unit of the following chunk.
+  auto resolve = [&](int Fc, int wbase, const int4& w, int ue, int& phys, int& flags) {
+    const int f = min(Fc + lane, F1 - 1);
+    int pos = 0;
 #pragma unroll
-        for (int g = 0; g < GW; ++g) qreg[g] = load16(qp + (size_t)g * G::RB);
-      }
+    for (int step = 32; step >= 1; step >>= 1) {
+      const int cand = pos + step;
+      if (__shfl(w.y, cand) <= f) pos = cand;
+    }
+    const int us = __shfl(w.y, pos), tofs = __shfl(w.z, pos), uen = __shfl(ue, pos);
+    phys = a.block_tables[tofs + (f - us)];   // clamped where it is read
+    flags = Fc + lane < F1 ? ((f == us || f == F0) ? 1 : 0) | ((f + 1 == uen || f + 1 == F1) ? 2 : 0) : 0;
+    return wbase + __builtin_amdgcn_readlane(pos, 63) + ((__builtin_amdgcn_readlane(flags, 63) & 2) ? 1 : 0);
+  };
 
-      float m_lane = kNegInf;   // running max of this lane's head (base 2)
-      float l_part = 0.f;
-      float acc[GW][G::EC];
+  int Fc = F0;
+  const int kfirst = sa.first[rng];
+  int4 wv; int wue;
+  int cphys, cflags, nphys = 0, nflags = 0;
+  window(kfirst, wv, wue);
+  int wbase = resolve(Fc, kfirst, wv, wue, cphys, cflags);   // window base of the next chunk
+  bool has_next = Fc + 64 < F1;
+  if (has_next) window(wbase, wv, wue);
+
+  // ---- unit staging ----
+  // The descriptors and query chunks of the next kStage units are staged at
+  // once: descriptors in registers (lane s holds unit kbase + s), queries in
+  // LDS.  Beginning a unit then issues no memory operation, so the K/V
+  // prefetch keeps running across unit boundaries; the stage itself waits for
+  // its loads and is refilled every kStage units.
+  constexpr int kStage = 8;
+  constexpr int QCH = G::NC * G::KW;          // distinct 16-byte query chunks per head
+  static_assert(GW * QCH <= 64, "one staged chunk per lane");
+  __shared__ __attribute__((aligned(16))) u32x4_t qlds[kMaxU][kStage][GW][QCH];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int sl = lane % (GW * QCH);             // lanes past GW * QCH repeat a chunk
+  const int sg = sl / QCH, sr = sl % QCH;        // chunk this lane stages: head sg, chunk sr
+  const int skl = sr / G::NC, sc = sr % G::NC;
+  int kbase = 0;
+  int4 sd;          // lane s: descriptor of unit kbase + s
+  int se = 0;       // lane s: flat start of unit kbase + s + 1 (its end)
+  auto stage = [&](int kb) {
+    kbase = kb;
+    sd = udesc[min(kb + lane, nu)];
+    se = udesc[min(kb + lane + 1, nu)].y;
+    u32x4_t tmp[kStage];
+#pragma unroll
+    for (int s = 0; s < kStage; ++s) {
+      const int tb_s = __builtin_amdgcn_readlane(sd.x, s);
+      const int t = tb_s / a.B, b = tb_s - t * a.B;
+      const unsigned char* qp = reinterpret_cast<const unsigned char*>(static_cast<const ST*>(a.q)) +
+                                (((size_t)(b * a.T + t) * a.Hq + h0 + skl * GW + sg) * D) * G::EB + sc * 16;
+      tmp[s] = load16(qp);
+    }
+    // consume every staged register here, so that no later use waits on these loads
+    __asm__ volatile("" ::"v"(sd.y), "v"(sd.z), "v"(sd.w), "v"(se));
+    if (lane < GW * QCH) {
+#pragma unroll
+      for (int s = 0; s < kStage; ++s) qlds[wave][s][sg][sr] = tmp[s];
+    }
+  };
+  int knext = kfirst;               // unit that begins next
+  stage(kfirst);
+  u32x4_t qreg[GW];
+
+  // current unit
+  int tb = 0, kb_off = 0, hi = 0;
+  bool direct = false;
+  float m_lane = kNegInf, l_part = 0.f;
+  float acc[GW][G::EC];
+
+  auto begin_unit = [&]() {
+    if (knext - kbase == kStage) stage(knext);
+    const int s = knext - kbase;
+    ++knext;
+    tb = __builtin_amdgcn_readlane(sd.x, s);
+    const int ustart = __builtin_amdgcn_readlane(sd.y, s);
+    const int tofs = __builtin_amdgcn_readlane(sd.z, s);
+    const int hv = __builtin_amdgcn_readlane(sd.w, s);
+    const int uend = __builtin_amdgcn_readlane(se, s);
+#pragma unroll
+    for (int g = 0; g < GW; ++g) qreg[g] = qlds[wave][s][g][kl * G::NC + c];
+    const int b = tb % a.B;
+    kb_off = (tofs - b * a.max_blocks) - ustart;   // logical block = flat index + kb_off
+    hi = hv < 0 ? -hv : hv;
+    direct = hv >= 0 && ustart >= F0 && uend <= F1;
+    m_lane = kNegInf;
+    l_part = 0.f;
+#pragma unroll
+    for (int g = 0; g < GW; ++g)
+#pragma unroll
+      for (int e = 0; e < G::EC; ++e) acc[g][e] = 0.f;
+  };
+
+  auto end_unit = [&]() {
+    // combine token groups and lanes of each head, then store
+    const float l_head = head_reduce<G::NC, GW, G::KW, false>(l_part);
+#pragma unroll
+    for (int bit = 0; bit < 6; ++bit) {
+      const int m = 1 << bit;
+      if (m < G::NC * G::KW) continue;       // tg bits only
 #pragma unroll
       for (int g = 0; g < GW; ++g)
 #pragma unroll
-        for (int e = 0; e < G::EC; ++e) acc[g][e] = 0.f;
-
-      const int nb = je - js;
-      u32x4_t kbuf[PD][G::LOADS], vbuf[PD][G::LOADS];
-      int tbl = 0, cn = 0;
-      // Loads are fenced from the scheduler: left alone it sinks them next to
-      // their use to shorten register live ranges, which undoes the prefetch.
-      auto load_block = [&](u32x4_t (&dst)[G::LOADS], const unsigned char* pool, int ph) {
-        const unsigned char* base = pool + (size_t)ph * block_bytes;
-        __builtin_amdgcn_sched_barrier(0);
+        for (int e = 0; e < G::EC; ++e) acc[g][e] += __shfl_xor(acc[g][e], m);
+    }
+    if (tg == 0) {
+      const int t = tb / a.B, b = tb - t * a.B;
+      const size_t row0 = ((size_t)b * a.T + t) * a.Hq + h0;
+      float* slot = sa.part + ((size_t)(rng + tb) * a.Hq + h0) * (D + 1);
 #pragma unroll
-        for (int l = 0; l < G::LOADS; ++l) {
-#ifdef PKV_NT_LOADS
-          dst[l] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(base + l * load_step));
-#else
-          dst[l] = load16(base + l * load_step);
-#endif
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      };
-      auto phys = [&](int i) { return __builtin_amdgcn_readlane(tbl, i < cn ? i : cn - 1); };
-
-      auto body = [&](u32x4_t (&kcur)[G::LOADS], u32x4_t (&vcur)[G::LOADS], int kb, int i) {
-        const int ph_ahead = phys(i + PD);
-        // scores: partial dots of this lane's chunk, then reduce-scatter along the row
-        float part[G::NCOMB];
+      for (int g = 0; g < GW; ++g) {
+        const int hh = kl * GW + g;            // head within the unit
+        const float lh = __shfl(l_head, grp * G::NC + g);
+        const float mh = __shfl(m_lane, grp * G::NC + g);
+        float o[G::EC];
 #pragma unroll
-        for (int l = 0; l < G::LOADS; ++l)
+        for (int e = 0; e < G::EC; ++e) o[e] = lh != 0.f ? acc[g][e] / lh : 0.f;
+        const float lse = lh != 0.f ? (mh + log2f(lh)) * kLn2 : kNegInf;
+        if (direct) {
+          store_chunk<ET>(static_cast<unsigned char*>(a.out) + ((row0 + hh) * D + c * G::EC) * G::EB, o);
+          if (c == 0 && a.lse_out) a.lse_out[row0 + hh] = lse;
+        } else {
+          float* od = slot + hh * (D + 1) + c * G::EC;
 #pragma unroll
-          for (int g = 0; g < GW; ++g) part[l * GW + g] = chunk_dot4<ET>(kcur[l], qreg[g], 0.f);
-        load_block(kcur, kpool, ph_ahead);
-        const float sc = reduce_scatter<G::NC>(part, c);
-        const int tok = kb * kBS + lc * G::RPL + tg;
-        const bool valid = tok < hi;
-        const float s2 = valid ? sc * scale_log2e : kNegInf;
-        if (__builtin_amdgcn_ballot_w64(s2 > m_lane + kSlack)) {
-          const float m_new = fmaxf(m_lane, head_reduce<G::NC, GW, G::KW, true>(s2));
-          // 1 while a head is still empty (both -inf), 0 on its first key
-          const float alpha = m_lane == m_new ? 1.f : __builtin_amdgcn_exp2f(m_lane - m_new);
-          l_part *= alpha;
-          m_lane = m_new;
-#pragma unroll
-          for (int g = 0; g < GW; ++g) {
-            const float ag = __shfl(alpha, grp * G::NC + g);
-#pragma unroll
-            for (int e = 0; e < G::EC; ++e) acc[g][e] *= ag;
-          }
-        }
-        const float p = valid ? __builtin_amdgcn_exp2f(s2 - m_lane) : 0.f;
-        l_part += p;
-        // acc += p * V; V of tokens past the end is zeroed (never multiply poison by 0)
-#pragma unroll
-        for (int l = 0; l < G::LOADS; ++l) {
-          const bool vvalid = kb * kBS + l * G::RPL + tg < hi;
-          const u32x4_t vz{0u, 0u, 0u, 0u};
-          float vf[G::EC];
-          widen<ET>(vvalid ? vcur[l] : vz, vf);
-#pragma unroll
-          for (int g = 0; g < GW; ++g) {
-            const float pb = group_bcast<G::NC>(p, l * GW + g, upper_half);
-#pragma unroll
-            for (int e = 0; e < G::EC; ++e) acc[g][e] = fmaf(pb, vf[e], acc[g][e]);
-          }
-        }
-        load_block(vcur, vpool, ph_ahead);
-      };
-
-      for (int c0 = 0; c0 < nb; c0 += 64) {
-        cn = min(64, nb - c0);
-        tbl = lane < cn ? clampi(trow[js + c0 + lane], 0, nmax) : 0;
-#pragma unroll
-        for (int s = 0; s < PD; ++s) {
-          load_block(kbuf[s], kpool, phys(s));
-          load_block(vbuf[s], vpool, phys(s));
-        }
-        for (int i = 0; i < cn; i += PD) {
-#pragma unroll
-          for (int s = 0; s < PD; ++s) body(kbuf[s], vbuf[s], js + c0 + i + s, i + s);
-        }
-      }
-
-      // ---- finish the piece: combine token groups and lanes of each head ----
-      const float l_head = head_reduce<G::NC, GW, G::KW, false>(l_part);
-#pragma unroll
-      for (int bit = 0; bit < 6; ++bit) {
-        const int m = 1 << bit;
-        if (m < G::NC * G::KW) continue;       // tg bits only
-#pragma unroll
-        for (int g = 0; g < GW; ++g)
-#pragma unroll
-          for (int e = 0; e < G::EC; ++e) acc[g][e] += __shfl_xor(acc[g][e], m);
-      }
-      if (tg == 0) {
-        const size_t row0 = ((size_t)b * a.T + t) * a.Hq + h0;
-        float* slot = sa.part + ((size_t)(rng + tb) * a.Hq + h0) * (D + 1);
-#pragma unroll
-        for (int g = 0; g < GW; ++g) {
-          const int hh = kl * GW + g;            // head within the unit
-          const float lh = __shfl(l_head, grp * G::NC + g);
-          const float mh = __shfl(m_lane, grp * G::NC + g);
-          float o[G::EC];
-#pragma unroll
-          for (int e = 0; e < G::EC; ++e) o[e] = lh != 0.f ? acc[g][e] / lh : 0.f;
-          const float lse = lh != 0.f ? (mh + log2f(lh)) * kLn2 : kNegInf;
-          if (direct) {
-            store_chunk<ET>(static_cast<unsigned char*>(a.out) + ((row0 + hh) * D + c * G::EC) * G::EB, o);
-            if (c == 0 && a.lse_out) a.lse_out[row0 + hh] = lse;
-          } else {
-            float* od = slot + hh * (D + 1) + c * G::EC;
-#pragma unroll
-            for (int e = 0; e < G::EC; e += 4) store16(od + e, u32x4_t{__float_as_uint(o[e]), __float_as_uint(o[e + 1]),
-                                                                        __float_as_uint(o[e + 2]), __float_as_uint(o[e + 3])});
-            if (c == 0) slot[hh * (D + 1) + D] = lse;
-          }
+          for (int e = 0; e < G::EC; e += 4) store16(od + e, u32x4_t{__float_as_uint(o[e]), __float_as_uint(o[e + 1]),
+                                                                      __float_as_uint(o[e + 2]), __float_as_uint(o[e + 3])});
+          if (c == 0) slot[hh * (D + 1) + D] = lse;
         }
       }
     }
-    if (ustart + plen >= F1) break;
-    ++tb;
+  };
+
+  u32x4_t kbuf[PD][G::LOADS], vbuf[PD][G::LOADS];
+  // Loads are fenced from the scheduler: left alone it sinks them next to
+  // their use to shorten register live ranges, which undoes the prefetch.
+  auto load_block = [&](u32x4_t (&dst)[G::LOADS], const unsigned char* pool, int ph) {
+    const unsigned char* base = pool + (size_t)ph * block_bytes;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int l = 0; l < G::LOADS; ++l) dst[l] = load16(base + l * load_step);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto rl = [&](int v, int j) { return clampi(__builtin_amdgcn_readlane(v, j), 0, nmax); };
+
+  auto body = [&](u32x4_t (&kcur)[G::LOADS], u32x4_t (&vcur)[G::LOADS], int kb, int ph_ahead) {
+    // scores: partial dots of this lane's chunk, then reduce-scatter along the row
+    float part[G::NCOMB];
+#pragma unroll
+    for (int l = 0; l < G::LOADS; ++l)
+#pragma unroll
+      for (int g = 0; g < GW; ++g) part[l * GW + g] = chunk_dot4<ET>(kcur[l], qreg[g], 0.f);
+    load_block(kcur, kpool, ph_ahead);
+    const float sc = reduce_scatter<G::NC>(part, c);
+    const int tok = kb * kBS + lc * G::RPL + tg;
+    const bool valid = tok < hi;
+    const float s2 = valid ? sc * scale_log2e : kNegInf;
+    if (__builtin_amdgcn_ballot_w64(s2 > m_lane + kSlack)) {
+      const float m_new = fmaxf(m_lane, head_reduce<G::NC, GW, G::KW, true>(s2));
+      // 1 while a head is still empty (both -inf), 0 on its first key
+      const float alpha = m_lane == m_new ? 1.f : __builtin_amdgcn_exp2f(m_lane - m_new);
+      l_part *= alpha;
+      m_lane = m_new;
+#pragma unroll
+      for (int g = 0; g < GW; ++g) {
+        const float ag = __shfl(alpha, grp * G::NC + g);
+#pragma unroll
+        for (int e = 0; e < G::EC; ++e) acc[g][e] *= ag;
+      }
+    }
+    const float p = valid ? __builtin_amdgcn_exp2f(s2 - m_lane) : 0.f;
+    l_part += p;
+    // acc += p * V; V of tokens past the end is zeroed (never multiply poison by 0)
+#pragma unroll
+    for (int l = 0; l < G::LOADS; ++l) {
+      const bool vvalid = kb * kBS + l * G::RPL + tg < hi;
+      const u32x4_t vz{0u, 0u, 0u, 0u};
+      float vf[G::EC];
+      widen<ET>(vvalid ? vcur[l] : vz, vf);
+#pragma unroll
+      for (int g = 0; g < GW; ++g) {
+        const float pb = group_bcast<G::NC>(p, l * GW + g, upper_half);
+#pragma unroll
+        for (int e = 0; e < G::EC; ++e) acc[g][e] = fmaf(pb, vf[e], acc[g][e]);
+      }
+    }
+    load_block(vcur, vpool, ph_ahead);
+  };
+
+#pragma unroll
+  for (int s = 0; s < PD; ++s) {
+    const int ph = rl(cphys, s);
+    load_block(kbuf[s], kpool, ph);
+    load_block(vbuf[s], vpool, ph);
+  }
+
+  auto step = [&](u32x4_t (&kb)[G::LOADS], u32x4_t (&vb)[G::LOADS], int ii, int ph_ahead) {
+    const int fl = __builtin_amdgcn_readlane(cflags, ii);
+    if (fl & 1) begin_unit();
+    body(kb, vb, Fc + ii + kb_off, ph_ahead);
+    if (fl & 2) end_unit();
+  };
+
+  while (true) {
+    if (has_next) {   // a full chunk of 64 blocks with another one after it
+#pragma unroll
+      for (int ii = 0; ii < kResolveAt; ii += PD)
+#pragma unroll
+        for (int s = 0; s < PD; ++s) step(kbuf[s], vbuf[s], ii + s, rl(cphys, ii + s + PD));
+      const int wnext = resolve(Fc + 64, wbase, wv, wue, nphys, nflags);
+      for (int ii = kResolveAt; ii < 64 - PD; ii += PD)
+#pragma unroll
+        for (int s = 0; s < PD; ++s) step(kbuf[s], vbuf[s], ii + s, rl(cphys, ii + s + PD));
+#pragma unroll
+      for (int s = 0; s < PD; ++s) step(kbuf[s], vbuf[s], 64 - PD + s, rl(nphys, s));
+      Fc += 64;
+      cphys = nphys;
+      cflags = nflags;
+      wbase = wnext;
+      has_next = Fc + 64 < F1;
+      if (has_next) window(wbase, wv, wue);
+    } else {
+      // The last chunk: 1 .. 64 blocks; lanes past the end repeat the last
+      // block.  A pad step (cnt odd with PD = 2) has no unit events and runs
+      // after the range's last unit has been stored, so it only touches dead
+      // state; it keeps the load count per step constant.
+      const int cnt = F1 - Fc;
+      for (int i = 0; i < cnt; i += PD) {
+#pragma unroll
+        for (int s = 0; s < PD; ++s) step(kbuf[s], vbuf[s], i + s, rl(cphys, min(i + s + PD, 63)));
+      }
+      break;
+    }
   }
 }
 
@@ -450,17 +605,42 @@ __global__ __launch_bounds__(256) void stream_merge_kernel(StreamArgs sa) {
   const size_t orow = (((size_t)b * a.T + t) * a.Hq + u * kHPW + h) * D + d0;
   OT* out = static_cast<OT*>(a.out) + orow;
   float* lse_out = a.lse_out ? a.lse_out + ((size_t)b * a.T + t) * a.Hq + u * kHPW + h : nullptr;
-  if (plen == 0) {   // nothing visible: out = 0, lse = -inf
+  const int gch = sa.gnch ? sa.gnch[b] : 0;   // group partials of this sequence (T = 1)
+  if (plen == 0 && gch == 0) {   // nothing visible: out = 0, lse = -inf
 #pragma unroll
     for (int e = 0; e < EPL; ++e) store_out<ET>(out + e, 0.f);
     if (lse_out && (lane & 15) == 0) *lse_out = kNegInf;
     return;
   }
-  const int w0 = (int)(ustart / per), w1 = (int)((ustart + plen - 1) / per);
-  if (w0 == w1) return;   // finished by one wave
+  const int w0 = plen ? (int)(ustart / per) : 0, w1 = plen ? (int)((ustart + plen - 1) / per) : -1;
+  if (w0 == w1 && gch == 0) return;   // finished by one wave
   float m = kNegInf, ssum = 0.f, acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  if (gch > 0) {
+    float lv[kGroupChunks], ov[kGroupChunks][EPL];
+#pragma unroll
+    for (int k = 0; k < kGroupChunks; ++k) {
+      lv[k] = kNegInf;
+      if (k < gch) {
+        const float* slot = sa.gpart + (((size_t)b * kGroupChunks + k) * a.Hq + u * kHPW + h) * (D + 1);
+        lv[k] = slot[D];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) ov[k][e] = slot[d0 + e];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kGroupChunks; ++k) {
+      if (lv[k] == kNegInf) continue;
+      const float nm = fmaxf(m, lv[k]);
+      const float sa_ = __builtin_amdgcn_exp2f((m - nm) * kLog2e);
+      const float sb = __builtin_amdgcn_exp2f((lv[k] - nm) * kLog2e);
+      ssum = ssum * sa_ + sb;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = acc[e] * sa_ + sb * ov[k][e];
+      m = nm;
+    }
+  }
   for (int w = w0; w <= w1; w += BATCH) {
     float lv[BATCH], ov[BATCH][EPL];
 #pragma unroll
@@ -491,42 +671,51 @@ __global__ __launch_bounds__(256) void stream_merge_kernel(StreamArgs sa) {
   if (lse_out && (lane & 15) == 0) *lse_out = ssum != 0.f ? m + logf(ssum) : kNegInf;
 }
 
+// `join`: an event the merge must wait for (the group partials), or null.
 template <typename ET, int D, int GW>
-hipError_t launch_s(const StreamArgs& sa, hipStream_t stream) {
+hipError_t launch_s(const StreamArgs& sa, hipStream_t stream, hipEvent_t join) {
   constexpr int LOADS = SGeo<ET, D, GW>::LOADS;
 #ifdef PKV_STREAM_PD
   constexpr int PD = PKV_STREAM_PD;
 #else
-  // Two blocks in flight per wave: measured as fast as four on the 8B-shaped
-  // batch (deeper prefetch only lengthens memory queues) and half the VGPRs.
-  constexpr int PD = LOADS >= 16 ? 1 : 2;
+  // One block ahead per wave: with the block stream running across unit
+  // boundaries this measured faster than two (8B- and 1B-shaped batches) and
+  // needs 60 fewer VGPRs.
+  constexpr int PD = 1;
+  (void)LOADS;
 #endif
   const float sl2 = sa.a.scale * kLog2e;
   const int U = sa.a.Hq / kHPW;
   const int wpg = U < kMaxU ? U : kMaxU;
   hipLaunchKernelGGL((stream_decode_kernel<ET, D, GW, PD>), dim3(sa.ranges * (U / wpg)), dim3(64 * wpg), 0, stream,
-                     sa, sl2);
+                     sa, sa.udesc, sl2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (join && (e = hipStreamWaitEvent(stream, join, 0)) != hipSuccess) return e;
   const int G = (sa.a.Hq / kHPW) * sa.TB;
   hipLaunchKernelGGL((stream_merge_kernel<ET, D>), dim3((G + 3) / 4), dim3(256), 0, stream, sa);
   return hipGetLastError();
 }
 
 template <typename ET, int D>
-hipError_t launch_sd(const StreamArgs& sa, hipStream_t stream) {
+hipError_t launch_sd(const StreamArgs& sa, hipStream_t stream, hipEvent_t join) {
   const int G = sa.a.Hq / sa.a.Hkv;
-  if (G >= 4) return launch_s<ET, D, 4>(sa, stream);
-  if (G == 2) return launch_s<ET, D, 2>(sa, stream);
-  return launch_s<ET, D, 1>(sa, stream);
+  if (G >= 4) return launch_s<ET, D, 4>(sa, stream, join);
+  if (G == 2) return launch_s<ET, D, 2>(sa, stream, join);
+  return launch_s<ET, D, 1>(sa, stream, join);
+}
+
+hipError_t launch_main(const StreamArgs& sa, hipStream_t stream, hipEvent_t join) {
+  if (sa.a.bf16) return sa.a.D == 64 ? launch_sd<Bf16, 64>(sa, stream, join) : launch_sd<Bf16, 128>(sa, stream, join);
+  return launch_sd<float, 64>(sa, stream, join);
 }
 
 }  // namespace
 
-hipError_t launch_plan(const int32_t* lens, int B, int T, int ranges, int max_tokens, int* hdr, int* prefix, int* first,
-                       hipStream_t stream) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, lens, B, T, ranges, max_tokens, B * T, hdr,
-                     prefix, first);
+hipError_t launch_plan(const int32_t* lens, int B, int T, int ranges, int max_blocks, int* hdr, int* prefix, int* first,
+                       int4* udesc, hipStream_t stream, const int* sfx, const int* nch, const int* cnt, int* clist) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, lens, B, T, ranges, max_blocks, B * T, hdr,
+                     prefix, first, udesc, sfx, nch, cnt, clist);
   return hipGetLastError();
 }
 
@@ -537,8 +726,10 @@ size_t stream_workspace_bytes(int B, int T, int Hq, int D) {
   const size_t R = (size_t)stream_ranges(Hq);
   size_t off = 256;                                       // header
   off += ((TB + 1) * 4 + 255) / 256 * 256;                // prefix
-  off += (R * 4 + 255) / 256 * 256;                       // first pair per range
+  off += (R * 4 + 255) / 256 * 256;                       // first unit per range
+  off += ((TB + 1) * 16 + 255) / 256 * 256;               // unit descriptors
   off += (R + TB) * Hq * (D + 1) * 4;                     // partial slots
+  if (T == 1) off += 256 + group_workspace_bytes(B, Hq, D);   // shared-prefix groups (256-aligned)
   return off;
 }
 
@@ -559,13 +750,38 @@ hipError_t launch_decode_stream(const DecodeArgs& a, void* workspace, hipStream_
   int* hdr = reinterpret_cast<int*>(ws);
   int* prefix = reinterpret_cast<int*>(ws + 256);
   int* first = reinterpret_cast<int*>(ws + 256 + ((size_t)(sa.TB + 1) * 4 + 255) / 256 * 256);
-  float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(first) +
-                                         ((size_t)sa.ranges * 4 + 255) / 256 * 256);
-  sa.hdr = hdr; sa.prefix = prefix; sa.first = first; sa.part = part;
-  hipError_t e = launch_plan(a.context_lens, a.B, a.T, sa.ranges, a.max_blocks * kBS, hdr, prefix, first, stream);
+  int4* udesc = reinterpret_cast<int4*>(reinterpret_cast<unsigned char*>(first) +
+                                        ((size_t)sa.ranges * 4 + 255) / 256 * 256);
+  float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(udesc) +
+                                         ((size_t)(sa.TB + 1) * 16 + 255) / 256 * 256);
+  sa.hdr = hdr; sa.prefix = prefix; sa.first = first; sa.udesc = udesc; sa.part = part;
+  hipError_t e;
+#ifndef PKV_NO_GROUPS
+  if (groups_supported(a)) {
+    const size_t part_bytes = ((size_t)stream_ranges(a.Hq) + sa.TB) * a.Hq * (a.D + 1) * 4;
+    const GroupPlan gp = group_plan_layout(reinterpret_cast<unsigned char*>(part) + (part_bytes + 255) / 256 * 256,
+                                           a.B, a.Hq, a.D);
+    sa.gsfx = gp.sfx; sa.gnch = gp.nch; sa.gpart = gp.part;
+    if ((e = launch_group_detect(a, gp, stream)) != hipSuccess) return e;
+    e = launch_plan(a.context_lens, a.B, a.T, sa.ranges, a.max_blocks, hdr, prefix, first, udesc, stream, gp.sfx, gp.nch,
+                    gp.cnt, gp.clist);
+    if (e != hipSuccess) return e;
+    // The group kernel runs beside the decode kernel on the device's side
+    // stream (forked after the plan, joined before the merge); both fit on
+    // every CU at once, so the group work hides under the block stream.
+    GroupSide side;
+    if ((e = group_side(&side)) != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(group_side_mutex());
+    if ((e = hipEventRecord(side.fork, stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(side.stream, side.fork, 0)) != hipSuccess) return e;
+    if ((e = launch_group_prefix(a, gp, hdr, side.cus, side.stream)) != hipSuccess) return e;
+    if ((e = hipEventRecord(side.join, side.stream)) != hipSuccess) return e;
+    return launch_main(sa, stream, side.join);
+  }
+#endif
+  e = launch_plan(a.context_lens, a.B, a.T, sa.ranges, a.max_blocks, hdr, prefix, first, udesc, stream);
   if (e != hipSuccess) return e;
-  if (a.bf16) return a.D == 64 ? launch_sd<Bf16, 64>(sa, stream) : launch_sd<Bf16, 128>(sa, stream);
-  return launch_sd<float, 64>(sa, stream);
+  return launch_main(sa, stream, nullptr);
 }
 
 }  // namespace pkv

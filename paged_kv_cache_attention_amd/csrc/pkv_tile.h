@@ -1,0 +1,253 @@
+// A 16-row attention tile on MFMA (gfx950), shared by the multi-query verify
+// kernel and the shared-prefix group kernel.
+//
+// One wave owns up to 16 query rows that read the same KV head.  Per 16-token
+// block of the cache:
+//   S^T[token][row] = K[token][:] . Q[row][:]      v_mfma_f32_16x16x32_bf16
+//     A = K straight from 16-byte global loads (lane: token lane%16, d chunk
+//     32c + 8*(lane/16)); B = Q^T from registers (same chunking).  The result
+//     leaves row lane%16 and tokens 4*(lane/16) .. +3 in each lane.
+//   online softmax per row (running max in base-2 units, raised lazily)
+//   O[row][d] += P[row][token] . V[token][d]       v_mfma_f32_16x16x16_bf16
+//     A = P in exactly the S^T layout, split into bf16 hi + lo parts so the
+//     product keeps about 16 bits of P; B = V transposed through a padded
+//     LDS tile (272-byte rows: writes and reads are bank-conflict free).
+// K and V of the next PD blocks are in flight while a block is processed.
+#pragma once
+
+#include "pkv_device.h"
+
+namespace pkv {
+namespace tile {
+
+constexpr int kBS = 16;
+constexpr int kVRow = 272;   // padded LDS row (bytes) of a staged token: conflict-free for D <= 128
+constexpr float kSlack = 8.f;
+
+typedef __bf16 bf16x4_v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ bf16x8_v as_bf16x8(u32x4_t v) {
+  bf16x8_v r;
+  __builtin_memcpy(&r, &v, sizeof(r));
+  return r;
+}
+__device__ __forceinline__ uint32_t pack_bf16(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
+
+template <int D>
+struct State {
+  floatx4_t acc[D / 16];   // O rows 4*(lane/16) + k, column 16*d + lane%16
+  float m_row;             // running max of row lane%16 (base 2)
+  float l_part;            // this lane's share of row lane%16's denominator
+};
+
+template <int D>
+__device__ __forceinline__ void init(State<D>& st) {
+#pragma unroll
+  for (int d = 0; d < D / 16; ++d) st.acc[d] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  st.m_row = kNegInf;
+  st.l_part = 0.f;
+}
+
+// Q^T operand of this lane's row: 16 bytes per MFMA step; rows outside the
+// tile (row_ok false) read a safe row and are zeroed.
+template <int D>
+__device__ __forceinline__ void load_q(u32x4_t (&qreg)[D / 32], const uint16_t* qrow, bool row_ok, int lane) {
+  const unsigned char* qp = reinterpret_cast<const unsigned char*>(qrow) + (lane >> 4) * 16;
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    const u32x4_t v = load16(qp + c * 64);
+    qreg[c] = row_ok ? v : u32x4_t{0u, 0u, 0u, 0u};
+  }
+}
+
+// Process logical blocks [kb0, kb0 + nb) whose physical ids are trow[0 .. nb).
+// hi_row: keys of this lane's row with position < hi_row are visible.
+// vlimit: V rows at positions >= vlimit are zeroed before use (they may hold
+// poison, and p = 0 there).  kpool/vpool point at this lane's 16-byte chunk
+// of token 0 of physical block 0 of the KV head.
+template <int D, int PD>
+__device__ __forceinline__ void run(State<D>& st, const u32x4_t (&qreg)[D / 32], int hi_row, int vlimit,
+                                    const int32_t* trow, int kb0, int nb, int nmax, const unsigned char* kpool,
+                                    const unsigned char* vpool, size_t block_bytes, unsigned char* vtile,
+                                    float scale_log2e, int lane) {
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  const int row = lane & 15, quad = lane >> 4;
+  hi_row = min(hi_row, (kb0 + nb) * kBS);   // pad steps past the range stay masked
+  u32x4_t kbuf[PD][KS], vbuf[PD][KS];
+  int tbl = 0, cn = 0;
+  auto load_block = [&](u32x4_t (&dst)[KS], const unsigned char* pool, int ph) {
+    const unsigned char* base = pool + (size_t)ph * block_bytes;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < KS; ++c) dst[c] = load16(base + c * 64);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto phys = [&](int i) { return __builtin_amdgcn_readlane(tbl, i < cn ? i : cn - 1); };
+
+  auto body = [&](u32x4_t (&kcur)[KS], u32x4_t (&vcur)[KS], int kb, int i) {
+    const int ph_ahead = phys(i + PD);
+    const bool vok = kb * kBS + row < vlimit;
+#pragma unroll
+    for (int c = 0; c < KS; ++c)
+      store16(vtile + row * kVRow + (32 * c + 8 * quad) * 2, vok ? vcur[c] : u32x4_t{0u, 0u, 0u, 0u});
+    floatx4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < KS; ++c) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kcur[c]), as_bf16x8(qreg[c]), s, 0, 0, 0);
+    load_block(kcur, kpool, ph_ahead);
+    load_block(vcur, vpool, ph_ahead);
+    const int tok0 = kb * kBS + 4 * quad;
+    float sv[4];
+    bool need = false;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      sv[k] = tok0 + k < hi_row ? s[k] * scale_log2e : kNegInf;
+      need |= sv[k] > st.m_row + kSlack;
+    }
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(st.m_row, mx);
+      // 1 for rows that are still empty (both -inf), 0 on a row's first key
+      const float alpha = st.m_row == m_new ? 1.f : __builtin_amdgcn_exp2f(st.m_row - m_new);
+      st.l_part *= alpha;
+      st.m_row = m_new;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float ak = __shfl(alpha, 4 * quad + k);
+#pragma unroll
+        for (int d = 0; d < DT; ++d) st.acc[d][k] *= ak;
+      }
+    }
+    uint16_t ph[4], pl[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float p = sv[k] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(sv[k] - st.m_row);
+      st.l_part += p;
+      ph[k] = f32_to_bf16_rne(p);
+      pl[k] = f32_to_bf16_rne(p - __uint_as_float((uint32_t)ph[k] << 16));
+    }
+    bf16x4_v phi, plo;
+    {
+      const uint32_t h2[2] = {pack_bf16(ph[0], ph[1]), pack_bf16(ph[2], ph[3])};
+      const uint32_t l2[2] = {pack_bf16(pl[0], pl[1]), pack_bf16(pl[2], pl[3])};
+      __builtin_memcpy(&phi, h2, 8);
+      __builtin_memcpy(&plo, l2, 8);
+    }
+    __asm__ volatile("" ::: "memory");
+    const uint16_t* vt16 = reinterpret_cast<const uint16_t*>(vtile);
+#pragma unroll
+    for (int d = 0; d < DT; ++d) {
+      const int col = 16 * d + row;
+      uint16_t vv[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) vv[k] = vt16[((4 * quad + k) * kVRow) / 2 + col];
+      bf16x4_v bv;
+      const uint32_t v2[2] = {pack_bf16(vv[0], vv[1]), pack_bf16(vv[2], vv[3])};
+      __builtin_memcpy(&bv, v2, 8);
+      st.acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, st.acc[d], 0, 0, 0);
+      st.acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, st.acc[d], 0, 0, 0);
+    }
+    __asm__ volatile("" ::: "memory");
+  };
+
+  for (int c0 = 0; c0 < nb; c0 += 64) {
+    cn = min(64, nb - c0);
+    tbl = lane < cn ? clampi(trow[c0 + lane], 0, nmax) : 0;
+#pragma unroll
+    for (int s = 0; s < PD; ++s) {
+      load_block(kbuf[s], kpool, phys(s));
+      load_block(vbuf[s], vpool, phys(s));
+    }
+    for (int i = 0; i < cn; i += PD) {
+#pragma unroll
+      for (int s = 0; s < PD; ++s) body(kbuf[s], vbuf[s], kb0 + c0 + i + s, i + s);
+    }
+  }
+}
+
+// Same tile step with K and V already staged in LDS by the workgroup:
+// nblk blocks, token row r (0 .. 16*nblk) at ks + r * ROW (K) and
+// vs + r * ROW (V; rows past the last visible position zeroed by the
+// stager).  kb0 is the logical index of the first staged block.  ROW = 2D + 16
+// bytes keeps the row reads bank-conflict free.
+template <int D, int ROW = 2 * D + 16>
+__device__ __forceinline__ void run_lds(State<D>& st, const u32x4_t (&qreg)[D / 32], int hi_row, int kb0, int nblk,
+                                        const unsigned char* ks, const unsigned char* vs, float scale_log2e,
+                                        int lane) {
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  const int row = lane & 15, quad = lane >> 4;
+  for (int j = 0; j < nblk; ++j) {
+    const unsigned char* kr = ks + (j * kBS + row) * ROW + quad * 16;
+    floatx4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < KS; ++c) {
+      const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(kr + c * 64);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv), as_bf16x8(qreg[c]), s, 0, 0, 0);
+    }
+    const int tok0 = (kb0 + j) * kBS + 4 * quad;
+    float sv[4];
+    bool need = false;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      sv[k] = tok0 + k < hi_row ? s[k] * scale_log2e : kNegInf;
+      need |= sv[k] > st.m_row + kSlack;
+    }
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(st.m_row, mx);
+      const float alpha = st.m_row == m_new ? 1.f : __builtin_amdgcn_exp2f(st.m_row - m_new);
+      st.l_part *= alpha;
+      st.m_row = m_new;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float ak = __shfl(alpha, 4 * quad + k);
+#pragma unroll
+        for (int d = 0; d < DT; ++d) st.acc[d][k] *= ak;
+      }
+    }
+    uint16_t ph[4], pl[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float p = sv[k] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(sv[k] - st.m_row);
+      st.l_part += p;
+      ph[k] = f32_to_bf16_rne(p);
+      pl[k] = f32_to_bf16_rne(p - __uint_as_float((uint32_t)ph[k] << 16));
+    }
+    bf16x4_v phi, plo;
+    {
+      const uint32_t h2[2] = {pack_bf16(ph[0], ph[1]), pack_bf16(ph[2], ph[3])};
+      const uint32_t l2[2] = {pack_bf16(pl[0], pl[1]), pack_bf16(pl[2], pl[3])};
+      __builtin_memcpy(&phi, h2, 8);
+      __builtin_memcpy(&plo, l2, 8);
+    }
+    const uint16_t* vt16 = reinterpret_cast<const uint16_t*>(vs + j * kBS * ROW);
+#pragma unroll
+    for (int d = 0; d < DT; ++d) {
+      const int col = 16 * d + row;
+      uint16_t vv[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) vv[k] = vt16[((4 * quad + k) * ROW) / 2 + col];
+      bf16x4_v bv;
+      const uint32_t v2[2] = {pack_bf16(vv[0], vv[1]), pack_bf16(vv[2], vv[3])};
+      __builtin_memcpy(&bv, v2, 8);
+      st.acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, st.acc[d], 0, 0, 0);
+      st.acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, st.acc[d], 0, 0, 0);
+    }
+  }
+}
+
+// Row totals after the range: l summed over the 4 lanes of each row.
+template <int D>
+__device__ __forceinline__ float row_sum(const State<D>& st) {
+  float l = st.l_part + __shfl_xor(st.l_part, 16);
+  return l + __shfl_xor(l, 32);
+}
+
+}  // namespace tile
+}  // namespace pkv

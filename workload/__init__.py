@@ -207,6 +207,29 @@ def uniform_batch(name, *, seed, B, T, Hq, Hkv, D, dtype, lens, pool_blocks=None
                    max_blocks=max_blocks, poison=poison, append=append, note=note)
 
 
+def batch_from_block_lists(name, *, seed, T, Hq, Hkv, D, dtype, lens, per_seq_blocks, max_blocks=None,
+                           pool_blocks=None, partition_size=0, poison=True, note=""):
+    """Batch with an explicit block structure: ``per_seq_blocks[b]`` lists the
+    logical block keys of sequence b (equal keys = one shared physical block).
+
+    Physical ids come from a seeded permutation of the pool, handed out in
+    first-seen key order; the pool defaults to ceil(1.1 * distinct keys)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = np.asarray(lens, dtype=np.int64)
+    for b, L in enumerate(lens):
+        if len(per_seq_blocks[b]) != _cdiv(int(L), BLOCK_SIZE):
+            raise ValueError(f"sequence {b}: {len(per_seq_blocks[b])} blocks for {int(L)} tokens")
+    used = len(dict.fromkeys(k for keys in per_seq_blocks for k in keys))
+    if pool_blocks is None:
+        pool_blocks = max(used + 1, _cdiv(11 * used, 10))
+    if max_blocks is None:
+        max_blocks = max(1, max(len(k) for k in per_seq_blocks))
+    perm = rng.permutation(pool_blocks)
+    return _finish(name, rng=rng, B=len(lens), T=T, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, partition_size=partition_size,
+                   context_lens=lens, per_seq_blocks=per_seq_blocks, n_blocks_total=pool_blocks, perm=perm,
+                   max_blocks=max_blocks, poison=poison, append=False, note=note)
+
+
 # ---------------------------------------------------------------------------
 # The five workloads.  Seeds equal the workload number.
 # ---------------------------------------------------------------------------
