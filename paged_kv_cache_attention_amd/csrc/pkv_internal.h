@@ -3,7 +3,6 @@
 
 #include <hip/hip_runtime.h>
 
-#include <mutex>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -48,6 +47,7 @@ hipError_t launch_decode_stream(const DecodeArgs& a, void* workspace, hipStream_
 constexpr int kGroupWindow = 16;
 constexpr int kGroupChunks = 4;      // partials per member (chunks of a group's prefix)
 constexpr int kGroupMinShare = 4;    // blocks in common before a group pays off
+constexpr int kGroupMaxB = 1024;     // detection runs inside the planning workgroup
 inline int group_members(int G) { return 64 / G < kGroupWindow ? 64 / G : kGroupWindow; }   // G <= 32
 __host__ __device__ inline int group_chunk_blocks(int d) {
   const int c = (d + kGroupChunks - 1) / kGroupChunks;
@@ -57,29 +57,19 @@ __host__ __device__ inline int group_chunk_blocks(int d) {
 struct GroupPlan {
   int* sfx;        // [B] blocks of the sequence attended by its group (0: not grouped)
   int* nch;        // [B] chunk partials of the sequence's group (0: not grouped)
-  int* cnt;        // [B] chunks of the group led by this sequence (0 unless leader)
   int4* desc;      // [B] leader: {canonical, members, shared blocks, V row limit}
   int* clist;      // [B * kGroupChunks / 2] leader * kGroupChunks + chunk
   float* part;     // [B][kGroupChunks][Hq][D + 1] normalised partials and lse
 };
+// Off unless PKV_PREFIX_GROUPS=1 (read on every call): on MI355X the 256 MB
+// last-level cache already serves most re-reads of a shared prefix, and the
+// detection and the group workgroups cost more than they save on the
+// prefix-sharing 8B-shaped batch (measured 243 us with groups, 238 us without).
+bool groups_enabled();
 bool groups_supported(const DecodeArgs& a);
 size_t group_workspace_bytes(int B, int Hq, int D);
 GroupPlan group_plan_layout(void* base, int B, int Hq, int D);
-hipError_t launch_group_detect(const DecodeArgs& a, const GroupPlan& gp, hipStream_t stream);
-hipError_t launch_group_prefix(const DecodeArgs& a, const GroupPlan& gp, const int* hdr, int grid, hipStream_t stream);
-
-// Per-device side stream (default priority, created on first use and kept
-// for the life of the process) with a fork and a join event, and the
-// device's CU count.  Record fork -> side waits -> side work -> record join ->
-// main waits, all under group_side_mutex(), so that calls from several host
-// threads never interleave their records and waits.
-struct GroupSide {
-  hipStream_t stream;
-  hipEvent_t fork, join;
-  int cus;
-};
-hipError_t group_side(GroupSide* out);
-std::mutex& group_side_mutex();
+int device_cus();   // compute units of the current device (cached)
 
 // VALU decode kernel: any T (one query token per work item), Hq/Hkv in {1,2,4,8}.
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
@@ -89,12 +79,21 @@ hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
 // compact list of non-empty pairs (udesc, nu + 1 entries with a sentinel) and
 // each range's first non-empty pair as an index into that list
 // (B*T <= kStreamMaxTB).  hdr = {total, per range, total, group chunks, nu}.
-// With `sfx` (T = 1 only) the first sfx[b] blocks of sequence b are left out
-// of its unit, and the chunks of every group leader (cnt) are listed in clist;
-// hdr[3] receives the number of listed chunks.
+// With `gp` non-null (T = 1 only) the planning workgroup first detects the
+// shared-prefix groups (gp->sfx, nch, desc), leaves the first sfx[b] blocks of
+// sequence b out of its unit and lists the chunks of every group in
+// gp->clist; hdr[3] receives the number of listed chunks.
+// With `fin` the planning kernel also writes the result of every unit with
+// no visible token (out = 0, lse = -inf), which no decode wave visits.
+struct PlanFinish {
+  void* out;         // [B, T, Hq, D]
+  float* lse_out;    // [B, T, Hq] or null
+  int Hq, D;
+  bool bf16;
+};
 hipError_t launch_plan(const int32_t* lens, int B, int T, int ranges, int max_blocks, int* hdr, int* prefix, int* first,
-                       int4* udesc, hipStream_t stream, const int* sfx = nullptr, const int* nch = nullptr,
-                       const int* cnt = nullptr, int* clist = nullptr);
+                       int4* udesc, hipStream_t stream, const GroupPlan* gp = nullptr,
+                       const int32_t* tables = nullptr, int G = 1, const PlanFinish* fin = nullptr);
 
 // MFMA verify tile for bf16 with 2 <= T and T * (Hq/Hkv) <= 16 query rows per
 // KV head; balanced like the VALU path, with its own workspace layout.

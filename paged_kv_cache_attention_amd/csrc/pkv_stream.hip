@@ -24,9 +24,10 @@
 //   * p is broadcast back along the row with DPP and multiplies the lane's
 //     own V chunk into fp32 accumulators;
 //   * K and V of the next PD blocks are in flight while a block is processed.
-#include <mutex>
+#include <type_traits>
 
 #include "pkv_device.h"
+#include "pkv_group.h"
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -36,7 +37,7 @@ constexpr int kBS = 16;
 constexpr int kHPW = 4;              // query heads per work unit
 constexpr int kWaves = kStreamWaves;   // about 8 waves per CU
 #ifndef PKV_STREAM_WPG
-#define PKV_STREAM_WPG 8
+#define PKV_STREAM_WPG 4
 #endif
 constexpr int kMaxU = PKV_STREAM_WPG;  // head groups (waves) per workgroup
 constexpr int kMinBlocksPerRange = 16;
@@ -49,9 +50,9 @@ struct StreamArgs {
   const int* first;    // [ranges] first non-empty unit (compact index) of each range, -1 if idle
   const int4* udesc;   // [nu + 1] non-empty units: {tb, flat start, table offset, visible tokens}
   float* part;         // partial slots [(ranges + TB)][Hq][D + 1]
-  const int* gsfx;     // [B] leading blocks attended by the sequence's group, or null
-  const int* gnch;     // [B] group partials to merge (0: not grouped), or null
-  const float* gpart;  // [B][kGroupChunks][Hq][D + 1]
+  GroupPlan gp;        // shared-prefix groups (when `groups`)
+  bool groups;
+  int stream_wgs;      // decode workgroups; any further workgroups run group items
   int TB;
   int ranges;          // workgroups splitting the block list
 };
@@ -195,27 +196,33 @@ __device__ __forceinline__ int unit_visible(const int32_t* lens, int tb, int B, 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ lens, int B, int T,
                                                             int ranges, int max_blocks, int TB, int* __restrict__ hdr,
                                                             int* __restrict__ prefix, int* __restrict__ first,
-                                                            int4* __restrict__ udesc, const int* __restrict__ sfx,
-                                                            const int* __restrict__ nch, const int* __restrict__ cnt,
-                                                            int* __restrict__ clist) {
+                                                            int4* __restrict__ udesc, GroupPlan gp, bool groups,
+                                                            const int32_t* __restrict__ tables, int GM,
+                                                            PlanFinish fin, bool finish) {
   __shared__ int part[kPlanThreads];
   __shared__ int npart[kPlanThreads];
   __shared__ int cpart[kPlanThreads];
   __shared__ int spref[kStreamMaxTB + 1];   // flat start of each non-empty unit
+  __shared__ int ssfx[kGroupMaxB], snch[kGroupMaxB], scnt[kGroupMaxB];
   const int tid = threadIdx.x;
   const int max_tokens = max_blocks * kBS;
+  if (groups) {   // T = 1 and B <= kGroupMaxB: one wave per window of sequences
+    for (int w0 = (tid >> 6) * kGroupWindow; w0 < B; w0 += (kPlanThreads / 64) * kGroupWindow)
+      grp::detect_window(w0, tables, lens, B, max_blocks, GM, gp, ssfx, snch, scnt);
+    __syncthreads();
+  }
   const int per_t = (TB + kPlanThreads - 1) / kPlanThreads;
   const int s0 = min(TB, tid * per_t), s1 = min(TB, s0 + per_t);
   auto blocks_of = [&](int i, int vis) {
     const int nb = (vis + kBS - 1) / kBS;
-    return sfx ? nb - sfx[i] : nb;   // sfx only with T = 1 (i = b)
+    return groups ? nb - ssfx[i] : nb;   // groups only with T = 1 (i = b)
   };
   int sum = 0, ne = 0, csum = 0;
   for (int i = s0; i < s1; ++i) {
     const int nb = blocks_of(i, unit_visible(lens, i, B, T, max_tokens));
     sum += nb;
     ne += nb > 0;
-    if (cnt) csum += cnt[i];
+    if (groups) csum += scnt[i];
   }
   part[tid] = sum;
   npart[tid] = ne;
@@ -240,17 +247,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     const int nb = blocks_of(i, vis);
     if (nb > 0) {
       const int b = i % B;
-      const int sb = sfx ? sfx[i] : 0;
-      const bool grouped = nch && nch[i] > 0;
+      const int sb = groups ? ssfx[i] : 0;
+      const bool grouped = groups && snch[i] > 0;
       // {unit, flat start, table offset of its first block, visible tokens (negative: merged with a group)}
       udesc[krun] = make_int4(i, run, b * max_blocks + sb, grouped ? -vis : vis);
       spref[krun] = run;
       ++krun;
     }
     run += nb;
-    if (cnt) {
-      const int c = cnt[i];
-      for (int k = 0; k < c; ++k) clist[crun + k] = i * kGroupChunks + k;
+    if (groups) {
+      const int c = scnt[i];
+      for (int k = 0; k < c; ++k) gp.clist[crun + k] = i * kGroupChunks + k;
       crun += c;
     }
   }
@@ -269,6 +276,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     hdr[2] = tbtot;
     hdr[3] = cpart[kPlanThreads - 1];
     hdr[4] = nu;
+  }
+  if (finish) {
+    // units with nothing visible: out = 0, lse = -inf
+    for (int i = s0; i < s1; ++i) {
+      const int nb = blocks_of(i, unit_visible(lens, i, B, T, max_tokens));
+      if (nb > 0) continue;
+      const int t = i / B, b = i - t * B;
+      const size_t row = ((size_t)b * T + t) * fin.Hq;
+      for (int e = 0; e < fin.Hq * fin.D; ++e) {
+        if (fin.bf16) static_cast<uint16_t*>(fin.out)[row * fin.D + e] = 0;
+        else static_cast<float*>(fin.out)[row * fin.D + e] = 0.f;
+      }
+      if (fin.lse_out)
+        for (int h = 0; h < fin.Hq; ++h) fin.lse_out[row + h] = kNegInf;
+    }
   }
   for (int w = tid; w < ranges; w += kPlanThreads) {
     const long long F0 = (long long)w * per;
@@ -306,11 +328,106 @@ constexpr int kResolveAt = 4;   // step of a full chunk at which the next chunk 
 // steps run a loop of constant trip count and the last PD steps, which
 // prefetch from the next chunk, are unrolled after it.  The compiler's wait
 // counts are then exact instead of draining the prefetch queue.
-template <typename ET, int D, int GW, int PD>
-__global__ __launch_bounds__(64 * kMaxU) void stream_decode_kernel(StreamArgs sa, const int4* __restrict__ udesc,
-                                                                 float scale_log2e) {
+// Log-sum-exp merge of the pieces of one unit cut by range boundaries, for
+// the four heads of head group u, by one wave: lanes 16h .. 16h+15 hold head
+// h, D/16 elements each.  Pieces come from the partial slots of ranges w0 .. w1
+// (slot of range w: w + tb), loaded in batches of BATCH with all loads issued
+// together and merged online (running max, rescaled sum and accumulator).
+// gch > 0 adds that many group partials of sequence b first.
+template <typename ET, int D, int BATCH>
+__device__ __forceinline__ void merge_pieces(const DecodeArgs& a, const float* part, int tb, int u, int w0, int w1,
+                                             int lane, const float* gpart = nullptr, int gch = 0) {
+  constexpr int EPL = D / 16;
+  using OT = typename Storage<ET>::T;
+  const int t = tb / a.B, b = tb - t * a.B;
+  const int h = lane >> 4, d0 = (lane & 15) * EPL;
+  const size_t orow = (((size_t)b * a.T + t) * a.Hq + u * kHPW + h) * D + d0;
+  OT* out = static_cast<OT*>(a.out) + orow;
+  float* lse_out = a.lse_out ? a.lse_out + ((size_t)b * a.T + t) * a.Hq + u * kHPW + h : nullptr;
+  float m = kNegInf, ssum = 0.f, acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  auto absorb = [&](float lv, const float* ov) {
+    if (lv == kNegInf) return;   // absent or empty piece: its o is not read
+    const float nm = fmaxf(m, lv);
+    const float sa_ = __builtin_amdgcn_exp2f((m - nm) * kLog2e);
+    const float sb = __builtin_amdgcn_exp2f((lv - nm) * kLog2e);
+    ssum = ssum * sa_ + sb;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = acc[e] * sa_ + sb * ov[e];
+    m = nm;
+  };
+  if (gch > 0) {
+    float lv[kGroupChunks], ov[kGroupChunks][EPL];
+#pragma unroll
+    for (int k = 0; k < kGroupChunks; ++k) {
+      lv[k] = kNegInf;
+      if (k < gch) {
+        const float* slot = gpart + (((size_t)b * kGroupChunks + k) * a.Hq + u * kHPW + h) * (D + 1);
+        lv[k] = slot[D];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) ov[k][e] = slot[d0 + e];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kGroupChunks; ++k) absorb(lv[k], ov[k]);
+  }
+  for (int w = w0; w <= w1; w += BATCH) {
+    float lv[BATCH], ov[BATCH][EPL];
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      lv[k] = kNegInf;
+      if (w + k <= w1) {
+        const float* slot = part + ((size_t)(w + k + tb) * a.Hq + u * kHPW + h) * (D + 1);
+        lv[k] = slot[D];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) ov[k][e] = slot[d0 + e];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) absorb(lv[k], ov[k]);
+  }
+  const float inv = ssum != 0.f ? 1.f / ssum : 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) store_out<ET>(out + e, acc[e] * inv);
+  if (lse_out && (lane & 15) == 0) *lse_out = ssum != 0.f ? m + logf(ssum) : kNegInf;
+}
+
+constexpr int kStage = 8;   // units whose descriptors and queries are staged at a time
+
+// GROUPS: the instantiation also runs shared-prefix group items on the
+// workgroups past stream_wgs (bf16, D in {64, 128}, four waves per workgroup).
+template <typename ET, int D, int GW, bool GROUPS>
+struct StreamLds {
+  static constexpr int QCH = SGeo<ET, D, GW>::NC * SGeo<ET, D, GW>::KW;   // distinct 16-byte query chunks per head
+  static constexpr int QBYTES = kMaxU * kStage * GW * QCH * 16;
+  static constexpr bool G_OK = GROUPS && std::is_same<ET, Bf16>::value && (D == 64 || D == 128) &&
+                               kMaxU == grp::kTiles;
+  static constexpr int GBYTES = G_OK ? grp::Stage<D>::BYTES : 0;
+  static constexpr int BYTES = QBYTES > GBYTES ? QBYTES : GBYTES;
+};
+
+// With groups, three waves per SIMD (<= 168 VGPRs): two decode workgroups
+// and one group workgroup per CU.  The widest geometry (one head per KV head,
+// 16 loads per block) keeps two waves per SIMD rather than spill.
+template <typename ET, int D, int GW, bool GROUPS>
+constexpr int stream_waves_per_eu() { return GROUPS && SGeo<ET, D, GW>::LOADS < 16 ? 3 : 2; }
+
+template <typename ET, int D, int GW, int PD, bool GROUPS>
+__global__ __launch_bounds__(64 * kMaxU) __attribute__((amdgpu_waves_per_eu(stream_waves_per_eu<ET, D, GW, GROUPS>())))
+void stream_decode_kernel(StreamArgs sa, const int4* __restrict__ udesc, float scale_log2e) {
   using G = SGeo<ET, D, GW>;
   using ST = typename Storage<ET>::T;
+  using LD = StreamLds<ET, D, GW, GROUPS>;
+  // one LDS buffer: staged queries on decode workgroups, staged K/V on group ones
+  __shared__ __attribute__((aligned(16))) unsigned char lds[LD::BYTES];
+  if constexpr (LD::G_OK) {
+    if ((int)blockIdx.x >= sa.stream_wgs) {
+      grp::group_items<D>(sa.a, sa.gp, sa.hdr[3] * sa.a.Hkv, blockIdx.x - sa.stream_wgs, gridDim.x - sa.stream_wgs, lds,
+                          scale_log2e);
+      return;
+    }
+  }
   const DecodeArgs& a = sa.a;
   const int lane = threadIdx.x & 63;
   const int U = a.Hq / kHPW;
@@ -374,10 +491,9 @@ __global__ __launch_bounds__(64 * kMaxU) void stream_decode_kernel(StreamArgs sa
   // LDS.  Beginning a unit then issues no memory operation, so the K/V
   // prefetch keeps running across unit boundaries; the stage itself waits for
   // its loads and is refilled every kStage units.
-  constexpr int kStage = 8;
-  constexpr int QCH = G::NC * G::KW;          // distinct 16-byte query chunks per head
+  constexpr int QCH = LD::QCH;
   static_assert(GW * QCH <= 64, "one staged chunk per lane");
-  __shared__ __attribute__((aligned(16))) u32x4_t qlds[kMaxU][kStage][GW][QCH];
+  u32x4_t (*qlds)[kStage][GW][QCH] = reinterpret_cast<u32x4_t (*)[kStage][GW][QCH]>(lds);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int sl = lane % (GW * QCH);             // lanes past GW * QCH repeat a chunk
   const int sg = sl / QCH, sr = sl % QCH;        // chunk this lane stages: head sg, chunk sr
@@ -585,95 +701,59 @@ __global__ __launch_bounds__(64 * kMaxU) void stream_decode_kernel(StreamArgs sa
 // ---------------------------------------------------------------------------
 template <typename ET, int D>
 __global__ __launch_bounds__(256) void stream_merge_kernel(StreamArgs sa) {
-  // One wave per unit: lanes 16h .. 16h+15 hold head h, EPL elements each.
-  // The pieces' (o, lse) are loaded in batches of 8 with all loads issued
-  // together, and merged online: running max, rescaled sum and accumulator.
-  constexpr int EPL = D / 16;
-  constexpr int BATCH = 8;
+  // One wave per (unit, head group): units cut by ranges and, with groups,
+  // every grouped sequence (its group partials plus its own pieces).
   using OT = typename Storage<ET>::T;
   const DecodeArgs& a = sa.a;
   const int lane = threadIdx.x & 63;
-  const int gidx = blockIdx.x * 4 + (threadIdx.x >> 6);   // (t, b) pair and head group
+  const int gidx = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int U = a.Hq / kHPW;
   if (gidx >= U * sa.TB) return;
   const int per = sa.hdr[1];
   const int tb = gidx / U, u = gidx - tb * U;
   const int t = tb / a.B, b = tb - t * a.B;
   const int pstart = sa.prefix[tb], plen = sa.prefix[tb + 1] - pstart;
-  const long long ustart = pstart;
-  const int h = lane >> 4, d0 = (lane & 15) * EPL;
-  const size_t orow = (((size_t)b * a.T + t) * a.Hq + u * kHPW + h) * D + d0;
-  OT* out = static_cast<OT*>(a.out) + orow;
-  float* lse_out = a.lse_out ? a.lse_out + ((size_t)b * a.T + t) * a.Hq + u * kHPW + h : nullptr;
-  const int gch = sa.gnch ? sa.gnch[b] : 0;   // group partials of this sequence (T = 1)
+  const int gch = sa.groups ? sa.gp.nch[b] : 0;   // group partials of this sequence (T = 1)
   if (plen == 0 && gch == 0) {   // nothing visible: out = 0, lse = -inf
+    constexpr int EPL = D / 16;
+    const int h = lane >> 4, d0 = (lane & 15) * EPL;
+    OT* out = static_cast<OT*>(a.out) + (((size_t)b * a.T + t) * a.Hq + u * kHPW + h) * D + d0;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) store_out<ET>(out + e, 0.f);
-    if (lse_out && (lane & 15) == 0) *lse_out = kNegInf;
+    if (a.lse_out && (lane & 15) == 0) a.lse_out[((size_t)b * a.T + t) * a.Hq + u * kHPW + h] = kNegInf;
     return;
   }
-  const int w0 = plen ? (int)(ustart / per) : 0, w1 = plen ? (int)((ustart + plen - 1) / per) : -1;
-  if (w0 == w1 && gch == 0) return;   // finished by one wave
-  float m = kNegInf, ssum = 0.f, acc[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  if (gch > 0) {
-    float lv[kGroupChunks], ov[kGroupChunks][EPL];
-#pragma unroll
-    for (int k = 0; k < kGroupChunks; ++k) {
-      lv[k] = kNegInf;
-      if (k < gch) {
-        const float* slot = sa.gpart + (((size_t)b * kGroupChunks + k) * a.Hq + u * kHPW + h) * (D + 1);
-        lv[k] = slot[D];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) ov[k][e] = slot[d0 + e];
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kGroupChunks; ++k) {
-      if (lv[k] == kNegInf) continue;
-      const float nm = fmaxf(m, lv[k]);
-      const float sa_ = __builtin_amdgcn_exp2f((m - nm) * kLog2e);
-      const float sb = __builtin_amdgcn_exp2f((lv[k] - nm) * kLog2e);
-      ssum = ssum * sa_ + sb;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = acc[e] * sa_ + sb * ov[k][e];
-      m = nm;
-    }
-  }
-  for (int w = w0; w <= w1; w += BATCH) {
-    float lv[BATCH], ov[BATCH][EPL];
-#pragma unroll
-    for (int k = 0; k < BATCH; ++k) {
-      lv[k] = kNegInf;
-      if (w + k <= w1) {
-        const float* slot = sa.part + ((size_t)(w + k + tb) * a.Hq + u * kHPW + h) * (D + 1);
-        lv[k] = slot[D];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) ov[k][e] = slot[d0 + e];
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < BATCH; ++k) {
-      if (lv[k] == kNegInf) continue;   // absent or empty piece: its o is not read
-      const float nm = fmaxf(m, lv[k]);
-      const float sa_ = __builtin_amdgcn_exp2f((m - nm) * kLog2e);
-      const float sb = __builtin_amdgcn_exp2f((lv[k] - nm) * kLog2e);
-      ssum = ssum * sa_ + sb;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = acc[e] * sa_ + sb * ov[k][e];
-      m = nm;
-    }
-  }
-  const float inv = ssum != 0.f ? 1.f / ssum : 0.f;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) store_out<ET>(out + e, acc[e] * inv);
-  if (lse_out && (lane & 15) == 0) *lse_out = ssum != 0.f ? m + logf(ssum) : kNegInf;
+  const int w0 = plen ? pstart / per : 0, w1 = plen ? (pstart + plen - 1) / per : -1;
+  if (w0 == w1 && gch == 0) return;   // finished by one range
+  merge_pieces<ET, D, 8>(a, sa.part, tb, u, w0, w1, lane, sa.gp.part, gch);
 }
 
-// `join`: an event the merge must wait for (the group partials), or null.
+// Without groups only units cut by range boundaries need a merge, and each
+// boundary cuts at most one unit: the one containing the boundary's first
+// block.  Workgroup (r, j) merges that unit for head groups 4j .. 4j+3 when
+// the unit begins in range r - 1 (its first cut), one wave per head group.
+// Units with nothing visible were written by the plan.
+template <typename ET, int D>
+__global__ __launch_bounds__(256) void boundary_merge_kernel(StreamArgs sa) {
+  const DecodeArgs& a = sa.a;
+  const int lane = threadIdx.x & 63;
+  const int U = a.Hq / kHPW;
+  const int nj = (U + 3) / 4;
+  const int r = blockIdx.x / nj + 1;
+  const int u = (blockIdx.x % nj) * 4 + (threadIdx.x >> 6);
+  if (u >= U) return;
+  const int total = sa.hdr[0], per = sa.hdr[1];
+  const int F0 = r * per;
+  if (F0 >= total) return;
+  const int k = sa.first[r];
+  const int4 d = sa.udesc[k];
+  const int ustart = d.y, uend = sa.udesc[k + 1].y;
+  if (ustart >= F0 || ustart < F0 - per) return;   // not cut here, or cut first at an earlier boundary
+  merge_pieces<ET, D, 8>(a, sa.part, d.x, u, ustart / per, (uend - 1) / per, lane);
+}
+
 template <typename ET, int D, int GW>
-hipError_t launch_s(const StreamArgs& sa, hipStream_t stream, hipEvent_t join) {
+hipError_t launch_s(StreamArgs sa, hipStream_t stream) {
   constexpr int LOADS = SGeo<ET, D, GW>::LOADS;
 #ifdef PKV_STREAM_PD
   constexpr int PD = PKV_STREAM_PD;
@@ -687,35 +767,51 @@ hipError_t launch_s(const StreamArgs& sa, hipStream_t stream, hipEvent_t join) {
   const float sl2 = sa.a.scale * kLog2e;
   const int U = sa.a.Hq / kHPW;
   const int wpg = U < kMaxU ? U : kMaxU;
-  hipLaunchKernelGGL((stream_decode_kernel<ET, D, GW, PD>), dim3(sa.ranges * (U / wpg)), dim3(64 * wpg), 0, stream,
-                     sa, sa.udesc, sl2);
+  sa.stream_wgs = sa.ranges * (U / wpg);
+  int group_wgs = 0;
+  if (sa.groups) {
+    // persistent group workgroups, one per CU at most (they sit beside the decode ones)
+    const long long items = (long long)(sa.a.B / 2) * kGroupChunks * sa.a.Hkv;
+    group_wgs = (int)(items < device_cus() ? items : device_cus());
+  }
+  if (sa.groups)
+    hipLaunchKernelGGL((stream_decode_kernel<ET, D, GW, PD, true>), dim3(sa.stream_wgs + group_wgs), dim3(64 * wpg), 0,
+                       stream, sa, sa.udesc, sl2);
+  else
+    hipLaunchKernelGGL((stream_decode_kernel<ET, D, GW, PD, false>), dim3(sa.stream_wgs), dim3(64 * wpg), 0, stream, sa,
+                       sa.udesc, sl2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (join && (e = hipStreamWaitEvent(stream, join, 0)) != hipSuccess) return e;
-  const int G = (sa.a.Hq / kHPW) * sa.TB;
-  hipLaunchKernelGGL((stream_merge_kernel<ET, D>), dim3((G + 3) / 4), dim3(256), 0, stream, sa);
+  if (sa.groups) {
+    const int G = U * sa.TB;
+    hipLaunchKernelGGL((stream_merge_kernel<ET, D>), dim3((G + 3) / 4), dim3(256), 0, stream, sa);
+  } else if (sa.ranges > 1) {
+    hipLaunchKernelGGL((boundary_merge_kernel<ET, D>), dim3((sa.ranges - 1) * ((U + 3) / 4)), dim3(256), 0, stream, sa);
+  }
   return hipGetLastError();
 }
 
 template <typename ET, int D>
-hipError_t launch_sd(const StreamArgs& sa, hipStream_t stream, hipEvent_t join) {
+hipError_t launch_sd(const StreamArgs& sa, hipStream_t stream) {
   const int G = sa.a.Hq / sa.a.Hkv;
-  if (G >= 4) return launch_s<ET, D, 4>(sa, stream, join);
-  if (G == 2) return launch_s<ET, D, 2>(sa, stream, join);
-  return launch_s<ET, D, 1>(sa, stream, join);
+  if (G >= 4) return launch_s<ET, D, 4>(sa, stream);
+  if (G == 2) return launch_s<ET, D, 2>(sa, stream);
+  return launch_s<ET, D, 1>(sa, stream);
 }
 
-hipError_t launch_main(const StreamArgs& sa, hipStream_t stream, hipEvent_t join) {
-  if (sa.a.bf16) return sa.a.D == 64 ? launch_sd<Bf16, 64>(sa, stream, join) : launch_sd<Bf16, 128>(sa, stream, join);
-  return launch_sd<float, 64>(sa, stream, join);
+hipError_t launch_main(const StreamArgs& sa, hipStream_t stream) {
+  if (sa.a.bf16) return sa.a.D == 64 ? launch_sd<Bf16, 64>(sa, stream) : launch_sd<Bf16, 128>(sa, stream);
+  return launch_sd<float, 64>(sa, stream);
 }
 
 }  // namespace
 
 hipError_t launch_plan(const int32_t* lens, int B, int T, int ranges, int max_blocks, int* hdr, int* prefix, int* first,
-                       int4* udesc, hipStream_t stream, const int* sfx, const int* nch, const int* cnt, int* clist) {
+                       int4* udesc, hipStream_t stream, const GroupPlan* gp, const int32_t* tables, int G,
+                       const PlanFinish* fin) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, lens, B, T, ranges, max_blocks, B * T, hdr,
-                     prefix, first, udesc, sfx, nch, cnt, clist);
+                     prefix, first, udesc, gp ? *gp : GroupPlan{}, gp != nullptr, tables, group_members(G),
+                     fin ? *fin : PlanFinish{}, fin != nullptr);
   return hipGetLastError();
 }
 
@@ -729,7 +825,8 @@ size_t stream_workspace_bytes(int B, int T, int Hq, int D) {
   off += (R * 4 + 255) / 256 * 256;                       // first unit per range
   off += ((TB + 1) * 16 + 255) / 256 * 256;               // unit descriptors
   off += (R + TB) * Hq * (D + 1) * 4;                     // partial slots
-  if (T == 1) off += 256 + group_workspace_bytes(B, Hq, D);   // shared-prefix groups (256-aligned)
+  off = (off + 255) / 256 * 256;
+  if (T == 1) off += group_workspace_bytes(B, Hq, D);     // shared-prefix groups
   return off;
 }
 
@@ -756,32 +853,24 @@ hipError_t launch_decode_stream(const DecodeArgs& a, void* workspace, hipStream_
                                          ((size_t)(sa.TB + 1) * 16 + 255) / 256 * 256);
   sa.hdr = hdr; sa.prefix = prefix; sa.first = first; sa.udesc = udesc; sa.part = part;
   hipError_t e;
+  const int U = a.Hq / kHPW;
+  const int wpg = U < kMaxU ? U : kMaxU;
 #ifndef PKV_NO_GROUPS
-  if (groups_supported(a)) {
-    const size_t part_bytes = ((size_t)stream_ranges(a.Hq) + sa.TB) * a.Hq * (a.D + 1) * 4;
-    const GroupPlan gp = group_plan_layout(reinterpret_cast<unsigned char*>(part) + (part_bytes + 255) / 256 * 256,
-                                           a.B, a.Hq, a.D);
-    sa.gsfx = gp.sfx; sa.gnch = gp.nch; sa.gpart = gp.part;
-    if ((e = launch_group_detect(a, gp, stream)) != hipSuccess) return e;
-    e = launch_plan(a.context_lens, a.B, a.T, sa.ranges, a.max_blocks, hdr, prefix, first, udesc, stream, gp.sfx, gp.nch,
-                    gp.cnt, gp.clist);
-    if (e != hipSuccess) return e;
-    // The group kernel runs beside the decode kernel on the device's side
-    // stream (forked after the plan, joined before the merge); both fit on
-    // every CU at once, so the group work hides under the block stream.
-    GroupSide side;
-    if ((e = group_side(&side)) != hipSuccess) return e;
-    std::lock_guard<std::mutex> lock(group_side_mutex());
-    if ((e = hipEventRecord(side.fork, stream)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(side.stream, side.fork, 0)) != hipSuccess) return e;
-    if ((e = launch_group_prefix(a, gp, hdr, side.cus, side.stream)) != hipSuccess) return e;
-    if ((e = hipEventRecord(side.join, side.stream)) != hipSuccess) return e;
-    return launch_main(sa, stream, side.join);
-  }
+  sa.groups = groups_enabled() && groups_supported(a) && wpg == grp::kTiles;
 #endif
-  e = launch_plan(a.context_lens, a.B, a.T, sa.ranges, a.max_blocks, hdr, prefix, first, udesc, stream);
+  const size_t part_bytes = ((size_t)stream_ranges(a.Hq) + sa.TB) * a.Hq * (a.D + 1) * 4;
+  unsigned char* after_part = reinterpret_cast<unsigned char*>(part) + (part_bytes + 255) / 256 * 256;
+  if (sa.groups) {
+    sa.gp = group_plan_layout(after_part, a.B, a.Hq, a.D);
+    e = launch_plan(a.context_lens, a.B, a.T, sa.ranges, a.max_blocks, hdr, prefix, first, udesc, stream, &sa.gp,
+                    a.block_tables, a.Hq / a.Hkv);
+  } else {
+    const PlanFinish fin{a.out, a.lse_out, a.Hq, a.D, a.bf16};
+    e = launch_plan(a.context_lens, a.B, a.T, sa.ranges, a.max_blocks, hdr, prefix, first, udesc, stream, nullptr,
+                    nullptr, 1, &fin);
+  }
   if (e != hipSuccess) return e;
-  return launch_main(sa, stream, nullptr);
+  return launch_main(sa, stream);
 }
 
 }  // namespace pkv

@@ -19,6 +19,14 @@ pytestmark = pytest.mark.gpu
 BS = workload.BLOCK_SIZE
 
 
+@pytest.fixture(autouse=True, params=["groups", "plain"])
+def group_switch(request, monkeypatch):
+    """Every case runs with the shared-prefix group path switched on
+    (PKV_PREFIX_GROUPS=1, read by the library on each call) and off."""
+    monkeypatch.setenv("PKV_PREFIX_GROUPS", "1" if request.param == "groups" else "0")
+    return request.param
+
+
 def cdiv(a, b):
     return -(-a // b)
 
