@@ -37,9 +37,14 @@ constexpr int kBS = 16;
 constexpr int kHPW = 4;              // query heads per work unit
 constexpr int kWaves = kStreamWaves;   // about 8 waves per CU
 #ifndef PKV_STREAM_WPG
-#define PKV_STREAM_WPG 4
+#define PKV_STREAM_WPG 8
 #endif
-constexpr int kMaxU = PKV_STREAM_WPG;  // head groups (waves) per workgroup
+// Head groups (waves) per decode workgroup: one workgroup per range and CU
+// (a second workgroup on a CU measured about 8 % slower than the first).
+// The group-capable instantiation uses workgroups of grp::kTiles waves so
+// that a group workgroup fits beside two decode ones.
+constexpr int kMaxU = PKV_STREAM_WPG;
+template <bool GROUPS> constexpr int stream_wpg() { return GROUPS ? grp::kTiles : kMaxU; }
 constexpr int kMinBlocksPerRange = 16;
 constexpr float kSlack = 8.f;
 
@@ -400,9 +405,8 @@ constexpr int kStage = 8;   // units whose descriptors and queries are staged at
 template <typename ET, int D, int GW, bool GROUPS>
 struct StreamLds {
   static constexpr int QCH = SGeo<ET, D, GW>::NC * SGeo<ET, D, GW>::KW;   // distinct 16-byte query chunks per head
-  static constexpr int QBYTES = kMaxU * kStage * GW * QCH * 16;
-  static constexpr bool G_OK = GROUPS && std::is_same<ET, Bf16>::value && (D == 64 || D == 128) &&
-                               kMaxU == grp::kTiles;
+  static constexpr int QBYTES = stream_wpg<GROUPS>() * kStage * GW * QCH * 16;
+  static constexpr bool G_OK = GROUPS && std::is_same<ET, Bf16>::value && (D == 64 || D == 128);
   static constexpr int GBYTES = G_OK ? grp::Stage<D>::BYTES : 0;
   static constexpr int BYTES = QBYTES > GBYTES ? QBYTES : GBYTES;
 };
@@ -414,7 +418,8 @@ template <typename ET, int D, int GW, bool GROUPS>
 constexpr int stream_waves_per_eu() { return GROUPS && SGeo<ET, D, GW>::LOADS < 16 ? 3 : 2; }
 
 template <typename ET, int D, int GW, int PD, bool GROUPS>
-__global__ __launch_bounds__(64 * kMaxU) __attribute__((amdgpu_waves_per_eu(stream_waves_per_eu<ET, D, GW, GROUPS>())))
+__global__ __launch_bounds__(64 * stream_wpg<GROUPS>())
+__attribute__((amdgpu_waves_per_eu(stream_waves_per_eu<ET, D, GW, GROUPS>())))
 void stream_decode_kernel(StreamArgs sa, const int4* __restrict__ udesc, float scale_log2e) {
   using G = SGeo<ET, D, GW>;
   using ST = typename Storage<ET>::T;
@@ -766,7 +771,8 @@ hipError_t launch_s(StreamArgs sa, hipStream_t stream) {
 #endif
   const float sl2 = sa.a.scale * kLog2e;
   const int U = sa.a.Hq / kHPW;
-  const int wpg = U < kMaxU ? U : kMaxU;
+  const int wmax = sa.groups ? stream_wpg<true>() : stream_wpg<false>();
+  const int wpg = U < wmax ? U : wmax;
   sa.stream_wgs = sa.ranges * (U / wpg);
   int group_wgs = 0;
   if (sa.groups) {
@@ -854,9 +860,8 @@ hipError_t launch_decode_stream(const DecodeArgs& a, void* workspace, hipStream_
   sa.hdr = hdr; sa.prefix = prefix; sa.first = first; sa.udesc = udesc; sa.part = part;
   hipError_t e;
   const int U = a.Hq / kHPW;
-  const int wpg = U < kMaxU ? U : kMaxU;
 #ifndef PKV_NO_GROUPS
-  sa.groups = groups_enabled() && groups_supported(a) && wpg == grp::kTiles;
+  sa.groups = groups_enabled() && groups_supported(a) && U % grp::kTiles == 0;
 #endif
   const size_t part_bytes = ((size_t)stream_ranges(a.Hq) + sa.TB) * a.Hq * (a.D + 1) * 4;
   unsigned char* after_part = reinterpret_cast<unsigned char*>(part) + (part_bytes + 255) / 256 * 256;
