@@ -204,7 +204,8 @@ def main():
                    "append": has_append},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "paged_attention_decode call (partition kernel + lse merge)",
+                     "kernel": ("paged_attention_decode call (plan + balanced decode + boundary merge)" if part == 0
+                                else "paged_attention_decode call (partition kernel + lse merge)"),
                      "bytes_per_launch": nb["decode"], "launch_ms": round(decode_ms, 5),
                      "logical_GBps": round(nb["logical"] / (decode_ms * 1e-3) / 1e9, 1)},
     }

@@ -105,10 +105,14 @@ pkv_status paged_kv_gather(const void* k_pool, const void* v_pool, const int32_t
 
 /*
  * pkv_decode_workspace_bytes -- bytes of device workspace paged_attention_decode
- * needs for these sizes and this partition size (0 when partition_size == 0).
- * The split-KV partials use B*T*Hq*P_max*(D+1) float32 values, where
- * P_max = ceil(max_blocks * block_size / partition_size).  Returns 0 for
- * invalid sizes.
+ * needs for these sizes and this partition size.  With partition_size > 0 the
+ * split-KV partials use B*T*Hq*P_max*(D+1) float32 values, where
+ * P_max = ceil(max_blocks * block_size / partition_size).  With
+ * partition_size = 0 the workspace holds the plan of the balanced split
+ * (a header, per-unit prefix sums and descriptors) and one normalised partial
+ * per (range, unit) piece: (ranges + B*T) * Hq * (D+1) float32 values, where
+ * ranges = 2048 / (Hq/4) (256 at Hq = 32), plus the shared-prefix group area
+ * when T = 1.  Returns 0 for invalid sizes.
  */
 size_t pkv_decode_workspace_bytes(int B, int T, int Hq, int D, int max_blocks, int block_size,
                                   int partition_size);
@@ -123,7 +127,22 @@ size_t pkv_decode_workspace_bytes(int B, int T, int Hq, int D, int max_blocks, i
  * scale is normally 1/sqrt(D).  lse_out, when not NULL, receives the natural
  * log of the softmax denominator, log sum_j exp(scale * q.k_j).
  *
- * partition_size = 0 evaluates each (sequence, head group) in one pass.
+ * partition_size = 0 (the fast path) splits the whole batch evenly: the 16-token
+ * blocks of all (sequence, query token) units are laid end to end and cut into
+ * equal ranges, one per persistent workgroup, whatever the length mix.  A unit
+ * inside one range is written straight to `out`; a unit cut by range
+ * boundaries leaves one normalised partial per piece and a merge kernel
+ * combines them by log-sum-exp weights.  Shapes: bf16 with D in {64, 128} or
+ * fp32 with D = 64, Hq a multiple of 4 with Hq/4 <= 8 or a multiple of 8,
+ * Hq/Hkv in {1, 2, 4, 8}, B*T <= 8192.  bf16 with 2 <= T and T*Hq/Hkv <= 16
+ * (multi-query verify) runs 16-row MFMA tiles instead, split the same way.
+ * Other shapes run the partitioned kernel below with one partition.
+ * With T = 1, bf16 and the environment variable PKV_PREFIX_GROUPS=1, adjacent
+ * sequences whose tables start with the same physical block are grouped and
+ * their common blocks are attended once per group on MFMA (off by default:
+ * on MI355X the last-level cache already serves most shared-prefix re-reads).
+ * The partitioned path and the balanced path give results that agree within
+ * rounding; each is deterministic: equal inputs give equal bits.
  * partition_size > 0 (a multiple of block_size) splits every sequence into
  * partitions of that many tokens starting at position 0; each partition
  * emits a normalised partial output and its log-sum-exp into `workspace`,
@@ -135,7 +154,10 @@ size_t pkv_decode_workspace_bytes(int B, int T, int Hq, int D, int max_blocks, i
  * for p < P_b; everything else in it is unspecified.  A partition with no
  * visible token for a query row has part_lse = -inf and part_out = 0.
  *
- * out must not alias any input.  workspace is ignored when partition_size is 0.
+ * out must not alias any input.  The workspace must be at least
+ * pkv_decode_workspace_bytes(...) bytes of device memory (else PKV_EWORKSPACE);
+ * it is overwritten by every call and two calls in flight at once need two
+ * workspaces.
  */
 pkv_status paged_attention_decode(const void* q, const void* k_pool, const void* v_pool,
                                   const int32_t* block_tables, const int32_t* context_lens,
