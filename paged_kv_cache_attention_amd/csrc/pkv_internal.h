@@ -66,6 +66,10 @@ struct GroupPlan {
 // detection and the group workgroups cost more than they save on the
 // prefix-sharing 8B-shaped batch (measured 243 us with groups, 238 us without).
 bool groups_enabled();
+// Plan inside the decode kernel when the unit list fits in LDS (default;
+// PKV_INLINE_PLAN=0 launches the planning kernel instead).
+bool inline_plan_enabled();
+int device_lds_per_block();
 bool groups_supported(const DecodeArgs& a);
 size_t group_workspace_bytes(int B, int Hq, int D);
 GroupPlan group_plan_layout(void* base, int B, int Hq, int D);

@@ -1,7 +1,7 @@
 // Shared-prefix groups for single-token decode: host side (sizes, layout,
 // applicability).  The device code is in pkv_group.h; detection runs in the
 // planning kernel and the group items run on extra workgroups of the decode
-// launch.
+// launch.  Also the cached device attributes and switches the launchers use.
 #include <cstdlib>
 #include <mutex>
 
@@ -46,18 +46,31 @@ GroupPlan group_plan_layout(void* base, int B, int Hq, int D) {
   return gp;
 }
 
-int device_cus() {
+namespace {
+// A device attribute of the current device, cached per device; `fallback`
+// when it cannot be read.
+int cached_attribute(hipDeviceAttribute_t attr, int slot, int fallback) {
   constexpr int kMaxDevices = 64;
-  static int cus[kMaxDevices];
+  static int vals[2][kMaxDevices];
   static std::mutex mu;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return fallback;
   std::lock_guard<std::mutex> lock(mu);
-  if (cus[dev] == 0) {
+  if (vals[slot][dev] == 0) {
     int n = 0;
-    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+    vals[slot][dev] = hipDeviceGetAttribute(&n, attr, dev) == hipSuccess && n > 0 ? n : fallback;
   }
-  return cus[dev];
+  return vals[slot][dev];
+}
+}  // namespace
+
+int device_cus() { return cached_attribute(hipDeviceAttributeMultiprocessorCount, 0, 256); }
+
+int device_lds_per_block() { return cached_attribute(hipDeviceAttributeMaxSharedMemoryPerBlock, 1, 65536); }
+
+bool inline_plan_enabled() {
+  const char* v = std::getenv("PKV_INLINE_PLAN");
+  return !(v && v[0] == '0');
 }
 
 }  // namespace pkv

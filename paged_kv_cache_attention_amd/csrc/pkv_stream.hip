@@ -50,16 +50,17 @@ constexpr float kSlack = 8.f;
 
 struct StreamArgs {
   DecodeArgs a;
-  const int* hdr;      // [total, per, tbtot]
-  const int* prefix;   // [TB + 1]
-  const int* first;    // [ranges] first non-empty unit (compact index) of each range, -1 if idle
-  const int4* udesc;   // [nu + 1] non-empty units: {tb, flat start, table offset, visible tokens}
+  int* hdr;            // [total, per, total, group chunks, nu]
+  int* prefix;         // [TB + 1] (written by the planning kernel only)
+  int* first;          // [ranges] first non-empty unit (compact index) of each range, -1 if idle
+  int4* udesc;         // [nu + 1] non-empty units: {tb, flat start, table offset, visible tokens}
   float* part;         // partial slots [(ranges + TB)][Hq][D + 1]
   GroupPlan gp;        // shared-prefix groups (when `groups`)
   bool groups;
   int stream_wgs;      // decode workgroups; any further workgroups run group items
   int TB;
   int ranges;          // workgroups splitting the block list
+  bool inl;            // plan computed inside the decode kernel (no planning kernel)
 };
 
 template <typename ET, int D, int GW>
@@ -314,6 +315,103 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 }
 
 // ---------------------------------------------------------------------------
+// The same plan computed inside the decode kernel, when the unit list fits in
+// LDS (B*T + 1 <= kInlineUnitsPerWave entries per wave of the workgroup):
+// every workgroup derives it from the lengths, so no planning launch precedes
+// the decode launch.  Thread i counts the blocks of units 4i .. 4i+3; a wave
+// scan plus a pass over the waves' totals gives their flat starts; the
+// compact descriptors go to LDS.  The merge kernel reads the header, the
+// descriptors and each range's first unit from the workspace: workgroup g
+// publishes descriptors g*threads + tid (+ multiples of all threads), every
+// range its own first unit and workgroup 0 the header.
+// ---------------------------------------------------------------------------
+constexpr int kInlineUnitsPerWave = 256;
+constexpr int kInlinePT = kInlineUnitsPerWave / 64;   // units per thread
+
+struct InlinePlan {
+  int total, per, nu;
+};
+
+__device__ __forceinline__ InlinePlan inline_plan(const StreamArgs& sa, int4* lud, int* wsc) {
+  const DecodeArgs& a = sa.a;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), nw = blockDim.x >> 6;
+  const int max_tokens = a.max_blocks * kBS;
+  int vis[kInlinePT];
+  int sum = 0, ne = 0;
+#pragma unroll
+  for (int j = 0; j < kInlinePT; ++j) {
+    const int i = tid * kInlinePT + j;
+    vis[j] = i < sa.TB ? unit_visible(a.context_lens, i, a.B, a.T, max_tokens) : 0;
+    const int nb = (vis[j] + kBS - 1) / kBS;
+    sum += nb;
+    ne += nb > 0;
+  }
+  int is = sum, in = ne;   // inclusive scans over the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int ys = __shfl_up(is, off), yn = __shfl_up(in, off);
+    if (lane >= off) {
+      is += ys;
+      in += yn;
+    }
+  }
+  if (lane == 63) {
+    wsc[wave] = is;
+    wsc[16 + wave] = in;
+  }
+  __syncthreads();
+  int run = is - sum, krun = in - ne, total = 0, nu = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int vs = wsc[w], vn = wsc[16 + w];
+    if (w < wave) {
+      run += vs;
+      krun += vn;
+    }
+    total += vs;
+    nu += vn;
+  }
+#pragma unroll
+  for (int j = 0; j < kInlinePT; ++j) {
+    const int i = tid * kInlinePT + j;
+    const int nb = (vis[j] + kBS - 1) / kBS;
+    if (nb > 0) lud[krun++] = make_int4(i, run, (i % a.B) * a.max_blocks, vis[j]);
+    run += nb;
+  }
+  if (tid == 0) lud[nu] = make_int4(0, total, 0, 0);   // sentinel
+  __syncthreads();
+  const int per = max(kMinBlocksPerRange, (total + sa.ranges - 1) / sa.ranges);
+  if (sa.ranges > 1) {   // for the merge kernel
+    for (int k = blockIdx.x * blockDim.x + tid; k <= nu; k += gridDim.x * blockDim.x) sa.udesc[k] = lud[k];
+    if (blockIdx.x == 0 && tid == 0) {
+      sa.hdr[0] = total;
+      sa.hdr[1] = per;
+      sa.hdr[2] = total;
+      sa.hdr[3] = 0;
+      sa.hdr[4] = nu;
+    }
+  }
+  return InlinePlan{total, per, nu};
+}
+
+// Largest k < nu with lud[k].y <= F, by one wave (unit starts strictly
+// increase and lud[0].y = 0 <= F): 64-way splits of the candidate interval.
+__device__ __forceinline__ int find_unit(const int4* lud, int nu, int F) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, hi = nu;   // the answer lies in [lo, hi); lud[lo].y <= F
+  while (hi - lo > 64) {
+    const int step = (hi - lo + 63) / 64;
+    const int k = lo + lane * step;
+    const unsigned long long m = __builtin_amdgcn_ballot_w64(k < hi && lud[min(k, hi - 1)].y <= F);
+    lo += (63 - __builtin_clzll(m)) * step;
+    hi = min(hi, lo + step);
+  }
+  const int k = lo + lane;
+  const unsigned long long m = __builtin_amdgcn_ballot_w64(k < hi && lud[min(k, hi - 1)].y <= F);
+  return lo + 63 - __builtin_clzll(m);
+}
+
+// ---------------------------------------------------------------------------
 // The persistent decode kernel.
 //
 // A wave walks the flat blocks [F0, F1) of its range as one continuous
@@ -405,7 +503,8 @@ constexpr int kStage = 8;   // units whose descriptors and queries are staged at
 template <typename ET, int D, int GW, bool GROUPS>
 struct StreamLds {
   static constexpr int QCH = SGeo<ET, D, GW>::NC * SGeo<ET, D, GW>::KW;   // distinct 16-byte query chunks per head
-  static constexpr int QBYTES = stream_wpg<GROUPS>() * kStage * GW * QCH * 16;
+  static constexpr int QWAVE = kStage * GW * QCH * 16;                   // staged query bytes per wave
+  static constexpr int QBYTES = stream_wpg<GROUPS>() * QWAVE;
   static constexpr bool G_OK = GROUPS && std::is_same<ET, Bf16>::value && (D == 64 || D == 128);
   static constexpr int GBYTES = G_OK ? grp::Stage<D>::BYTES : 0;
   static constexpr int BYTES = QBYTES > GBYTES ? QBYTES : GBYTES;
@@ -417,15 +516,23 @@ struct StreamLds {
 template <typename ET, int D, int GW, bool GROUPS>
 constexpr int stream_waves_per_eu() { return GROUPS && SGeo<ET, D, GW>::LOADS < 16 ? 3 : 2; }
 
-template <typename ET, int D, int GW, int PD, bool GROUPS>
+// INL: the plan is computed by the kernel itself (inline_plan) and the unit
+// descriptors are read from LDS; otherwise the planning kernel wrote them to
+// the workspace.  LDS: staged queries (QWAVE bytes per wave), then, with INL,
+// the unit descriptors; dynamic, sized by the launch.  The group-capable
+// instantiation uses a static buffer shared with the group stage.
+template <typename ET, int D, int GW, int PD, bool GROUPS, bool INL>
 __global__ __launch_bounds__(64 * stream_wpg<GROUPS>())
 __attribute__((amdgpu_waves_per_eu(stream_waves_per_eu<ET, D, GW, GROUPS>())))
 void stream_decode_kernel(StreamArgs sa, const int4* __restrict__ udesc, float scale_log2e) {
+  static_assert(!(GROUPS && INL), "groups need the planning kernel");
   using G = SGeo<ET, D, GW>;
   using ST = typename Storage<ET>::T;
   using LD = StreamLds<ET, D, GW, GROUPS>;
   // one LDS buffer: staged queries on decode workgroups, staged K/V on group ones
-  __shared__ __attribute__((aligned(16))) unsigned char lds[LD::BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char slds[GROUPS ? LD::BYTES : 16];
+  extern __shared__ __attribute__((aligned(16))) unsigned char dlds[];
+  unsigned char* lds = GROUPS ? slds : dlds;
   if constexpr (LD::G_OK) {
     if ((int)blockIdx.x >= sa.stream_wgs) {
       grp::group_items<D>(sa.a, sa.gp, sa.hdr[3] * sa.a.Hkv, blockIdx.x - sa.stream_wgs, gridDim.x - sa.stream_wgs, lds,
@@ -439,9 +546,42 @@ void stream_decode_kernel(StreamArgs sa, const int4* __restrict__ udesc, float s
   const int wpg = blockDim.x >> 6;                      // waves per workgroup
   const int rng = blockIdx.x / (U / wpg);               // block range of this workgroup
   const int u = (blockIdx.x % (U / wpg)) * wpg + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int total = sa.hdr[0], per = sa.hdr[1], nu = sa.hdr[4];
+  int4* lud = reinterpret_cast<int4*>(lds + wpg * LD::QWAVE);   // INL: unit descriptors
+  __shared__ int wsc[32];
+  int total, per, nu;
+  if constexpr (INL) {
+    const InlinePlan ip = inline_plan(sa, lud, wsc);
+    total = __builtin_amdgcn_readfirstlane(ip.total);
+    per = __builtin_amdgcn_readfirstlane(ip.per);
+    nu = __builtin_amdgcn_readfirstlane(ip.nu);
+  } else {
+    total = sa.hdr[0];
+    per = sa.hdr[1];
+    nu = sa.hdr[4];
+  }
+  // INL: units with nothing visible get out = 0 and lse = -inf, spread over
+  // all waves of the grid (the planning kernel does this otherwise)
+  auto finish_empty = [&]() {
+    if constexpr (INL) {
+      using OT = typename Storage<ET>::T;
+      const int lane_ = threadIdx.x & 63;
+      const int gw = blockIdx.x * wpg + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), nwt = gridDim.x * wpg;
+      for (int i = gw; i < sa.TB; i += nwt) {
+        if (unit_visible(a.context_lens, i, a.B, a.T, a.max_blocks * kBS) > 0) continue;
+        const int t = i / a.B, b = i - t * a.B;
+        const size_t row = ((size_t)b * a.T + t) * a.Hq;
+        OT* o = static_cast<OT*>(a.out) + row * D;
+        for (int e = lane_; e < a.Hq * D; e += 64) store_out<ET>(o + e, 0.f);
+        if (a.lse_out)
+          for (int h = lane_; h < a.Hq; h += 64) a.lse_out[row + h] = kNegInf;
+      }
+    }
+  };
   const int F0 = rng * per;
-  if (F0 >= total) return;
+  if (F0 >= total) {
+    finish_empty();
+    return;
+  }
   const int F1 = min(total, F0 + per);
 
   const int c = lane % G::NC;
@@ -461,9 +601,13 @@ void stream_decode_kernel(StreamArgs sa, const int4* __restrict__ udesc, float s
   const unsigned char* vpool = static_cast<const unsigned char*>(a.v_pool) + lane_off;
 
   // ---- chunk resolution ----
+  auto desc = [&](int k) -> int4 {
+    if constexpr (INL) return lud[k];
+    else return udesc[k];
+  };
   auto window = [&](int kc, int4& w, int& ue) {
-    w = udesc[min(kc + lane, nu)];
-    ue = udesc[min(kc + lane + 1, nu)].y;
+    w = desc(min(kc + lane, nu));
+    ue = desc(min(kc + lane + 1, nu)).y;
   };
   // Resolves flat blocks Fc + lane against the window of units starting at
   // wbase; returns the first unit of the following chunk.
@@ -482,7 +626,13 @@ void stream_decode_kernel(StreamArgs sa, const int4* __restrict__ udesc, float s
   };
 
   int Fc = F0;
-  const int kfirst = sa.first[rng];
+  int kfirst;
+  if constexpr (INL) {
+    kfirst = __builtin_amdgcn_readfirstlane(find_unit(lud, nu, F0));
+    if (sa.ranges > 1 && threadIdx.x == 0 && blockIdx.x % (U / wpg) == 0) sa.first[rng] = kfirst;
+  } else {
+    kfirst = sa.first[rng];
+  }
   int4 wv; int wue;
   int cphys, cflags, nphys = 0, nflags = 0;
   window(kfirst, wv, wue);
@@ -508,8 +658,8 @@ void stream_decode_kernel(StreamArgs sa, const int4* __restrict__ udesc, float s
   int se = 0;       // lane s: flat start of unit kbase + s + 1 (its end)
   auto stage = [&](int kb) {
     kbase = kb;
-    sd = udesc[min(kb + lane, nu)];
-    se = udesc[min(kb + lane + 1, nu)].y;
+    sd = desc(min(kb + lane, nu));
+    se = desc(min(kb + lane + 1, nu)).y;
     u32x4_t tmp[kStage];
 #pragma unroll
     for (int s = 0; s < kStage; ++s) {
@@ -699,6 +849,7 @@ void stream_decode_kernel(StreamArgs sa, const int4* __restrict__ udesc, float s
       break;
     }
   }
+  finish_empty();
 }
 
 // ---------------------------------------------------------------------------
@@ -780,12 +931,17 @@ hipError_t launch_s(StreamArgs sa, hipStream_t stream) {
     const long long items = (long long)(sa.a.B / 2) * kGroupChunks * sa.a.Hkv;
     group_wgs = (int)(items < device_cus() ? items : device_cus());
   }
+  using LD = StreamLds<ET, D, GW, false>;
+  const size_t qbytes = (size_t)wpg * LD::QWAVE;
   if (sa.groups)
-    hipLaunchKernelGGL((stream_decode_kernel<ET, D, GW, PD, true>), dim3(sa.stream_wgs + group_wgs), dim3(64 * wpg), 0,
-                       stream, sa, sa.udesc, sl2);
+    hipLaunchKernelGGL((stream_decode_kernel<ET, D, GW, PD, true, false>), dim3(sa.stream_wgs + group_wgs),
+                       dim3(64 * wpg), 0, stream, sa, sa.udesc, sl2);
+  else if (sa.inl)
+    hipLaunchKernelGGL((stream_decode_kernel<ET, D, GW, PD, false, true>), dim3(sa.stream_wgs), dim3(64 * wpg),
+                       qbytes + (size_t)kInlineUnitsPerWave * wpg * sizeof(int4), stream, sa, sa.udesc, sl2);
   else
-    hipLaunchKernelGGL((stream_decode_kernel<ET, D, GW, PD, false>), dim3(sa.stream_wgs), dim3(64 * wpg), 0, stream, sa,
-                       sa.udesc, sl2);
+    hipLaunchKernelGGL((stream_decode_kernel<ET, D, GW, PD, false, false>), dim3(sa.stream_wgs), dim3(64 * wpg), qbytes,
+                       stream, sa, sa.udesc, sl2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (sa.groups) {
@@ -819,6 +975,15 @@ hipError_t launch_plan(const int32_t* lens, int B, int T, int ranges, int max_bl
                      prefix, first, udesc, gp ? *gp : GroupPlan{}, gp != nullptr, tables, group_members(G),
                      fin ? *fin : PlanFinish{}, fin != nullptr);
   return hipGetLastError();
+}
+
+// LDS of the inline-plan decode launch: staged queries plus the unit list.
+static size_t inline_lds_bytes(const DecodeArgs& a, int wpg) {
+  const int G = a.Hq / a.Hkv;
+  const int GW = G >= 4 ? 4 : (G == 2 ? 2 : 1);
+  const int EB = a.bf16 ? 2 : 4;
+  const int NC = a.D * EB / 16, KW = kHPW / GW;
+  return (size_t)wpg * kStage * GW * NC * KW * 16 + (size_t)kInlineUnitsPerWave * wpg * sizeof(int4) + 256;
 }
 
 int stream_ranges(int Hq) { return kWaves / (Hq >= kHPW ? Hq / kHPW : 1); }
@@ -870,9 +1035,13 @@ hipError_t launch_decode_stream(const DecodeArgs& a, void* workspace, hipStream_
     e = launch_plan(a.context_lens, a.B, a.T, sa.ranges, a.max_blocks, hdr, prefix, first, udesc, stream, &sa.gp,
                     a.block_tables, a.Hq / a.Hkv);
   } else {
+    const int wpg = U < kMaxU ? U : kMaxU;
+    sa.inl = inline_plan_enabled() && sa.TB + 1 <= kInlineUnitsPerWave * wpg &&
+             inline_lds_bytes(a, wpg) <= (size_t)device_lds_per_block();
     const PlanFinish fin{a.out, a.lse_out, a.Hq, a.D, a.bf16};
-    e = launch_plan(a.context_lens, a.B, a.T, sa.ranges, a.max_blocks, hdr, prefix, first, udesc, stream, nullptr,
-                    nullptr, 1, &fin);
+    e = sa.inl ? hipSuccess
+               : launch_plan(a.context_lens, a.B, a.T, sa.ranges, a.max_blocks, hdr, prefix, first, udesc, stream,
+                             nullptr, nullptr, 1, &fin);
   }
   if (e != hipSuccess) return e;
   return launch_main(sa, stream);
