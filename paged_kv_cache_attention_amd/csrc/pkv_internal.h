@@ -97,7 +97,8 @@ struct PlanFinish {
 };
 hipError_t launch_plan(const int32_t* lens, int B, int T, int ranges, int max_blocks, int* hdr, int* prefix, int* first,
                        int4* udesc, hipStream_t stream, const GroupPlan* gp = nullptr,
-                       const int32_t* tables = nullptr, int G = 1, const PlanFinish* fin = nullptr);
+                       const int32_t* tables = nullptr, int G = 1, const PlanFinish* fin = nullptr,
+                       int4* mdesc = nullptr);
 
 // MFMA verify tile for bf16 with 2 <= T and T * (Hq/Hkv) <= 16 query rows per
 // KV head; balanced like the VALU path, with its own workspace layout.

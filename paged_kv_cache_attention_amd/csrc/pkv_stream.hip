@@ -53,6 +53,7 @@ struct StreamArgs {
   int* hdr;            // [total, per, total, group chunks, nu]
   int* prefix;         // [TB + 1] (written by the planning kernel only)
   int* first;          // [ranges] first non-empty unit (compact index) of each range, -1 if idle
+  int4* mdesc;         // [ranges] merge at boundary r: {unit, first range, last range} or x = -1
   int4* udesc;         // [nu + 1] non-empty units: {tb, flat start, table offset, visible tokens}
   float* part;         // partial slots [(ranges + TB)][Hq][D + 1]
   GroupPlan gp;        // shared-prefix groups (when `groups`)
@@ -202,13 +203,15 @@ __device__ __forceinline__ int unit_visible(const int32_t* lens, int tb, int B, 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ lens, int B, int T,
                                                             int ranges, int max_blocks, int TB, int* __restrict__ hdr,
                                                             int* __restrict__ prefix, int* __restrict__ first,
-                                                            int4* __restrict__ udesc, GroupPlan gp, bool groups,
+                                                            int4* __restrict__ udesc, int4* __restrict__ mdesc,
+                                                            GroupPlan gp, bool groups,
                                                             const int32_t* __restrict__ tables, int GM,
                                                             PlanFinish fin, bool finish) {
   __shared__ int part[kPlanThreads];
   __shared__ int npart[kPlanThreads];
   __shared__ int cpart[kPlanThreads];
   __shared__ int spref[kStreamMaxTB + 1];   // flat start of each non-empty unit
+  __shared__ int sid[kStreamMaxTB];         // its unit index
   __shared__ int ssfx[kGroupMaxB], snch[kGroupMaxB], scnt[kGroupMaxB];
   const int tid = threadIdx.x;
   const int max_tokens = max_blocks * kBS;
@@ -258,6 +261,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
       // {unit, flat start, table offset of its first block, visible tokens (negative: merged with a group)}
       udesc[krun] = make_int4(i, run, b * max_blocks + sb, grouped ? -vis : vis);
       spref[krun] = run;
+      sid[krun] = i;
       ++krun;
     }
     run += nb;
@@ -302,6 +306,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     const long long F0 = (long long)w * per;
     if (F0 >= tbtot) {
       first[w] = -1;
+      if (mdesc) mdesc[w] = make_int4(-1, 0, 0, 0);
       continue;
     }
     const int r = (int)F0;
@@ -311,6 +316,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
       if (spref[mid] <= r) lo = mid; else hi = mid;
     }
     first[w] = lo;
+    // the unit cut by boundary w is merged there if boundary w cuts it first
+    if (mdesc) {
+      const int us = spref[lo], ue = spref[lo + 1];
+      mdesc[w] = w > 0 && us < r && us >= r - per ? make_int4(sid[lo], w - 1, (ue - 1) / per, 0) : make_int4(-1, 0, 0, 0);
+    }
   }
 }
 
@@ -320,10 +330,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 // every workgroup derives it from the lengths, so no planning launch precedes
 // the decode launch.  Thread i counts the blocks of units 4i .. 4i+3; a wave
 // scan plus a pass over the waves' totals gives their flat starts; the
-// compact descriptors go to LDS.  The merge kernel reads the header, the
-// descriptors and each range's first unit from the workspace: workgroup g
-// publishes descriptors g*threads + tid (+ multiples of all threads), every
-// range its own first unit and workgroup 0 the header.
+// compact descriptors go to LDS.  Each range publishes the merge descriptor
+// of its boundary to the workspace for the merge kernel.
 // ---------------------------------------------------------------------------
 constexpr int kInlineUnitsPerWave = 256;
 constexpr int kInlinePT = kInlineUnitsPerWave / 64;   // units per thread
@@ -381,16 +389,6 @@ __device__ __forceinline__ InlinePlan inline_plan(const StreamArgs& sa, int4* lu
   if (tid == 0) lud[nu] = make_int4(0, total, 0, 0);   // sentinel
   __syncthreads();
   const int per = max(kMinBlocksPerRange, (total + sa.ranges - 1) / sa.ranges);
-  if (sa.ranges > 1) {   // for the merge kernel
-    for (int k = blockIdx.x * blockDim.x + tid; k <= nu; k += gridDim.x * blockDim.x) sa.udesc[k] = lud[k];
-    if (blockIdx.x == 0 && tid == 0) {
-      sa.hdr[0] = total;
-      sa.hdr[1] = per;
-      sa.hdr[2] = total;
-      sa.hdr[3] = 0;
-      sa.hdr[4] = nu;
-    }
-  }
   return InlinePlan{total, per, nu};
 }
 
@@ -578,7 +576,9 @@ void stream_decode_kernel(StreamArgs sa, const int4* __restrict__ udesc, float s
     }
   };
   const int F0 = rng * per;
+  const bool mwriter = INL && rng > 0 && threadIdx.x == 0 && blockIdx.x % (U / wpg) == 0;
   if (F0 >= total) {
+    if (mwriter) sa.mdesc[rng] = make_int4(-1, 0, 0, 0);
     finish_empty();
     return;
   }
@@ -629,7 +629,11 @@ void stream_decode_kernel(StreamArgs sa, const int4* __restrict__ udesc, float s
   int kfirst;
   if constexpr (INL) {
     kfirst = __builtin_amdgcn_readfirstlane(find_unit(lud, nu, F0));
-    if (sa.ranges > 1 && threadIdx.x == 0 && blockIdx.x % (U / wpg) == 0) sa.first[rng] = kfirst;
+    if (mwriter) {   // the unit cut by this range's start is merged here if this is its first cut
+      const int4 d = lud[kfirst];
+      const int ue = lud[kfirst + 1].y;
+      sa.mdesc[rng] = d.y < F0 && d.y >= F0 - per ? make_int4(d.x, rng - 1, (ue - 1) / per, 0) : make_int4(-1, 0, 0, 0);
+    }
   } else {
     kfirst = sa.first[rng];
   }
@@ -887,7 +891,8 @@ __global__ __launch_bounds__(256) void stream_merge_kernel(StreamArgs sa) {
 // Without groups only units cut by range boundaries need a merge, and each
 // boundary cuts at most one unit: the one containing the boundary's first
 // block.  Workgroup (r, j) merges that unit for head groups 4j .. 4j+3 when
-// the unit begins in range r - 1 (its first cut), one wave per head group.
+// the unit begins in range r - 1 (its first cut), one wave per head group;
+// the plan left that decision and the unit's ranges in mdesc[r].
 // Units with nothing visible were written by the plan.
 template <typename ET, int D>
 __global__ __launch_bounds__(256) void boundary_merge_kernel(StreamArgs sa) {
@@ -898,14 +903,9 @@ __global__ __launch_bounds__(256) void boundary_merge_kernel(StreamArgs sa) {
   const int r = blockIdx.x / nj + 1;
   const int u = (blockIdx.x % nj) * 4 + (threadIdx.x >> 6);
   if (u >= U) return;
-  const int total = sa.hdr[0], per = sa.hdr[1];
-  const int F0 = r * per;
-  if (F0 >= total) return;
-  const int k = sa.first[r];
-  const int4 d = sa.udesc[k];
-  const int ustart = d.y, uend = sa.udesc[k + 1].y;
-  if (ustart >= F0 || ustart < F0 - per) return;   // not cut here, or cut first at an earlier boundary
-  merge_pieces<ET, D, 8>(a, sa.part, d.x, u, ustart / per, (uend - 1) / per, lane);
+  const int4 md = sa.mdesc[r];   // {unit, first range, last range}; x < 0: nothing to merge here
+  if (md.x < 0) return;
+  merge_pieces<ET, D, 8>(a, sa.part, md.x, u, md.y, md.z, lane);
 }
 
 template <typename ET, int D, int GW>
@@ -970,9 +970,9 @@ hipError_t launch_main(const StreamArgs& sa, hipStream_t stream) {
 
 hipError_t launch_plan(const int32_t* lens, int B, int T, int ranges, int max_blocks, int* hdr, int* prefix, int* first,
                        int4* udesc, hipStream_t stream, const GroupPlan* gp, const int32_t* tables, int G,
-                       const PlanFinish* fin) {
+                       const PlanFinish* fin, int4* mdesc) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, lens, B, T, ranges, max_blocks, B * T, hdr,
-                     prefix, first, udesc, gp ? *gp : GroupPlan{}, gp != nullptr, tables, group_members(G),
+                     prefix, first, udesc, mdesc, gp ? *gp : GroupPlan{}, gp != nullptr, tables, group_members(G),
                      fin ? *fin : PlanFinish{}, fin != nullptr);
   return hipGetLastError();
 }
@@ -994,6 +994,7 @@ size_t stream_workspace_bytes(int B, int T, int Hq, int D) {
   size_t off = 256;                                       // header
   off += ((TB + 1) * 4 + 255) / 256 * 256;                // prefix
   off += (R * 4 + 255) / 256 * 256;                       // first unit per range
+  off += R * 16;                                          // merge descriptor per boundary
   off += ((TB + 1) * 16 + 255) / 256 * 256;               // unit descriptors
   off += (R + TB) * Hq * (D + 1) * 4;                     // partial slots
   off = (off + 255) / 256 * 256;
@@ -1018,11 +1019,12 @@ hipError_t launch_decode_stream(const DecodeArgs& a, void* workspace, hipStream_
   int* hdr = reinterpret_cast<int*>(ws);
   int* prefix = reinterpret_cast<int*>(ws + 256);
   int* first = reinterpret_cast<int*>(ws + 256 + ((size_t)(sa.TB + 1) * 4 + 255) / 256 * 256);
-  int4* udesc = reinterpret_cast<int4*>(reinterpret_cast<unsigned char*>(first) +
+  int4* mdesc = reinterpret_cast<int4*>(reinterpret_cast<unsigned char*>(first) +
                                         ((size_t)sa.ranges * 4 + 255) / 256 * 256);
+  int4* udesc = mdesc + sa.ranges;
   float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(udesc) +
                                          ((size_t)(sa.TB + 1) * 16 + 255) / 256 * 256);
-  sa.hdr = hdr; sa.prefix = prefix; sa.first = first; sa.udesc = udesc; sa.part = part;
+  sa.hdr = hdr; sa.prefix = prefix; sa.first = first; sa.mdesc = mdesc; sa.udesc = udesc; sa.part = part;
   hipError_t e;
   const int U = a.Hq / kHPW;
 #ifndef PKV_NO_GROUPS
@@ -1041,7 +1043,7 @@ hipError_t launch_decode_stream(const DecodeArgs& a, void* workspace, hipStream_
     const PlanFinish fin{a.out, a.lse_out, a.Hq, a.D, a.bf16};
     e = sa.inl ? hipSuccess
                : launch_plan(a.context_lens, a.B, a.T, sa.ranges, a.max_blocks, hdr, prefix, first, udesc, stream,
-                             nullptr, nullptr, 1, &fin);
+                             nullptr, nullptr, 1, &fin, mdesc);
   }
   if (e != hipSuccess) return e;
   return launch_main(sa, stream);

@@ -17,7 +17,10 @@
 // Work distribution is the balanced one of the VALU path: a fixed grid of
 // persistent workgroups, one wave per KV head, splits the block list of all
 // sequences into equal ranges; sequences cut by range boundaries leave
-// normalised partials merged by log-sum-exp weights.
+// normalised partials merged by log-sum-exp weights.  While B + 1 fits the
+// workgroup's LDS list (kInlinePerWave entries per wave) every workgroup scans
+// the lengths itself and keeps the per-sequence block prefix sums in LDS;
+// otherwise the planning kernel writes them to the workspace first.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 #include "pkv_tile.h"
@@ -28,17 +31,73 @@ namespace {
 constexpr int kBS = 16;
 constexpr int kMaxWpg = 8;
 
+constexpr int kInlinePerWave = 512;            // LDS prefix entries per wave
+constexpr int kInlinePT = kInlinePerWave / 64;  // sequences per thread
+constexpr int kMinBlocksPerRange = 16;
+
 struct VerifyArgs {
   DecodeArgs a;
-  const int* hdr;     // [total, per, tbtot]
-  const int* prefix;  // [B + 1] blocks per sequence, prefix sums
+  int* hdr;           // [total, per, tbtot]
+  int* prefix;        // [B + 1] blocks per sequence, prefix sums
   const int* first;   // [ranges] first non-empty sequence of each range (index into udesc)
   const int4* udesc;  // [B + 1] non-empty sequences, x = sequence
   float* part;        // [(ranges + B)][T][Hq][D + 1]
   int ranges;
 };
 
-template <int D, int PD>
+// Block prefix sums of the sequences (blocks = ceil(L / 16)) into sp[0..B],
+// by the whole workgroup; returns the total.  Workgroup g publishes entries
+// g*threads + tid (+ multiples of all threads) and workgroup 0 the header, for
+// the merge kernel.
+__device__ __forceinline__ int verify_inline_prefix(const VerifyArgs& va, int* sp, int* wsc) {
+  const DecodeArgs& a = va.a;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), nw = blockDim.x >> 6;
+  const int max_tokens = a.max_blocks * kBS;
+  int nb[kInlinePT];
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < kInlinePT; ++j) {
+    const int i = tid * kInlinePT + j;
+    nb[j] = i < a.B ? (clampi(a.context_lens[i], 0, max_tokens) + kBS - 1) / kBS : 0;
+    sum += nb[j];
+  }
+  int is = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(is, off);
+    if (lane >= off) is += y;
+  }
+  if (lane == 63) wsc[wave] = is;
+  __syncthreads();
+  int run = is - sum, total = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int v = wsc[w];
+    if (w < wave) run += v;
+    total += v;
+  }
+#pragma unroll
+  for (int j = 0; j < kInlinePT; ++j) {
+    const int i = tid * kInlinePT + j;
+    if (i <= a.B) sp[i] = run;   // i = B: the total
+    run += nb[j];
+  }
+  __syncthreads();
+  {   // the merge kernel reads prefix and per
+    for (int k = blockIdx.x * blockDim.x + tid; k <= a.B; k += gridDim.x * blockDim.x) va.prefix[k] = sp[k];
+    if (blockIdx.x == 0 && tid == 0) {
+      va.hdr[0] = total;
+      va.hdr[1] = max(kMinBlocksPerRange, (total + va.ranges - 1) / va.ranges);
+      va.hdr[2] = total;
+    }
+  }
+  return total;
+}
+
+// INL: prefix sums computed in the kernel (LDS); otherwise read from the
+// workspace written by the planning kernel.  LDS (dynamic): one V tile per
+// wave, then with INL the prefix list.
+template <int D, int PD, bool INL>
 __global__ __launch_bounds__(64 * kMaxWpg) void verify_mfma_kernel(VerifyArgs va, float scale_log2e) {
   constexpr int DT = D / 16;
   const DecodeArgs& a = va.a;
@@ -47,14 +106,37 @@ __global__ __launch_bounds__(64 * kMaxWpg) void verify_mfma_kernel(VerifyArgs va
   const int rng = blockIdx.x / (a.Hkv / wpg);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kv = (blockIdx.x % (a.Hkv / wpg)) * wpg + wave;
-  const int total = va.hdr[0], per = va.hdr[1];
+  extern __shared__ __attribute__((aligned(16))) unsigned char vlds[];
+  unsigned char* vtile = vlds + wave * (kBS * tile::kVRow);
+  int* sprefix = reinterpret_cast<int*>(vlds + wpg * (kBS * tile::kVRow));
+  __shared__ int wsc[16];
+  int total, per;
+  if constexpr (INL) {
+    total = __builtin_amdgcn_readfirstlane(verify_inline_prefix(va, sprefix, wsc));
+    per = max(kMinBlocksPerRange, (total + va.ranges - 1) / va.ranges);
+  } else {
+    total = va.hdr[0];
+    per = va.hdr[1];
+  }
+  auto prefix_of = [&](int i) -> int {
+    if constexpr (INL) return sprefix[i];
+    else return va.prefix[i];
+  };
   const int F0 = rng * per;
   if (F0 >= total) return;
   const int F1 = min(total, F0 + per);
-  int b = va.udesc[va.first[rng]].x;
-
-  __shared__ __attribute__((aligned(16))) unsigned char vtile_all[kMaxWpg][kBS * tile::kVRow];
-  unsigned char* vtile = vtile_all[wave];
+  int b;
+  if constexpr (INL) {
+    // the sequence holding block F0: largest b < B with prefix[b] <= F0
+    int lo = 0, hi = a.B;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (sprefix[mid] <= F0) lo = mid; else hi = mid;
+    }
+    b = __builtin_amdgcn_readfirstlane(lo);
+  } else {
+    b = va.udesc[va.first[rng]].x;
+  }
 
   const int G = a.Hq / a.Hkv;
   const int R = a.T * G;                 // query rows of this KV head (<= 16)
@@ -72,7 +154,7 @@ __global__ __launch_bounds__(64 * kMaxWpg) void verify_mfma_kernel(VerifyArgs va
   const int max_tokens = a.max_blocks * kBS;
 
   while (true) {
-    const int pstart = va.prefix[b], plen = va.prefix[b + 1] - pstart;
+    const int pstart = prefix_of(b), plen = prefix_of(b + 1) - pstart;
     const int js = max(F0, pstart) - pstart;
     const int je = min(F1, pstart + plen) - pstart;
     const bool direct = pstart >= F0 && pstart + plen <= F1;
@@ -212,15 +294,24 @@ hipError_t launch_verify_mfma(const DecodeArgs& a, void* workspace, hipStream_t 
   float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(udesc) +
                                          (((size_t)a.B + 1) * 16 + 255) / 256 * 256);
   va.hdr = hdr; va.prefix = prefix; va.first = first; va.udesc = udesc; va.part = part;
-  // one unit per sequence: blocks = ceil(L / 16)
-  hipError_t e = launch_plan(a.context_lens, a.B, 1, va.ranges, a.max_blocks, hdr, prefix, first, udesc, stream);
-  if (e != hipSuccess) return e;
   const int wpg = a.Hkv < kMaxWpg ? a.Hkv : kMaxWpg;
+  const size_t tiles = (size_t)wpg * kBS * tile::kVRow;
+  const size_t lds_inl = tiles + (size_t)kInlinePerWave * wpg * 4;
+  const bool inl = inline_plan_enabled() && a.B + 1 <= kInlinePerWave * wpg &&
+                   lds_inl + 64 <= (size_t)device_lds_per_block();
+  hipError_t e = hipSuccess;
+  // one unit per sequence: blocks = ceil(L / 16)
+  if (!inl) e = launch_plan(a.context_lens, a.B, 1, va.ranges, a.max_blocks, hdr, prefix, first, udesc, stream);
+  if (e != hipSuccess) return e;
   const float sl2 = a.scale * kLog2e;
-  if (a.D == 64)
-    hipLaunchKernelGGL((verify_mfma_kernel<64, 2>), dim3(va.ranges * (a.Hkv / wpg)), dim3(64 * wpg), 0, stream, va, sl2);
-  else
-    hipLaunchKernelGGL((verify_mfma_kernel<128, 2>), dim3(va.ranges * (a.Hkv / wpg)), dim3(64 * wpg), 0, stream, va, sl2);
+  const dim3 grid(va.ranges * (a.Hkv / wpg)), block(64 * wpg);
+  if (a.D == 64) {
+    if (inl) hipLaunchKernelGGL((verify_mfma_kernel<64, 2, true>), grid, block, lds_inl, stream, va, sl2);
+    else hipLaunchKernelGGL((verify_mfma_kernel<64, 2, false>), grid, block, tiles, stream, va, sl2);
+  } else {
+    if (inl) hipLaunchKernelGGL((verify_mfma_kernel<128, 2, true>), grid, block, lds_inl, stream, va, sl2);
+    else hipLaunchKernelGGL((verify_mfma_kernel<128, 2, false>), grid, block, tiles, stream, va, sl2);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int waves = a.B * a.T * (a.Hq / 4);
   if (a.D == 64)

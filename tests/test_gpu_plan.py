@@ -7,7 +7,8 @@ against the oracle.  Cases: unit lists just under and at the LDS capacity of
 every workgroup width, ranges that span hundreds of one-block units (query
 staging refilled many times), one long sequence among many short ones (a unit
 cut by many range boundaries), multi-row units (T > 1 on the VALU path) and a
-batch smaller than the number of ranges."""
+batch smaller than the number of ranges.  The multi-query verify tile plans
+the same way (per-sequence block prefix sums, 512 LDS entries per wave)."""
 import numpy as np
 import pytest
 import torch
@@ -106,3 +107,30 @@ def test_llama8b_shape_both_plans(monkeypatch):
     ref, ref_lse = oracle.paged_attention(*oracle_inputs(w, sel), w.scale, w.block_size)
     check_attention(o_in[sel], ref, "bf16", "8B sample")
     check_lse(l_in[sel], ref_lse, "8B sample")
+
+
+@pytest.mark.parametrize("Hq,Hkv,T,D,B", [(8, 2, 4, 128, 1023), (8, 2, 4, 128, 1024), (32, 8, 2, 64, 4095)])
+def test_verify_prefix_at_lds_capacity(monkeypatch, Hq, Hkv, T, D, B):
+    """Verify tile (T*G <= 16 rows per KV head), LDS list of 512 entries per
+    wave: B + 1 at the capacity (planned inline) and one past it (planning
+    kernel)."""
+    rng = np.random.Generator(np.random.PCG64(51 + B))
+    lens = rng.integers(T, 80, size=B)
+    w = workload.uniform_batch("vcap", seed=52, B=B, T=T, Hq=Hq, Hkv=Hkv, D=D, dtype="bf16", lens=lens)
+    say("verify cap", Hq, Hkv, T, D, "B", B)
+    both_plans_and_oracle(w, monkeypatch, f"verify Hq={Hq} Hkv={Hkv} T={T} B={B}")
+
+
+def test_longctx_verify_both_plans(monkeypatch):
+    """The long-context verify batch: both plans give the same bits; two
+    sequences against the oracle."""
+    w = workload.longctx_verify()
+    d = upload(w)
+    say("longctx both plans")
+    o_in, l_in = run(w, d, monkeypatch, True)
+    o_pk, l_pk = run(w, d, monkeypatch, False)
+    assert np.array_equal(o_in, o_pk) and np.array_equal(l_in, l_pk)
+    sel = [0, 9]
+    ref, ref_lse = oracle.paged_attention(*oracle_inputs(w, sel), w.scale, w.block_size)
+    check_attention(o_in[sel], ref, "bf16", "longctx sample")
+    check_lse(l_in[sel], ref_lse, "longctx sample")
