@@ -8,6 +8,10 @@ log-sum-exp merge when the workload is split).  Inputs are seeded synthetic
 tensors already resident in HBM.  Prints ONE JSON line with seq-steps/s, the
 roofline of the decode call (algorithmic bytes / event-timed duration against
 the 8 TB/s HBM peak) and the CPU oracle timed on a bounded sample.
+
+The roofline figure is warm: consecutive calls on the same batch, as in a
+decode loop.  roofline.cold_cache repeats the call after a 1 GiB flush of the
+caches (outside the timed events) and reports its percentiles beside it.
 """
 from __future__ import annotations
 
@@ -26,6 +30,7 @@ sys.path.insert(0, ROOT)
 import workload  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix peak of MI355X
 METRIC = "seq-steps/s and achieved HBM GB/s (% of peak) for paged decode attention"
 DEFAULT_WORKLOAD = "llama8b_prefix_share"
 
@@ -53,6 +58,14 @@ def algorithmic_bytes(w):
     append = 2 * 2 * w.B * w.T * row if w.lens_pre is not None else 0   # k_new+v_new read and written
     return dict(decode=kv_unique + qo + tables, logical=kv_logical + qo + tables, append=append,
                 kv_unique=kv_unique, kv_logical=kv_logical)
+
+
+def attention_flops(w):
+    """Useful flops of the attention: 4*D per (query row, visible key) pair
+    (2*D for q.k, 2*D for p*v); masked pairs are not counted."""
+    t = np.arange(w.T)
+    vis = np.clip(w.context_lens[:, None].astype(np.int64) - w.T + t[None, :] + 1, 0, None)
+    return int(vis.sum()) * w.Hq * 4 * w.D
 
 
 def cpu_baseline(w, budget_s):
@@ -133,6 +146,8 @@ def main():
     ap.add_argument("--partition", type=int, default=None, help="split-KV partition size (tokens); 0 = single pass")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-reps", type=int, default=20,
+                    help="extra untimed-region reps, each after a 1 GiB cache flush, for the cold-cache figure")
     ap.add_argument("--ceiling", action="store_true",
                     help="also time a plain 1 GiB device copy (torch) and the random-slice read probe")
     args = ap.parse_args()
@@ -170,14 +185,21 @@ def main():
     scale = float(w.scale)
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    prefill = w.T > 16   # a chunked-prefill workload: paged_attention_prefill
+
+    def attention():
+        if prefill:
+            pkv.paged_attention_prefill(q, kp, vp, tables, lens, out=out, scale=scale, stream=stream)
+        else:
+            pkv.paged_attention_decode(q, kp, vp, tables, lens, out=out, scale=scale, partition_size=part,
+                                       workspace=ws, stream=stream)
 
     def step(i=None):
         if has_append:
             pkv.paged_kv_append(k_new, v_new, kp, vp, tables, lens_pre, stream=stream)
         if i is not None:
             ev[i][0].record(stream)
-        pkv.paged_attention_decode(q, kp, vp, tables, lens, out=out, scale=scale, partition_size=part,
-                                   workspace=ws, stream=stream)
+        attention()
         if i is not None:
             ev[i][1].record(stream)
 
@@ -191,6 +213,24 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
     decode_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    warm = np.array([a.elapsed_time(b) for a, b in ev])
+
+    # Cold cache: before each rep a 1 GiB buffer is read and written (more than
+    # the 256 MB last-level cache plus the L2s), outside the timed events.
+    cold = np.array([])
+    if args.cold_reps > 0:
+        flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.cold_reps)]
+        for a, b in cev:
+            flush.add_(1.0)
+            a.record(stream)
+            attention()
+            b.record(stream)
+        torch.cuda.synchronize()
+        cold = np.array([a.elapsed_time(b) for a, b in cev])
+        del flush
 
     nb = algorithmic_bytes(w)
     achieved = nb["decode"] / (decode_ms * 1e-3) / 1e9
@@ -207,8 +247,31 @@ def main():
                      "kernel": ("paged_attention_decode call (plan + balanced decode + boundary merge)" if part == 0
                                 else "paged_attention_decode call (partition kernel + lse merge)"),
                      "bytes_per_launch": nb["decode"], "launch_ms": round(decode_ms, 5),
+                     "launch_ms_p10_p50_p90": [round(float(np.percentile(warm, p)), 5) for p in (10, 50, 90)],
                      "logical_GBps": round(nb["logical"] / (decode_ms * 1e-3) / 1e9, 1)},
     }
+    if prefill:
+        # compute-bound: useful flops against the dense bf16 matrix peak
+        fl = attention_flops(w)
+        tf = fl / (decode_ms * 1e-3) / 1e12
+        result["roofline"] = {
+            "bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "kernel": "paged_attention_prefill (MFMA tiles, LDS-staged K/V)", "flops_per_launch": fl,
+            "launch_ms": round(decode_ms, 5),
+            "launch_ms_p10_p50_p90": [round(float(np.percentile(warm, p)), 5) for p in (10, 50, 90)],
+            "bytes_per_launch": nb["decode"], "hbm_GBps": round(achieved, 1)}
+        result["tokens_per_s"] = round(w.B * w.T / (ms_step * 1e-3), 1)
+    if cold.size:
+        cold_med = float(np.median(cold))
+        cc = {"reps": int(cold.size),
+              "launch_ms_p10_p50_p90": [round(float(np.percentile(cold, p)), 5) for p in (10, 50, 90)]}
+        if prefill:
+            cc["TFLOPs_at_median"] = round(attention_flops(w) / (cold_med * 1e-3) / 1e12, 1)
+        else:
+            cc["GBps_at_median"] = round(nb["decode"] / (cold_med * 1e-3) / 1e9, 1)
+            cc["frac_at_median"] = round(nb["decode"] / (cold_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        result["roofline"]["cold_cache"] = cc
     if args.ceiling:
         result["copy_ceiling"] = copy_ceiling(torch, dev)
         result["read_ceiling"] = read_ceiling(torch, dev)

@@ -167,6 +167,30 @@ pkv_status paged_attention_decode(const void* q, const void* k_pool, const void*
                                   void* workspace, size_t workspace_bytes, pkv_dtype dtype, void* stream);
 
 /*
+ * paged_attention_prefill -- chunked-prefill attention over the paged cache
+ * ("Efficient LLM Inference", KV Caching: Verify Reuse, Positions and
+ * Windows: attending a prompt chunk by chunk against the cached prefix equals
+ * one pass over the whole prefix; "LLM Inference from Scratch", Architecture
+ * overview, M1).  The T chunk tokens of sequence b have already been appended
+ * (paged_kv_append), so context_lens[b] = L counts them; query t sits at
+ * position L - T + t and attends causally to keys 0 .. L - T + t:
+ *   out[b, t, h, :] = softmax_j(scale * q[b, t, h, :] . K_b[j, h / G, :]) V_b[j, h / G, :]
+ * with G = Hq / Hkv.  Same layouts, ownership, lse_out and stream semantics as
+ * paged_attention_decode; no workspace (every output row is finished by the
+ * workgroup that owns it).
+ * Supported: bf16 only (PKV_EUNSUPPORTED for fp32), D in {64, 128},
+ * Hq / Hkv in {1, 2, 4, 8}, 1 <= T <= 8192, block_size 16.  The device-side
+ * contract T <= L <= max_blocks * block_size is the decode one (checked under
+ * PKV_DEBUG=1).  Work is split into items of 128 query rows of one KV head;
+ * K and V of the item's visible keys are read once per item.
+ */
+pkv_status paged_attention_prefill(const void* q, const void* k_pool, const void* v_pool,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   void* out, float* lse_out,
+                                   int B, int T, int Hq, int Hkv, int D, int block_size, int max_blocks,
+                                   int N_blocks, float scale, pkv_dtype dtype, void* stream);
+
+/*
  * lse_reduce -- merge P_max normalised partial attention results per row by
  * their log-sum-exp ("Inference From Scratch", ch. 8: softmax pieces over
  * disjoint key ranges combine through their running max and sum):

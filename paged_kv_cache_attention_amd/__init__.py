@@ -18,7 +18,7 @@ PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP = range(5)
 PKV_FP32, PKV_BF16 = 0, 1
 STATUS_NAMES = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_EWORKSPACE", 4: "PKV_EHIP"}
 EXPORTS = ("paged_kv_append", "paged_kv_gather", "pkv_decode_workspace_bytes", "paged_attention_decode",
-           "lse_reduce", "pkv_last_error")
+           "paged_attention_prefill", "lse_reduce", "pkv_last_error")
 
 _lib = None
 
@@ -46,6 +46,8 @@ def load_library(path: pathlib.Path = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_decode_workspace_bytes.restype = S
     lib.paged_attention_decode.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, S, I, P]
     lib.paged_attention_decode.restype = I
+    lib.paged_attention_prefill.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P]
+    lib.paged_attention_prefill.restype = I
     lib.lse_reduce.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
     lib.lse_reduce.restype = I
     lib.pkv_last_error.argtypes = []
@@ -145,6 +147,25 @@ def paged_attention_decode(q, k_pool, v_pool, block_tables, context_lens, out=No
                                       _i32(context_lens, "context_lens"), _ptr(out), _ptr(lse_out), B, T, Hq, Hkv, D,
                                       bs, max_blocks, N, float(scale), int(partition_size), _ptr(workspace), ws_bytes,
                                       _dtype_code(q), _stream(stream, q.device)))
+    return out
+
+
+def paged_attention_prefill(q, k_pool, v_pool, block_tables, context_lens, out=None, lse_out=None, scale=None,
+                            stream=None):
+    """Chunked-prefill attention of q [B,T,Hq,D] (bf16) over the paged cache;
+    query t of sequence b sees keys 0 .. context_lens[b] - T + t.  Returns out."""
+    torch = _torch()
+    lib = load_library()
+    B, T, Hq, D = q.shape
+    N, bs, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
+    max_blocks = block_tables.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if scale is None:
+        scale = 1.0 / D ** 0.5
+    _check(lib.paged_attention_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool), _i32(block_tables, "block_tables"),
+                                       _i32(context_lens, "context_lens"), _ptr(out), _ptr(lse_out), B, T, Hq, Hkv, D,
+                                       bs, max_blocks, N, float(scale), _dtype_code(q), _stream(stream, q.device)))
     return out
 
 

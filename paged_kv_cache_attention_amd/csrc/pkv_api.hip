@@ -198,6 +198,37 @@ pkv_status paged_attention_decode(const void* q, const void* k_pool, const void*
                   "lse_reduce launch");
 }
 
+pkv_status paged_attention_prefill(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                                   const int32_t* context_lens, void* out, float* lse_out, int B, int T, int Hq, int Hkv,
+                                   int D, int block_size, int max_blocks, int N_blocks, float scale, pkv_dtype dtype,
+                                   void* stream) {
+  pkv_status st = check_dtype(dtype);
+  if (st != PKV_OK) return st;
+  if (B < 0 || T < 1 || Hq < 1) return fail(PKV_EINVAL, "B must be >= 0, T and Hq >= 1");
+  if ((st = check_pool_shape(Hkv, D, block_size, max_blocks, N_blocks)) != PKV_OK) return st;
+  if (Hq % Hkv) return fail(PKV_EINVAL, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(PKV_EUNSUPPORTED, "Hq/Hkv = %d unsupported", G);
+  if (dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "paged_attention_prefill computes in bf16 only");
+  if (T > pkv::kPrefillMaxT) return fail(PKV_EUNSUPPORTED, "T = %d unsupported (at most %d)", T, pkv::kPrefillMaxT);
+  if (!std::isfinite(scale)) return fail(PKV_EINVAL, "scale must be finite");
+  if (B == 0) return PKV_OK;
+  if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out) return fail(PKV_EINVAL, "null pointer argument");
+  if (out == q || out == k_pool || out == v_pool) return fail(PKV_EINVAL, "out must not alias an input");
+  if ((long long)B * T * Hq > (1LL << 30)) return fail(PKV_EINVAL, "B*T*Hq too large");
+
+  pkv::DecodeArgs a{};
+  a.q = q; a.k_pool = k_pool; a.v_pool = v_pool; a.block_tables = block_tables; a.context_lens = context_lens;
+  a.out = out; a.lse_out = lse_out;
+  a.B = B; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.block_size = block_size; a.max_blocks = max_blocks;
+  a.N_blocks = N_blocks; a.scale = scale; a.bf16 = true;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug_enabled() && (st = debug_validate(block_tables, context_lens, B, T, 0, block_size, max_blocks, N_blocks, s)) !=
+                             PKV_OK)
+    return st;
+  return from_hip(pkv::launch_prefill(a, s), "paged_attention_prefill launch");
+}
+
 pkv_status lse_reduce(const float* part_out, const float* part_lse, void* out, float* lse_out, int B, int T, int Hq,
                       int D, int P_max, pkv_dtype out_dtype, void* stream) {
   pkv_status st = check_dtype(out_dtype);

@@ -65,6 +65,11 @@ struct GroupPlan {
 // last-level cache already serves most re-reads of a shared prefix, and the
 // detection and the group workgroups cost more than they save on the
 // prefix-sharing 8B-shaped batch (measured 243 us with groups, 238 us without).
+// Chunked-prefill attention (T up to kPrefillMaxT causal query rows per
+// sequence, bf16) on MFMA tiles with LDS-staged keys and values.
+constexpr int kPrefillMaxT = 8192;
+hipError_t launch_prefill(const DecodeArgs& a, hipStream_t stream);
+
 bool groups_enabled();
 // Plan inside the decode kernel when the unit list fits in LDS (default;
 // PKV_INLINE_PLAN=0 launches the planning kernel instead).

@@ -207,7 +207,7 @@ __global__ __launch_bounds__(64 * kMaxWpg) void verify_mfma_kernel(VerifyArgs va
 template <int D>
 __global__ __launch_bounds__(256) void verify_merge_kernel(VerifyArgs va) {
   constexpr int EPL = D / 16;
-  constexpr int BATCH = 8;
+  constexpr int BATCH = 16;   // pieces whose loads are issued together
   const DecodeArgs& a = va.a;
   const int lane = threadIdx.x & 63;
   const int gidx = blockIdx.x * 4 + (threadIdx.x >> 6);     // ((b * T + t) * Hq/4 + hq)

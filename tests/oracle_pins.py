@@ -180,6 +180,30 @@ def pin_torch_sdpa_causal_verify():
         np.testing.assert_allclose(out[b], ref[:, L - T:, :].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
 
 
+def pin_torch_sdpa_chunked_prefill():
+    """A chunk of T = 37 query tokens (chunked prefill) equals the last 37 rows of
+    a causal full-prefix forward (torch SDPA, is_causal), for GQA 8/2; one
+    sequence is the chunk alone (L = T), the others have a cached prefix."""
+    T = 37
+    p = random_problem(15, T=T, Hq=8, Hkv=2, lens=(37, 52, 90))
+    out, lse = _run(p)
+    g = 4
+    rng = np.random.default_rng(98)
+    for b, L in enumerate(p["lens"]):
+        K = torch.from_numpy(np.repeat(p["Klog"][b], g, axis=1)).permute(1, 0, 2)
+        V = torch.from_numpy(np.repeat(p["Vlog"][b], g, axis=1)).permute(1, 0, 2)
+        Qfull = rng.standard_normal((8, int(L), K.shape[-1]))
+        Qfull[:, L - T:, :] = p["q"][b].transpose(1, 0, 2)
+        ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(Qfull), K, V, is_causal=True,
+                                                               scale=p["scale"])
+        np.testing.assert_allclose(out[b], ref[:, L - T:, :].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+        # lse of row t: log-sum-exp over the keys it sees
+        s = p["scale"] * torch.einsum("hld,hmd->hlm", torch.from_numpy(Qfull), K)
+        mask = torch.ones(int(L), int(L), dtype=torch.bool).tril()
+        ref_lse = torch.logsumexp(s.masked_fill(~mask, float("-inf")), dim=-1)[:, L - T:]
+        np.testing.assert_allclose(lse[b], ref_lse.permute(1, 0).numpy(), rtol=0, atol=1e-12)
+
+
 def pin_brute_force_fsum():
     """Tiny fp32 workload: every output recomputed with scalar loops and math.fsum."""
     w = workload.tiny_fp32()
@@ -343,6 +367,7 @@ def pin_bf16_rounding():
 ALL_PINS = [
     pin_golden_two_token, pin_golden_gqa_causal_verify, pin_golden_gqa_head_mapping, pin_golden_lse_merge,
     pin_gather_inverse_scatter, pin_append_then_gather, pin_torch_sdpa_decode, pin_torch_sdpa_causal_verify,
+    pin_torch_sdpa_chunked_prefill,
     pin_brute_force_fsum, pin_closed_forms, pin_dominant_score, pin_key_shift_invariance,
     pin_physical_permutation, pin_gqa_equals_repeated_mha, pin_verify_equals_decode_chain,
     pin_split_equals_full, pin_lse_merge_algebra, pin_bf16_rounding,

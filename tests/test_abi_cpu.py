@@ -80,6 +80,42 @@ def test_decode_empty_batch_is_a_noop():
     assert st == pkv.PKV_OK
 
 
+def _prefill(**kw):
+    args = dict(q=Q, k=K, v=V, tab=TAB, lens=LENS, out=OUT, lse=None, B=2, T=64, Hq=8, Hkv=2, D=128, bs=16, mb=8,
+                N=16, scale=0.088, dt=pkv.PKV_BF16)
+    args.update(kw)
+    lib = pkv.load_library()
+    st = lib.paged_attention_prefill(args["q"], args["k"], args["v"], args["tab"], args["lens"], args["out"],
+                                     args["lse"], args["B"], args["T"], args["Hq"], args["Hkv"], args["D"], args["bs"],
+                                     args["mb"], args["N"], args["scale"], args["dt"], None)
+    return st, lib.pkv_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), pkv.PKV_EINVAL),
+    (dict(out=None), pkv.PKV_EINVAL),
+    (dict(out=K), pkv.PKV_EINVAL),                  # out aliases k_pool
+    (dict(Hq=6, Hkv=4), pkv.PKV_EINVAL),
+    (dict(T=0), pkv.PKV_EINVAL),
+    (dict(scale=float("inf")), pkv.PKV_EINVAL),
+    (dict(dt=3), pkv.PKV_EINVAL),
+    (dict(dt=pkv.PKV_FP32), pkv.PKV_EUNSUPPORTED),
+    (dict(D=80), pkv.PKV_EUNSUPPORTED),
+    (dict(bs=8), pkv.PKV_EUNSUPPORTED),
+    (dict(T=8193), pkv.PKV_EUNSUPPORTED),
+    (dict(Hq=32, Hkv=2), pkv.PKV_EUNSUPPORTED),     # Hq/Hkv = 16
+])
+def test_prefill_argument_errors(kw, status):
+    st, msg = _prefill(**kw)
+    assert st == status, msg
+    assert msg
+
+
+def test_prefill_empty_batch_is_a_noop():
+    st, _ = _prefill(B=0, q=None, out=None)
+    assert st == pkv.PKV_OK
+
+
 def test_append_gather_reduce_argument_errors():
     lib = pkv.load_library()
     assert lib.paged_kv_append(P, P, P, P, P, None, 2, 1, 8, 64, 16, 4, 8, pkv.PKV_BF16, None) == pkv.PKV_EINVAL

@@ -8,7 +8,8 @@ import torch
 import oracle
 import workload
 import paged_kv_cache_attention_amd as pkv
-from gpu_util import assert_within_bf16_ulp, check_attention, check_lse, dev, host, oracle_inputs, upload
+from gpu_util import (assert_within_bf16_ulp, check_attention, check_lse, dev, host, mfma_floor, oracle_inputs,
+                      upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -73,6 +74,19 @@ def test_sharp_and_overflowing_scores(factor, dtype):
             smax = np.abs(ref_lse).max()
             assert np.abs(got - ref).max() <= 1e-5 * max(1.0, smax / 4), f"x{factor}"
         check_lse(host(lse), ref_lse, f"sharp x{factor}")
+
+
+@pytest.mark.parametrize("factor", [4.0, 64.0])
+def test_verify_tile_sharp_and_overflowing_scores(factor):
+    """The same two variants through the MFMA verify tile (T*G = 16 rows)."""
+    w = workload.uniform_batch("vsharp", seed=9, B=4, T=4, Hq=16, Hkv=4, D=128, dtype="bf16",
+                               lens=[4, 40, 300, 1000])
+    w = workload.scaled_queries(w, factor)
+    say("verify sharp", factor)
+    out, lse = decode(w, upload(w), 0)
+    ref, ref_lse = oracle.paged_attention(*oracle_inputs(w), w.scale, w.block_size)
+    check_attention(host(out), ref, "bf16", f"verify q x{factor}", floor=mfma_floor(w))
+    check_lse(host(lse), ref_lse, f"verify q x{factor}")
 
 
 def test_split_sizes_agree_and_runs_are_deterministic():

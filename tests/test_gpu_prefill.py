@@ -1,0 +1,118 @@
+"""Chunked-prefill attention (paged_attention_prefill) against the oracle.
+
+Query t of a T-token chunk sits at position L - T + t and sees keys
+0 .. L - T + t, which is exactly the oracle's causal definition for any T.
+Cases cover: a chunk with no cached prefix (L = T), prefixes ending on and
+just past block and 32-key step boundaries, every GQA ratio, row groups that
+fill only some waves of the workgroup, T = 1, sharp and overflowing scores,
+poisoned unread slots, physical relabelling (bit-identical), repeatability,
+and the 8B-shaped chunked-prefill batch (append then prefill) on sampled
+sequences."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload
+import paged_kv_cache_attention_amd as pkv
+from gpu_util import appended_oracle_pools, check_attention, check_lse, host, mfma_floor, oracle_inputs, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def prefill(w, d, lse=True):
+    lse_t = torch.full((w.B, w.T, w.Hq), float("nan"), device="cuda") if lse else None
+    out = pkv.paged_attention_prefill(d["q"], d["k"], d["v"], d["tables"], d["lens"], lse_out=lse_t,
+                                      scale=float(w.scale))
+    torch.cuda.synchronize()
+    return host(out), (host(lse_t) if lse else None)
+
+
+def check_vs_oracle(w, out, lse, where, seqs=None):
+    ref, ref_lse = oracle.paged_attention(*oracle_inputs(w, seqs), w.scale, w.block_size)
+    sel = slice(None) if seqs is None else list(seqs)
+    check_attention(out[sel], ref, "bf16", where, floor=mfma_floor(w))
+    if lse is not None:
+        check_lse(lse[sel], ref_lse, where)
+
+
+SHAPES = [  # (D, Hq, Hkv, T, lens)
+    (128, 32, 8, 64, [64, 65, 80, 96, 200, 333]),     # G=4, two row groups
+    (64, 8, 8, 100, [100, 117, 260]),                 # G=1, last wave half full
+    (128, 16, 8, 37, [37, 38, 500]),                  # G=2
+    (64, 32, 4, 17, [17, 40, 1000]),                  # G=8, a second group of 8 rows
+    (128, 32, 8, 1, [1, 30, 300]),                    # T=1 through the prefill path
+    (128, 8, 8, 300, [300, 301, 700]),                # MHA, three row groups
+    (64, 16, 4, 129, [129, 161, 192, 2000]),          # prefix ends on a 32-key step, long prefix
+]
+
+
+@pytest.mark.parametrize("D,Hq,Hkv,T,lens", SHAPES)
+def test_prefill_shapes(D, Hq, Hkv, T, lens):
+    w = workload.uniform_batch("prefill", seed=61 + T, B=len(lens), T=T, Hq=Hq, Hkv=Hkv, D=D, dtype="bf16",
+                               lens=lens)
+    say("prefill", D, Hq, Hkv, T, lens)
+    out, lse = prefill(w, upload(w))
+    check_vs_oracle(w, out, lse, f"prefill D={D} Hq={Hq} Hkv={Hkv} T={T}")
+
+
+@pytest.mark.parametrize("factor", [4.0, 64.0])
+def test_prefill_sharp_and_overflowing_scores(factor):
+    """q x4 sharpens the softmax; q x64 pushes scores far past the exp range."""
+    w = workload.uniform_batch("sharp", seed=71, B=3, T=48, Hq=16, Hkv=4, D=128, dtype="bf16", lens=[48, 90, 400])
+    w = workload.scaled_queries(w, factor)
+    say("prefill sharp", factor)
+    out, lse = prefill(w, upload(w))
+    check_vs_oracle(w, out, lse, f"prefill q x{factor}")
+
+
+def test_prefill_relabel_bit_identical_and_repeatable():
+    w = workload.uniform_batch("relabel", seed=81, B=4, T=70, Hq=32, Hkv=8, D=128, dtype="bf16",
+                               lens=[70, 100, 333, 1024])
+    say("prefill relabel")
+    d = upload(w)
+    o1, l1 = prefill(w, d)
+    o2, l2 = prefill(w, d)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    w2 = workload.relabel_physical(w, seed=5)
+    o3, l3 = prefill(w2, upload(w2))
+    assert np.array_equal(o1, o3) and np.array_equal(l1, l3)
+
+
+def test_prefill_rows_equal_decode_rows():
+    """Row t of a chunk is the single-token decode of position L - T + t."""
+    T = 20
+    w = workload.uniform_batch("chain", seed=91, B=2, T=T, Hq=32, Hkv=8, D=128, dtype="bf16", lens=[60, 301])
+    say("prefill vs decode rows")
+    d = upload(w)
+    out, _ = prefill(w, d, lse=False)
+    for t in (0, 7, T - 1):
+        lens_t = torch.from_numpy((w.context_lens - T + t + 1).astype(np.int32)).cuda()
+        dec = pkv.paged_attention_decode(d["q"][:, t:t + 1].contiguous(), d["k"], d["v"], d["tables"], lens_t,
+                                         scale=float(w.scale))
+        torch.cuda.synchronize()
+        ref, _ = oracle.paged_attention(w.values(w.q)[:, t:t + 1], w.values(w.k_pool), w.values(w.v_pool),
+                                        w.block_tables, w.context_lens - T + t + 1, w.scale, w.block_size)
+        check_attention(out[:, t:t + 1], ref, "bf16", f"prefill row {t}", floor=mfma_floor(w))
+        check_attention(host(dec), ref, "bf16", f"decode row {t}")
+
+
+def test_llama8b_chunked_prefill_full():
+    """The 8B-shaped chunked-prefill batch as the benchmark runs it (append of
+    the 512-token chunks, then prefill attention), sampled sequences against
+    the oracle on the appended pools."""
+    w = workload.llama8b_chunked_prefill()
+    say("8B chunked prefill")
+    d = upload(w)
+    pkv.paged_kv_append(d["k_new"], d["v_new"], d["k"], d["v"], d["tables"], d["lens_pre"])
+    out, lse = prefill(w, d)
+    kp, vp = appended_oracle_pools(w)
+    for b in (int(np.argmax(w.context_lens)), int(np.argmin(w.context_lens))):
+        ref, ref_lse = oracle.paged_attention(w.values(w.q)[b:b + 1], kp, vp, w.block_tables[b:b + 1],
+                                              w.context_lens[b:b + 1], w.scale, w.block_size)
+        check_attention(out[b:b + 1], ref, "bf16", f"8B prefill seq {b}", floor=mfma_floor(w))
+        check_lse(lse[b:b + 1], ref_lse, f"8B prefill seq {b}")

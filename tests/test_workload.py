@@ -34,6 +34,9 @@ def test_length_ranges():
     assert 700 < np.median(c4) < 1400
     c5 = workload.longctx_verify(structure_only=True).context_lens
     assert c5.min() >= 16384 and c5.max() <= 65536
+    pf = workload.llama8b_chunked_prefill(structure_only=True)
+    assert pf.T == 512 and (pf.context_lens == pf.lens_pre + 512).all()
+    assert pf.lens_pre.min() >= 0 and pf.lens_pre.max() <= 3584 and pf.max_blocks == 256
 
 
 def test_private_blocks_are_not_shared():

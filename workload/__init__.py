@@ -321,12 +321,32 @@ def longctx_verify(poison=True, partition_size=0, structure_only=False):
                    n_blocks_total=pool, perm=perm, max_blocks=4096, poison=poison, append=False, structure_only=structure_only)
 
 
+def llama8b_chunked_prefill(poison=True, partition_size=0, structure_only=False):
+    """B=8 sequences each prefilling a chunk of T=512 tokens (GQA 32/8, D=128,
+    bf16) after a cached prefix ~ U[0, 3584] tokens: the chunk's K/V rows are
+    appended at positions prefix .. prefix+511, then its 512 queries attend
+    causally (L = prefix + 512 <= 4096)."""
+    rng = np.random.Generator(np.random.PCG64(6))
+    T = 512
+    lens_pre = rng.integers(0, 3584, size=8, endpoint=True)
+    lens = lens_pre + T
+    nblk = [_cdiv(int(L), BLOCK_SIZE) for L in lens]
+    pool = _cdiv(11 * sum(nblk), 10)
+    perm = rng.permutation(pool)
+    per_seq = [[(b, i) for i in range(n)] for b, n in enumerate(nblk)]
+    return _finish("llama8b_chunked_prefill", rng=rng, B=8, T=T, Hq=32, Hkv=8, D=128, dtype="bf16",
+                   partition_size=partition_size, context_lens=lens, per_seq_blocks=per_seq,
+                   n_blocks_total=pool, perm=perm, max_blocks=256, poison=poison, append=True,
+                   structure_only=structure_only)
+
+
 WORKLOADS = {
     "tiny_fp32": tiny_fp32,
     "tinylm_mha_bf16": tinylm_mha_bf16,
     "llama1b_gqa_append": llama1b_gqa_append,
     "llama8b_prefix_share": llama8b_prefix_share,
     "longctx_verify": longctx_verify,
+    "llama8b_chunked_prefill": llama8b_chunked_prefill,
 }
 
 
