@@ -9,12 +9,13 @@
 // Unlike single-token decode this is a real GEMM pair per KV head:
 // T * Hq/Hkv query rows against the same keys.
 //
-// Work item = (row group of kRows query rows, sequence, KV head); rows are
-// r = t * G + g (G = Hq/Hkv).  A workgroup of kWaves waves owns one item; wave
-// w holds rows 32w .. 32w+31 as two 16-row MFMA tiles.  Keys advance kStep
-// (32) at a time, staged once per workgroup through LDS (double-buffered: the
-// next step's global loads are in flight while the tiles work on the current
-// one):
+// Work item = (row group, sequence, KV head); rows are r = t * G + g
+// (G = Hq/Hkv).  A workgroup of kWaves waves owns one item; each wave holds
+// TPW 16-row MFMA tiles (one in the shipped configuration: 64 rows per item).
+// Keys advance STEP (32) at a time, staged once per workgroup through LDS
+// (double-buffered: the next step's global loads are in flight while the
+// tiles work on the current one), with the item's block-table entries cached
+// in LDS 512 at a time:
 //   K[token][d]  row-major, padded rows        -> A operand of S^T = K Q^T
 //   V^T[d][token] transposed when staged        -> B operand of O += P V
 // Per wave and step, for each row tile:
@@ -24,6 +25,8 @@
 //     keys; P split into bf16 hi + lo so the product keeps about 16 bits of P
 // Keys at or past the group's last visible position are never used: their V
 // columns are zeroed when staged and their scores masked.
+#include <type_traits>
+
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -31,14 +34,14 @@ namespace pkv {
 namespace {
 
 constexpr int kBS = 16;
+constexpr int kTblWin = 512;   // block-table entries cached in LDS at a time
 constexpr int kWaves = 4;
-constexpr int kTilesPerWave = 2;
-constexpr int kRows = 16 * kTilesPerWave * kWaves;   // query rows per item
-constexpr int kStep = 32;                            // keys per step
 constexpr int kThreads = 64 * kWaves;
 constexpr float kSlack = 8.f;
 
 typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ bf16x8_v as_bf16x8(u32x4_t v) {
@@ -47,13 +50,28 @@ __device__ __forceinline__ bf16x8_v as_bf16x8(u32x4_t v) {
   return r;
 }
 
-template <int D>
-struct PLds {
+// Two floats to packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  const bf16x2_v r = __builtin_convertvector((f32x2_v){a, b}, bf16x2_v);
+  uint32_t u;
+  __builtin_memcpy(&u, &r, 4);
+  return u;
+}
+
+// TPW 16-row tiles per wave, STEP keys per staged step.
+template <int D, int TPW, int STEP>
+struct PGeo {
+  static constexpr int ROWS = 16 * TPW * kWaves;     // query rows per item
+  static constexpr int NQ = STEP / 16;               // 16-key quarters per step (S^T tiles)
+  static constexpr int NK = STEP / 32;               // 32-key MFMA k-chunks per step (P.V)
   static constexpr int KROW = 2 * D + 16;            // K row bytes (conflict-free 16-byte reads)
-  static constexpr int VROW = 2 * kStep + 8;         // V^T row bytes: one d, 32 keys
-  static constexpr int KBYTES = kStep * KROW;
+  static constexpr int VROW = 2 * STEP + 8;          // V^T row bytes: one d, STEP keys
+  static constexpr int KBYTES = STEP * KROW;
   static constexpr int VBYTES = D * VROW;
-  static constexpr int BYTES = 2 * (KBYTES + VBYTES);
+  static constexpr int LDS = 2 * (KBYTES + VBYTES);
+  static constexpr int RC = D * 2 / 16;              // 16-byte chunks per token row
+  static constexpr int PER_T = STEP * RC / kThreads;  // staged chunks per thread (K, and again V)
+  static_assert(PER_T * kThreads == STEP * RC, "even staging split");
 };
 
 struct PrefillArgs {
@@ -61,19 +79,23 @@ struct PrefillArgs {
   int groups;   // row groups per (sequence, KV head)
 };
 
-// Two waves per SIMD: two workgroups per CU (registers of both tiles, 256 per lane).
-template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+// Waves per SIMD the register budget is sized for: one tile per wave with
+// 32-key steps fits four at D = 64 and three at D = 128 (that many
+// workgroups per CU, 18 or 36 KB of LDS each); the other shapes two.
+template <int D, int TPW, int STEP>
+constexpr int prefill_waves_per_eu() { return TPW == 1 && STEP == 32 ? (D == 64 ? 4 : 3) : 2; }
+
+template <int D, int TPW, int STEP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefill_waves_per_eu<D, TPW, STEP>())))
 void prefill_kernel(PrefillArgs pa, float scale_log2e) {
+  using PG = PGeo<D, TPW, STEP>;
   constexpr int KS = D / 32;                          // k-steps of QK^T
   constexpr int DT = D / 16;                          // output column tiles
-  constexpr int RC = D * 2 / 16;                      // 16-byte chunks per token row
-  constexpr int PER_T = kStep * RC / kThreads;        // staged chunks per thread (K, and again V)
-  static_assert(PER_T * kThreads == kStep * RC, "even staging split");
-  using LD = PLds<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[LD::BYTES];
-  auto kst = [&](int buf) { return lds + buf * LD::KBYTES; };
-  auto vst = [&](int buf) { return lds + 2 * LD::KBYTES + buf * LD::VBYTES; };
+  constexpr int NQ = PG::NQ, NK = PG::NK, RC = PG::RC, PER_T = PG::PER_T;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[PG::LDS];
+  __shared__ int stbl[kTblWin];   // physical ids of blocks [win * kTblWin, (win + 1) * kTblWin)
+  auto kst = [&](int buf) { return lds + buf * PG::KBYTES; };
+  auto vst = [&](int buf) { return lds + 2 * PG::KBYTES + buf * PG::VBYTES; };
 
   const DecodeArgs& a = pa.a;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -87,20 +109,24 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
   const int b = rem / a.Hkv, kv = rem - (rem / a.Hkv) * a.Hkv;
   const int max_tokens = a.max_blocks * kBS;
   const int L = clampi(a.context_lens[b], 0, max_tokens);
-  const int r0 = rg * kRows;
-  const int t_last = (min(R, r0 + kRows) - 1) / G;
+  const int r0 = rg * PG::ROWS;
+  const int t_last = (min(R, r0 + PG::ROWS) - 1) / G;
   const int kv_len = clampi(L - a.T + t_last + 1, 0, L);   // keys any row of the group sees
-  const int nsteps = (kv_len + kStep - 1) / kStep;
+  const int nsteps = (kv_len + STEP - 1) / STEP;
   const int nblk = (kv_len + kBS - 1) / kBS;
 
-  // ---- this wave's rows: tile j holds rows r0 + 32 wave + 16 j + (lane % 16) ----
+  // ---- this wave's rows: tile j holds rows rw + 16 j + (lane % 16) ----
   const int row = lane & 15, quad = lane >> 4;
+  const int rw = r0 + 16 * TPW * wave;
+  const bool wave_active = rw < R;
+  // keys below the wave's smallest causal limit need no mask
+  const int hi_min = clampi(L - a.T + rw / G + 1, 0, L);
   const uint16_t* qbase = static_cast<const uint16_t*>(a.q);
-  u32x4_t qreg[kTilesPerWave][KS];
-  int hi_row[kTilesPerWave];
+  u32x4_t qreg[TPW][KS];
+  int hi_row[TPW];
 #pragma unroll
-  for (int j = 0; j < kTilesPerWave; ++j) {
-    const int r = r0 + 32 * wave + 16 * j + row;
+  for (int j = 0; j < TPW; ++j) {
+    const int r = rw + 16 * j + row;
     const bool ok = r < R;
     const int rq = ok ? r : r0;
     const int t = rq / G, g = rq - (rq / G) * G;
@@ -113,88 +139,122 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
       qreg[j][c] = ok ? v : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
-  const bool wave_active = r0 + 32 * wave < R;
 
-  floatx4_t acc[kTilesPerWave][DT];
-  float m_row[kTilesPerWave], l_part[kTilesPerWave];
+  floatx4_t acc[TPW][DT];
+  float m_row[TPW], l_part[TPW];
 #pragma unroll
-  for (int j = 0; j < kTilesPerWave; ++j) {
+  for (int j = 0; j < TPW; ++j) {
 #pragma unroll
     for (int d = 0; d < DT; ++d) acc[j][d] = floatx4_t{0.f, 0.f, 0.f, 0.f};
     m_row[j] = kNegInf;
     l_part[j] = 0.f;
   }
 
-  // ---- staging: chunk i = tid + k * kThreads -> key i / RC of the step, columns 8 (i % RC) .. +7 ----
+  // ---- staging: chunk i = tid + k * kThreads.  K: key i / RC, columns
+  // 8 (i % RC) .. +7 (a row's chunks on consecutive lanes: coalesced, and the
+  // rows land as 16-byte LDS writes).  V: key i % STEP, columns 8 (i / STEP)
+  // .. +7 (consecutive lanes on consecutive keys, so each 16-bit write of the
+  // transpose covers one contiguous run of V^T: few bank conflicts). ----
   const size_t kv_row_bytes = (size_t)a.Hkv * D * 2;
   const size_t block_bytes = (size_t)kBS * kv_row_bytes;
   const int nmax = a.N_blocks - 1;
   const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks;
   const unsigned char* kpool = static_cast<const unsigned char*>(a.k_pool) + (size_t)kv * D * 2;
   const unsigned char* vpool = static_cast<const unsigned char*>(a.v_pool) + (size_t)kv * D * 2;
+  // The table window holding step s: entries are loaded once per kTblWin
+  // blocks instead of once per step, so the K/V loads of a step depend on no
+  // global load of their own.
+  auto load_window = [&](int win) {
+    for (int e = tid; e < kTblWin; e += kThreads) {
+      const int blk = min(win * kTblWin + e, nblk - 1);
+      stbl[e] = clampi(trow[blk], 0, nmax);
+    }
+  };
+  // Per thread and staged chunk k: the block of the step it reads (relative
+  // to the step's first block) and its byte offset inside a physical block;
+  // only the physical id changes from step to step.
+  constexpr int NB = STEP / kBS;                      // blocks per step
+  int kblk[PER_T], vblk[PER_T];
+  uint32_t koff[PER_T], voff[PER_T];
+#pragma unroll
+  for (int k = 0; k < PER_T; ++k) {
+    const int i = tid + k * kThreads;
+    const int key = i / RC, vkey = i % STEP;
+    kblk[k] = key / kBS;
+    vblk[k] = vkey / kBS;
+    koff[k] = (uint32_t)((key % kBS) * kv_row_bytes + (i % RC) * 16);
+    voff[k] = (uint32_t)((vkey % kBS) * kv_row_bytes + (i / STEP) * 16);
+  }
   u32x4_t kreg[PER_T], vreg[PER_T];
   auto issue = [&](int s) {
+    const int b0 = s * NB;
 #pragma unroll
     for (int k = 0; k < PER_T; ++k) {
-      const int i = tid + k * kThreads;
-      const int pos = s * kStep + i / RC;
-      const int ph = clampi(trow[min(pos / kBS, nblk - 1)], 0, nmax);
-      const size_t off = (size_t)ph * block_bytes + (size_t)(pos % kBS) * kv_row_bytes + (i % RC) * 16;
-      kreg[k] = load16(kpool + off);
-      vreg[k] = load16(vpool + off);
+      const uint32_t kph = (uint32_t)stbl[(uint32_t)min(b0 + kblk[k], nblk - 1) % kTblWin];
+      const uint32_t vph = (uint32_t)stbl[(uint32_t)min(b0 + vblk[k], nblk - 1) % kTblWin];
+      kreg[k] = load16(kpool + (uint64_t)kph * block_bytes + koff[k]);
+      vreg[k] = load16(vpool + (uint64_t)vph * block_bytes + voff[k]);
     }
   };
   auto commit = [&](int s, int buf) {
+    const bool tail = (s + 1) * STEP > kv_len;   // the step holds keys past the group's last visible one
 #pragma unroll
     for (int k = 0; k < PER_T; ++k) {
       const int i = tid + k * kThreads;
-      const int key = i / RC, c = i % RC;
-      store16(kst(buf) + key * LD::KROW + c * 16, kreg[k]);
+      store16(kst(buf) + (i / RC) * PG::KROW + (i % RC) * 16, kreg[k]);
       // keys past the group's last visible one may hold anything: zero their V
-      const u32x4_t v = s * kStep + key < kv_len ? vreg[k] : u32x4_t{0u, 0u, 0u, 0u};
+      const int vkey = i % STEP, vc = i / STEP;
+      const u32x4_t v = !tail || s * STEP + vkey < kv_len ? vreg[k] : u32x4_t{0u, 0u, 0u, 0u};
       const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-      uint16_t* vt = reinterpret_cast<uint16_t*>(vst(buf) + (8 * c) * LD::VROW) + key;
+      uint16_t* vt = reinterpret_cast<uint16_t*>(vst(buf) + (8 * vc) * PG::VROW) + vkey;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) vt[e * (LD::VROW / 2)] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+      for (int e = 0; e < 8; ++e) vt[e * (PG::VROW / 2)] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
     }
   };
 
-  auto compute = [&](int s, int buf) {
+  // One step for this wave's tiles.  MASKED: some key of the step is at or
+  // past the causal limit of one of the wave's rows.
+  auto compute = [&](int s, int buf, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const unsigned char* ks = kst(buf);
     const unsigned char* vs = vst(buf);
-    // S^T for both 16-key halves of the step and both row tiles
-    floatx4_t sacc[kTilesPerWave][2];
+    floatx4_t sacc[TPW][NQ];
 #pragma unroll
-    for (int j = 0; j < kTilesPerWave; ++j)
+    for (int j = 0; j < TPW; ++j)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) sacc[j][h] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      for (int h = 0; h < NQ; ++h) sacc[j][h] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const unsigned char* kr = ks + (16 * h + row) * LD::KROW + quad * 16;
+    for (int h = 0; h < NQ; ++h) {
+      const unsigned char* kr = ks + (16 * h + row) * PG::KROW + quad * 16;
 #pragma unroll
       for (int c = 0; c < KS; ++c) {
         const bf16x8_v kv8 = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kr + c * 64));
 #pragma unroll
-        for (int j = 0; j < kTilesPerWave; ++j)
+        for (int j = 0; j < TPW; ++j)
           sacc[j][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv8, as_bf16x8(qreg[j][c]), sacc[j][h], 0, 0, 0);
       }
     }
-    // softmax; k-slot 8*quad + i of P holds key 4*quad + i (i < 4) or 16 + 4*quad + i - 4
-    bf16x8_v phi[kTilesPerWave], plo[kTilesPerWave];
+    // softmax.  Score i of the lane (i = 4 h + k) is key 16 h + 4 quad + k of
+    // the step; k-slot 8 quad + e of P chunk kk holds score 8 kk + e.
+    u32x4_t phi[TPW][NK], plo[TPW][NK];
 #pragma unroll
-    for (int j = 0; j < kTilesPerWave; ++j) {
-      float sv[8];
+    for (int j = 0; j < TPW; ++j) {
+      float sv[4 * NQ];
       bool need = false;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int key = s * kStep + 16 * (i >> 2) + 4 * quad + (i & 3);
-        sv[i] = key < hi_row[j] ? sacc[j][i >> 2][i & 3] * scale_log2e : kNegInf;
+      for (int i = 0; i < 4 * NQ; ++i) {
+        if constexpr (MASKED) {
+          const int key = s * STEP + 16 * (i >> 2) + 4 * quad + (i & 3);
+          sv[i] = key < hi_row[j] ? sacc[j][i >> 2][i & 3] * scale_log2e : kNegInf;
+        } else {
+          sv[i] = sacc[j][i >> 2][i & 3] * scale_log2e;
+        }
         need |= sv[i] > m_row[j] + kSlack;
       }
       if (__builtin_amdgcn_ballot_w64(need)) {
         float mx = sv[0];
 #pragma unroll
-        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+        for (int i = 1; i < 4 * NQ; ++i) mx = fmaxf(mx, sv[i]);
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(m_row[j], mx);
@@ -209,41 +269,63 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
           for (int d = 0; d < DT; ++d) acc[j][d][k] *= ak;
         }
       }
-      uint16_t hb[8], lb[8];
+      float pv[4 * NQ];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float p = sv[i] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(sv[i] - m_row[j]);
-        l_part[j] += p;
-        hb[i] = f32_to_bf16_rne(p);
-        lb[i] = f32_to_bf16_rne(p - __uint_as_float((uint32_t)hb[i] << 16));
+      for (int i = 0; i < 4 * NQ; ++i) {
+        // masked keys (and rows that have seen none) give p = 0
+        pv[i] = MASKED && sv[i] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(sv[i] - m_row[j]);
+        l_part[j] += pv[i];
       }
-      __builtin_memcpy(&phi[j], hb, 16);
-      __builtin_memcpy(&plo[j], lb, 16);
-    }
-    // O += P V: B operand = V^T[d][keys 4*quad .. +3 and 16 + 4*quad .. +3]
 #pragma unroll
-    for (int d = 0; d < DT; ++d) {
-      const unsigned char* vr = vs + (16 * d + row) * LD::VROW + quad * 8;
-      const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vr);
-      const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vr + 32);
-      const u32x4_t w = {lo.x, lo.y, hi.x, hi.y};
-      const bf16x8_v bv = as_bf16x8(w);
+      for (int kk = 0; kk < NK; ++kk) {
+        uint32_t h4[4], l4[4];
 #pragma unroll
-      for (int j = 0; j < kTilesPerWave; ++j) {
-        acc[j][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi[j], bv, acc[j][d], 0, 0, 0);
-        acc[j][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[j], bv, acc[j][d], 0, 0, 0);
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = pv[8 * kk + 2 * e], p1 = pv[8 * kk + 2 * e + 1];
+          const uint32_t h = cvt_pk_bf16(p0, p1);
+          h4[e] = h;
+          l4[e] = cvt_pk_bf16(p0 - __uint_as_float(h << 16), p1 - __uint_as_float(h & 0xffff0000u));
+        }
+        phi[j][kk] = u32x4_t{h4[0], h4[1], h4[2], h4[3]};
+        plo[j][kk] = u32x4_t{l4[0], l4[1], l4[2], l4[3]};
       }
     }
+    // O += P V: B operand = V^T[d][keys 32 kk + 4 quad .. +3 and 32 kk + 16 + 4 quad .. +3]
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+      for (int d = 0; d < DT; ++d) {
+        const unsigned char* vr = vs + (16 * d + row) * PG::VROW + 64 * kk + quad * 8;
+        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vr);
+        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vr + 32);
+        const bf16x8_v bv = as_bf16x8(u32x4_t{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+          acc[j][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(phi[j][kk]), bv, acc[j][d], 0, 0, 0);
+          acc[j][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(plo[j][kk]), bv, acc[j][d], 0, 0, 0);
+        }
+      }
   };
 
+  constexpr int kStepsPerWin = kTblWin * kBS / STEP;
   if (nsteps > 0) {
+    load_window(0);
+    __syncthreads();
     issue(0);
     commit(0, 0);
     __syncthreads();
     for (int s = 0; s < nsteps; ++s) {
       const int buf = s & 1;
+      if (s + 1 < nsteps && (s + 1) % kStepsPerWin == 0) {   // step s + 1 opens a new table window
+        __syncthreads();
+        load_window((s + 1) / kStepsPerWin);
+        __syncthreads();
+      }
       if (s + 1 < nsteps) issue(s + 1);
-      if (wave_active) compute(s, buf);
+      if (wave_active) {
+        if ((s + 1) * STEP > hi_min) compute(s, buf, std::true_type{});
+        else compute(s, buf, std::false_type{});
+      }
       if (s + 1 < nsteps) commit(s + 1, buf ^ 1);
       __syncthreads();
     }
@@ -253,12 +335,12 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
   if (!wave_active) return;
   uint16_t* out = static_cast<uint16_t*>(a.out);
 #pragma unroll
-  for (int j = 0; j < kTilesPerWave; ++j) {
+  for (int j = 0; j < TPW; ++j) {
     float l = l_part[j] + __shfl_xor(l_part[j], 16);
     l += __shfl_xor(l, 32);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int rr = r0 + 32 * wave + 16 * j + 4 * quad + k;   // O row held in acc[j][*][k]
+      const int rr = rw + 16 * j + 4 * quad + k;   // O row held in acc[j][*][k]
       const float lr = __shfl(l, 4 * quad + k);
       const float mr = __shfl(m_row[j], 4 * quad + k);
       if (rr < R) {
@@ -273,22 +355,35 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
   }
 }
 
+template <int D, int TPW, int STEP>
+hipError_t launch_pf(const PrefillArgs& pa0, hipStream_t stream) {
+  using PG = PGeo<D, TPW, STEP>;
+  PrefillArgs pa = pa0;
+  const int G = pa.a.Hq / pa.a.Hkv;
+  pa.groups = (pa.a.T * G + PG::ROWS - 1) / PG::ROWS;
+  const long long items = (long long)pa.groups * pa.a.B * pa.a.Hkv;
+  if (items <= 0) return hipSuccess;
+  if (items > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prefill_kernel<D, TPW, STEP>), dim3((unsigned)items), dim3(kThreads), 0, stream, pa,
+                     pa.a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+// One 16-row tile per wave and 32-key steps: measured fastest on the
+// chunked-prefill batch of the benchmark (three workgroups per CU); two tiles
+// per wave halve the LDS reads per flop but leave two workgroups per CU and
+// were slower, and so were 64-key steps.
+template <int D>
+hipError_t launch_pf_d(const PrefillArgs& pa, hipStream_t stream) {
+  return launch_pf<D, 1, 32>(pa, stream);
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const DecodeArgs& a, hipStream_t stream) {
   PrefillArgs pa{};
   pa.a = a;
-  const int G = a.Hq / a.Hkv;
-  pa.groups = (a.T * G + kRows - 1) / kRows;
-  const long long items = (long long)pa.groups * a.B * a.Hkv;
-  if (items <= 0) return hipSuccess;
-  if (items > 0x7fffffff) return hipErrorInvalidValue;
-  const float sl2 = a.scale * kLog2e;
-  if (a.D == 64)
-    hipLaunchKernelGGL(prefill_kernel<64>, dim3((unsigned)items), dim3(kThreads), 0, stream, pa, sl2);
-  else
-    hipLaunchKernelGGL(prefill_kernel<128>, dim3((unsigned)items), dim3(kThreads), 0, stream, pa, sl2);
-  return hipGetLastError();
+  return a.D == 64 ? launch_pf_d<64>(pa, stream) : launch_pf_d<128>(pa, stream);
 }
 
 }  // namespace pkv
