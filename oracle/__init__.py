@@ -19,3 +19,4 @@ from .attention import (  # noqa: F401
     softmax_attention_row,
     visible_tokens,
 )
+from .rope import kv_append_rope, rope_angles, rope_rotate, token_positions  # noqa: F401,E402

@@ -204,6 +204,60 @@ def pin_torch_sdpa_chunked_prefill():
         np.testing.assert_allclose(lse[b], ref_lse.permute(1, 0).numpy(), rtol=0, atol=1e-12)
 
 
+def pin_rope_hand_values():
+    """D = 4, theta = 10000: w = (1, 0.01).  A unit vector in dimension 0 at
+    position 1 turns into dimension 2 (its pair partner is i + D/2) by 1 rad;
+    one in dimension 1 turns into dimension 3 by 0.01 rad; position 0 is the
+    identity."""
+    y = oracle.rope_rotate(np.array([[1.0, 0.0, 0.0, 0.0], [0.0, 1.0, 0.0, 0.0]]), np.array(1), 10000.0)
+    np.testing.assert_allclose(y[0], [math.cos(1.0), 0.0, math.sin(1.0), 0.0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(y[1], [0.0, math.cos(0.01), 0.0, math.sin(0.01)], rtol=0, atol=1e-15)
+    x = np.random.default_rng(3).standard_normal((5, 3, 64))
+    np.testing.assert_array_equal(oracle.rope_rotate(x, np.zeros(5), 500000.0), x)
+
+
+def pin_rope_relative_position():
+    """<R(q, m), R(k, n)> depends only on m - n (shifting both positions keeps
+    every pair's dot product), each pair keeps its length, and R(R(x, a), b) =
+    R(x, a + b)."""
+    rng = np.random.default_rng(4)
+    D, theta = 128, 10000.0
+    q, k = rng.standard_normal((2, 7, 1, D))
+    m, n = rng.integers(0, 5000, size=(2, 7))
+    shift = 1234
+    d1 = np.sum(oracle.rope_rotate(q, m, theta) * oracle.rope_rotate(k, n, theta), axis=-1)
+    d2 = np.sum(oracle.rope_rotate(q, m + shift, theta) * oracle.rope_rotate(k, n + shift, theta), axis=-1)
+    np.testing.assert_allclose(d1, d2, rtol=1e-9, atol=1e-9)
+    y = oracle.rope_rotate(q, m, theta)
+    np.testing.assert_allclose(y[..., :D // 2] ** 2 + y[..., D // 2:] ** 2,
+                               q[..., :D // 2] ** 2 + q[..., D // 2:] ** 2, rtol=1e-12)
+    np.testing.assert_allclose(oracle.rope_rotate(oracle.rope_rotate(q, m, theta), n, theta),
+                               oracle.rope_rotate(q, m + n, theta), rtol=0, atol=1e-9)
+
+
+def pin_rope_append_positions():
+    """The fused append writes R(k_new[b, t], lens_pre[b] + t) into that
+    position's slot and v_new unchanged; every other slot keeps its bytes."""
+    rng = np.random.default_rng(5)
+    B, T, Hkv, D, bs, N = 3, 5, 2, 8, 4, 12
+    lens_pre = np.array([0, 3, 9])
+    tables = rng.permutation(N)[: B * 4].reshape(B, 4)
+    kp, vp = rng.standard_normal((2, N, bs, Hkv, D))
+    k_new, v_new = rng.standard_normal((2, B, T, Hkv, D))
+    k2, v2 = oracle.kv_append_rope(kp, vp, tables, lens_pre, k_new, v_new, bs, 10000.0)
+    touched = np.zeros((N, bs), dtype=bool)
+    for b in range(B):
+        for t in range(T):
+            pos = int(lens_pre[b]) + t
+            blk, slot = tables[b, pos // bs], pos % bs
+            touched[blk, slot] = True
+            np.testing.assert_allclose(k2[blk, slot], oracle.rope_rotate(k_new[b, t], np.array(pos), 10000.0),
+                                       rtol=0, atol=1e-15)
+            np.testing.assert_array_equal(v2[blk, slot], v_new[b, t])
+    np.testing.assert_array_equal(k2[~touched], kp[~touched])
+    np.testing.assert_array_equal(v2[~touched], vp[~touched])
+
+
 def pin_brute_force_fsum():
     """Tiny fp32 workload: every output recomputed with scalar loops and math.fsum."""
     w = workload.tiny_fp32()
@@ -367,7 +421,7 @@ def pin_bf16_rounding():
 ALL_PINS = [
     pin_golden_two_token, pin_golden_gqa_causal_verify, pin_golden_gqa_head_mapping, pin_golden_lse_merge,
     pin_gather_inverse_scatter, pin_append_then_gather, pin_torch_sdpa_decode, pin_torch_sdpa_causal_verify,
-    pin_torch_sdpa_chunked_prefill,
+    pin_torch_sdpa_chunked_prefill, pin_rope_hand_values, pin_rope_relative_position, pin_rope_append_positions,
     pin_brute_force_fsum, pin_closed_forms, pin_dominant_score, pin_key_shift_invariance,
     pin_physical_permutation, pin_gqa_equals_repeated_mha, pin_verify_equals_decode_chain,
     pin_split_equals_full, pin_lse_merge_algebra, pin_bf16_rounding,

@@ -10,6 +10,7 @@ import pytest
 
 import oracle
 import oracle.attention as oa
+import oracle.rope as orp
 import oracle_pins
 
 
@@ -61,10 +62,41 @@ MUTATIONS = {
 }
 
 
-@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def _rope_interleaved(x, positions, theta):
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    ang = orp.rope_angles(positions, D, theta)[..., None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = x[..., 0::2], x[..., 1::2]
+    y = np.empty_like(x)
+    y[..., 0::2], y[..., 1::2] = a * c - b * s, b * c + a * s
+    return y
+
+
+def _rope_wrong_sign(x, positions, theta):
+    return _orig_rope(x, -np.asarray(positions, dtype=np.float64), theta)
+
+
+def _rope_exponent_halved(positions, D, theta):
+    i = np.arange(D // 2, dtype=np.float64)
+    return np.asarray(positions, dtype=np.float64)[..., None] * np.power(np.float64(theta), -i / D)
+
+
+_orig_rope = orp.rope_rotate
+
+ROPE_MUTATIONS = {
+    "rope_interleaved_pairs": ("rope_rotate", _rope_interleaved),
+    "rope_wrong_sign": ("rope_rotate", _rope_wrong_sign),
+    "rope_exponent_halved": ("rope_angles", _rope_exponent_halved),
+    "rope_position_one_late": ("token_positions", lambda lens_pre, T: np.asarray(lens_pre)[:, None]
+                               + np.arange(T)[None, :] + 1),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS) + sorted(ROPE_MUTATIONS))
 def test_planted_mistake_is_caught(name, monkeypatch):
-    attr, fn = MUTATIONS[name]
-    monkeypatch.setattr(oa, attr, fn)
+    attr, fn = MUTATIONS[name] if name in MUTATIONS else ROPE_MUTATIONS[name]
+    monkeypatch.setattr(oa if name in MUTATIONS else orp, attr, fn)
     if hasattr(oracle, attr):
         monkeypatch.setattr(oracle, attr, fn)
     failed = []
