@@ -10,8 +10,9 @@ roofline of the decode call (algorithmic bytes / event-timed duration against
 the 8 TB/s HBM peak) and the CPU oracle timed on a bounded sample.
 
 The roofline figure is warm: consecutive calls on the same batch, as in a
-decode loop.  roofline.cold_cache repeats the call after a 1 GiB flush of the
-caches (outside the timed events) and reports its percentiles beside it.
+decode loop.  roofline.cold_cache repeats the call after reading a 1 GiB
+buffer (evicting the caches, outside the timed events) and reports its
+percentiles beside it.
 """
 from __future__ import annotations
 
@@ -146,6 +147,8 @@ def main():
     ap.add_argument("--partition", type=int, default=None, help="split-KV partition size (tokens); 0 = single pass")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rope-theta", type=float, default=None,
+                    help="append workloads: fused RoPE append (paged_kv_append_rope, queries rotated too)")
     ap.add_argument("--cold-reps", type=int, default=20,
                     help="extra untimed-region reps, each after a 1 GiB cache flush, for the cold-cache figure")
     ap.add_argument("--ceiling", action="store_true",
@@ -194,9 +197,18 @@ def main():
             pkv.paged_attention_decode(q, kp, vp, tables, lens, out=out, scale=scale, partition_size=part,
                                        workspace=ws, stream=stream)
 
+    aev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
     def step(i=None):
         if has_append:
-            pkv.paged_kv_append(k_new, v_new, kp, vp, tables, lens_pre, stream=stream)
+            if i is not None:
+                aev[i][0].record(stream)
+            if args.rope_theta is not None:
+                pkv.paged_kv_append_rope(k_new, v_new, kp, vp, tables, lens_pre, args.rope_theta, q=q, stream=stream)
+            else:
+                pkv.paged_kv_append(k_new, v_new, kp, vp, tables, lens_pre, stream=stream)
+            if i is not None:
+                aev[i][1].record(stream)
         if i is not None:
             ev[i][0].record(stream)
         attention()
@@ -216,15 +228,17 @@ def main():
 
     warm = np.array([a.elapsed_time(b) for a, b in ev])
 
-    # Cold cache: before each rep a 1 GiB buffer is read and written (more than
-    # the 256 MB last-level cache plus the L2s), outside the timed events.
+    # Cold cache: before each rep a 1 GiB buffer is read (more than the 256 MB
+    # last-level cache plus the L2s), outside the timed events.  Reading only
+    # leaves no dirty lines whose write-back would land in the timed call.
     cold = np.array([])
     if args.cold_reps > 0:
-        flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        sink = torch.empty((), dtype=torch.float32, device=dev)
         cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.cold_reps)]
         for a, b in cev:
-            flush.add_(1.0)
+            torch.amax(flush, dim=0, out=sink)
             a.record(stream)
             attention()
             b.record(stream)
@@ -262,6 +276,13 @@ def main():
             "launch_ms_p10_p50_p90": [round(float(np.percentile(warm, p)), 5) for p in (10, 50, 90)],
             "bytes_per_launch": nb["decode"], "hbm_GBps": round(achieved, 1)}
         result["tokens_per_s"] = round(w.B * w.T / (ms_step * 1e-3), 1)
+    if has_append:
+        app_ms = float(np.mean([a.elapsed_time(b) for a, b in aev]))
+        rope = args.rope_theta is not None
+        app_bytes = nb["append"] + (2 * w.B * w.T * w.Hq * w.D * w.elem_bytes if rope else 0)   # + q read and written
+        result["append"] = {"kernel": "paged_kv_append_rope" if rope else "paged_kv_append",
+                            "rope_theta": args.rope_theta, "launch_ms": round(app_ms, 5), "bytes_per_launch": app_bytes,
+                            "GBps": round(app_bytes / (app_ms * 1e-3) / 1e9, 1)}
     if cold.size:
         cold_med = float(np.median(cold))
         cc = {"reps": int(cold.size),

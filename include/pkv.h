@@ -104,6 +104,28 @@ pkv_status paged_kv_gather(const void* k_pool, const void* v_pool, const int32_t
                            pkv_dtype dtype, void* stream);
 
 /*
+ * paged_kv_append_rope -- paged_kv_append with rotary position embedding
+ * fused in ("LLM Inference from Scratch", Architecture overview: the decoder
+ * is Llama-style with RoPE; "warpllama", Milestones: fused RoPE kernel).
+ * New key t of sequence b is written to position p = context_lens_pre[b] + t
+ * (same slot rule as paged_kv_append) rotated by its position: for each KV
+ * head and i < D/2, with w_i = rope_theta^(-2i/D),
+ *   k'[i]       = k[i] cos(p w_i) - k[i + D/2] sin(p w_i)
+ *   k'[i + D/2] = k[i + D/2] cos(p w_i) + k[i] sin(p w_i)
+ * (Llama's pairing of dimension i with i + D/2).  The value row is written
+ * unchanged.  When q (the step's queries, [B, T, Hq, D], same dtype) is not
+ * NULL it is rotated in place at the same positions; Hq is ignored otherwise.
+ * Angles and rotations are computed in float64 and rounded once to the
+ * storage type (round to nearest even).  k_new and v_new are not modified;
+ * the target blocks must already be in the table.  rope_theta must be
+ * finite and > 0 (PKV_EINVAL otherwise).
+ */
+pkv_status paged_kv_append_rope(void* q, int Hq, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                                const int32_t* block_tables, const int32_t* context_lens_pre,
+                                int B, int T, int Hkv, int D, int block_size, int max_blocks, int N_blocks,
+                                float rope_theta, pkv_dtype dtype, void* stream);
+
+/*
  * pkv_decode_workspace_bytes -- bytes of device workspace paged_attention_decode
  * needs for these sizes and this partition size.  With partition_size > 0 the
  * split-KV partials use B*T*Hq*P_max*(D+1) float32 values, where

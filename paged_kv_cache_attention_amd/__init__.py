@@ -17,7 +17,7 @@ LIB_PATH = pathlib.Path(__file__).resolve().with_name("libpkv.so")
 PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP = range(5)
 PKV_FP32, PKV_BF16 = 0, 1
 STATUS_NAMES = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_EWORKSPACE", 4: "PKV_EHIP"}
-EXPORTS = ("paged_kv_append", "paged_kv_gather", "pkv_decode_workspace_bytes", "paged_attention_decode",
+EXPORTS = ("paged_kv_append", "paged_kv_append_rope", "paged_kv_gather", "pkv_decode_workspace_bytes", "paged_attention_decode",
            "paged_attention_prefill", "lse_reduce", "pkv_last_error")
 
 _lib = None
@@ -40,6 +40,8 @@ def load_library(path: pathlib.Path = LIB_PATH) -> ctypes.CDLL:
     P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.paged_kv_append.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, P]
     lib.paged_kv_append.restype = I
+    lib.paged_kv_append_rope.argtypes = [P, I, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P]
+    lib.paged_kv_append_rope.restype = I
     lib.paged_kv_gather.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, P]
     lib.paged_kv_gather.restype = I
     lib.pkv_decode_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
@@ -111,6 +113,20 @@ def paged_kv_append(k_new, v_new, k_pool, v_pool, block_tables, context_lens_pre
                                _i32(block_tables, "block_tables"), _i32(context_lens_pre, "context_lens_pre"),
                                B, T, Hkv, D, bs, block_tables.shape[1], N, _dtype_code(k_pool),
                                _stream(stream, k_pool.device)))
+
+
+def paged_kv_append_rope(k_new, v_new, k_pool, v_pool, block_tables, context_lens_pre, rope_theta, q=None,
+                         stream=None):
+    """paged_kv_append with k_new rotated by RoPE at its positions; q [B,T,Hq,D],
+    when given, is rotated in place at the same positions."""
+    lib = load_library()
+    B, T, Hkv, D = k_new.shape
+    N, bs = k_pool.shape[0], k_pool.shape[1]
+    Hq = q.shape[2] if q is not None else 0
+    _check(lib.paged_kv_append_rope(_ptr(q), Hq, _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
+                                    _i32(block_tables, "block_tables"), _i32(context_lens_pre, "context_lens_pre"),
+                                    B, T, Hkv, D, bs, block_tables.shape[1], N, float(rope_theta),
+                                    _dtype_code(k_pool), _stream(stream, k_pool.device)))
 
 
 def paged_kv_gather(k_pool, v_pool, block_tables, context_lens, k_out, v_out, stream=None):

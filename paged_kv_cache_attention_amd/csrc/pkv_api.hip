@@ -122,6 +122,30 @@ pkv_status paged_kv_append(const void* k_new, const void* v_new, void* k_pool, v
                   "paged_kv_append launch");
 }
 
+pkv_status paged_kv_append_rope(void* q, int Hq, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                                const int32_t* block_tables, const int32_t* context_lens_pre, int B, int T, int Hkv,
+                                int D, int block_size, int max_blocks, int N_blocks, float rope_theta, pkv_dtype dtype,
+                                void* stream) {
+  pkv_status st = check_dtype(dtype);
+  if (st != PKV_OK) return st;
+  if (B < 0 || T < 1) return fail(PKV_EINVAL, "B must be >= 0 and T >= 1");
+  if ((st = check_pool_shape(Hkv, D, block_size, max_blocks, N_blocks)) != PKV_OK) return st;
+  if (!std::isfinite(rope_theta) || rope_theta <= 0.f) return fail(PKV_EINVAL, "rope_theta must be finite and > 0");
+  if (q && (Hq < 1 || Hq % Hkv)) return fail(PKV_EINVAL, "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
+  if (B == 0) return PKV_OK;
+  if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !context_lens_pre)
+    return fail(PKV_EINVAL, "null pointer argument");
+  if ((long long)B * T > (1LL << 30)) return fail(PKV_EINVAL, "B*T too large");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug_enabled() &&
+      (st = debug_validate(block_tables, context_lens_pre, B, T, T, block_size, max_blocks, N_blocks, s)) != PKV_OK)
+    return st;
+  return from_hip(pkv::launch_append_rope(q, Hq, k_new, v_new, k_pool, v_pool, block_tables, context_lens_pre, B, T,
+                                          Hkv, D, block_size, max_blocks, N_blocks, (double)rope_theta,
+                                          dtype == PKV_BF16, s),
+                  "paged_kv_append_rope launch");
+}
+
 pkv_status paged_kv_gather(const void* k_pool, const void* v_pool, const int32_t* block_tables,
                            const int32_t* context_lens, void* k_out, void* v_out, int B, int max_len, int Hkv, int D,
                            int block_size, int max_blocks, int N_blocks, pkv_dtype dtype, void* stream) {

@@ -116,6 +116,19 @@ def test_prefill_empty_batch_is_a_noop():
     assert st == pkv.PKV_OK
 
 
+def test_append_rope_argument_errors():
+    lib = pkv.load_library()
+    f = lib.paged_kv_append_rope
+    ok = (P, 8, P, P, P, P, P, P, 2, 1, 2, 64, 16, 4, 8)
+    assert f(*ok, 0.0, pkv.PKV_BF16, None) == pkv.PKV_EINVAL            # theta must be > 0
+    assert f(*ok, float("nan"), pkv.PKV_BF16, None) == pkv.PKV_EINVAL
+    assert f(P, 5, *ok[2:], 10000.0, pkv.PKV_BF16, None) == pkv.PKV_EINVAL      # Hq not a multiple of Hkv
+    assert f(P, 8, P, None, *ok[4:], 10000.0, pkv.PKV_BF16, None) == pkv.PKV_EINVAL   # v_new missing
+    assert f(P, 8, P, P, P, P, P, P, 2, 1, 2, 96, 16, 4, 8, 10000.0, pkv.PKV_BF16, None) == pkv.PKV_EUNSUPPORTED
+    assert f(P, 8, P, P, P, P, P, P, 0, 1, 2, 64, 16, 4, 8, 10000.0, pkv.PKV_BF16, None) == pkv.PKV_OK   # B = 0
+    assert f(P, 8, P, P, P, P, P, P, 2, 1, 2, 64, 16, 4, 8, 10000.0, 5, None) == pkv.PKV_EINVAL        # dtype
+
+
 def test_append_gather_reduce_argument_errors():
     lib = pkv.load_library()
     assert lib.paged_kv_append(P, P, P, P, P, None, 2, 1, 8, 64, 16, 4, 8, pkv.PKV_BF16, None) == pkv.PKV_EINVAL
