@@ -126,6 +126,17 @@ pkv_status paged_kv_append_rope(void* q, int Hq, const void* k_new, const void* 
                                 float rope_theta, pkv_dtype dtype, void* stream);
 
 /*
+ * paged_kv_copy_blocks -- copy-on-write support ("vLLM and PagedAttention":
+ * memory sharing; a sequence that appends into a block other sequences also
+ * reference writes to its own copy): for i < n, block dst[i] of both pools
+ * becomes a byte copy of block src[i].  src and dst are device arrays of n
+ * block ids; pairs with an id outside [0, N_blocks) are skipped; no id may be
+ * both a source and a destination in one call.  n = 0 is a no-op.
+ */
+pkv_status paged_kv_copy_blocks(void* k_pool, void* v_pool, const int32_t* src, const int32_t* dst, int n,
+                                int Hkv, int D, int block_size, int N_blocks, pkv_dtype dtype, void* stream);
+
+/*
  * pkv_decode_workspace_bytes -- bytes of device workspace paged_attention_decode
  * needs for these sizes and this partition size.  With partition_size > 0 the
  * split-KV partials use B*T*Hq*P_max*(D+1) float32 values, where

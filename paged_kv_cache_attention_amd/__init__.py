@@ -17,10 +17,40 @@ LIB_PATH = pathlib.Path(__file__).resolve().with_name("libpkv.so")
 PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP = range(5)
 PKV_FP32, PKV_BF16 = 0, 1
 STATUS_NAMES = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_EWORKSPACE", 4: "PKV_EHIP"}
-EXPORTS = ("paged_kv_append", "paged_kv_append_rope", "paged_kv_gather", "pkv_decode_workspace_bytes", "paged_attention_decode",
-           "paged_attention_prefill", "lse_reduce", "pkv_last_error")
+EXPORTS = ("paged_kv_append", "paged_kv_append_rope", "paged_kv_copy_blocks", "paged_kv_gather",
+           "pkv_decode_workspace_bytes", "paged_attention_decode", "paged_attention_prefill", "lse_reduce",
+           "pkv_last_error",
+           "pkv_engine_create", "pkv_engine_destroy", "pkv_engine_last_error", "pkv_engine_add_request",
+           "pkv_engine_schedule", "pkv_engine_commit", "pkv_engine_get_stats", "pkv_engine_request_tokens",
+           "pkv_engine_block_ref")
 
 _lib = None
+
+
+class EngineConfig(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int), ("block_size", ctypes.c_int), ("max_blocks_per_seq", ctypes.c_int),
+                ("max_running", ctypes.c_int), ("max_prefill_tokens", ctypes.c_int),
+                ("enable_prefix_cache", ctypes.c_int), ("pad_block", ctypes.c_int)]
+
+
+_I32P = ctypes.POINTER(ctypes.c_int32)
+_I64P = ctypes.POINTER(ctypes.c_int64)
+
+
+class EnginePlan(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int), ("request_id", _I64P), ("kind", _I32P), ("start", _I32P), ("count", _I32P),
+                ("token_offset", _I32P), ("tokens", _I32P), ("block_tables", _I32P), ("context_lens", _I32P),
+                ("max_blocks_per_seq", ctypes.c_int), ("n_copies", ctypes.c_int), ("copy_src", _I32P),
+                ("copy_dst", _I32P), ("n_preempted", ctypes.c_int), ("preempted", _I64P)]
+
+
+class EngineStats(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_int64) for k in ("iterations", "preemptions", "cow_copies", "prefix_hit_tokens",
+                                              "computed_tokens", "finished")] + \
+               [(k, ctypes.c_int) for k in ("waiting", "running", "free_blocks", "cached_blocks", "cache_entries")]
+
+
+PKV_ENGINE_PREFILL, PKV_ENGINE_DECODE = 0, 1
 
 
 class PkvError(RuntimeError):
@@ -52,6 +82,27 @@ def load_library(path: pathlib.Path = LIB_PATH) -> ctypes.CDLL:
     lib.paged_attention_prefill.restype = I
     lib.lse_reduce.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
     lib.lse_reduce.restype = I
+    lib.paged_kv_copy_blocks.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
+    lib.paged_kv_copy_blocks.restype = I
+    E = ctypes.c_void_p
+    lib.pkv_engine_create.argtypes = [ctypes.POINTER(EngineConfig)]
+    lib.pkv_engine_create.restype = E
+    lib.pkv_engine_destroy.argtypes = [E]
+    lib.pkv_engine_destroy.restype = None
+    lib.pkv_engine_last_error.argtypes = [E]
+    lib.pkv_engine_last_error.restype = ctypes.c_char_p
+    lib.pkv_engine_add_request.argtypes = [E, ctypes.c_int64, P, I, I]
+    lib.pkv_engine_add_request.restype = I
+    lib.pkv_engine_schedule.argtypes = [E, ctypes.POINTER(EnginePlan)]
+    lib.pkv_engine_schedule.restype = I
+    lib.pkv_engine_commit.argtypes = [E, P]
+    lib.pkv_engine_commit.restype = I
+    lib.pkv_engine_get_stats.argtypes = [E, ctypes.POINTER(EngineStats)]
+    lib.pkv_engine_get_stats.restype = I
+    lib.pkv_engine_request_tokens.argtypes = [E, ctypes.c_int64, P, I]
+    lib.pkv_engine_request_tokens.restype = I
+    lib.pkv_engine_block_ref.argtypes = [E, I]
+    lib.pkv_engine_block_ref.restype = I
     lib.pkv_last_error.argtypes = []
     lib.pkv_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -183,6 +234,99 @@ def paged_attention_prefill(q, k_pool, v_pool, block_tables, context_lens, out=N
                                        _i32(context_lens, "context_lens"), _ptr(out), _ptr(lse_out), B, T, Hq, Hkv, D,
                                        bs, max_blocks, N, float(scale), _dtype_code(q), _stream(stream, q.device)))
     return out
+
+
+def paged_kv_copy_blocks(k_pool, v_pool, src, dst, stream=None):
+    """Copy block src[i] to dst[i] in both pools (src, dst: int32 device tensors)."""
+    lib = load_library()
+    N, bs, Hkv, D = k_pool.shape
+    n = int(src.numel())
+    _check(lib.paged_kv_copy_blocks(_ptr(k_pool), _ptr(v_pool), _i32(src, "src"), _i32(dst, "dst"), n, Hkv, D, bs, N,
+                                    _dtype_code(k_pool), _stream(stream, k_pool.device)))
+
+
+class Plan:
+    """One iteration planned by the engine, copied out of the library's arrays."""
+
+    def __init__(self, p: "EnginePlan"):
+        import numpy as np
+        n, mb = p.n, p.max_blocks_per_seq
+
+        def arr(ptr, count, dtype):
+            return np.ctypeslib.as_array(ptr, shape=(count,)).astype(dtype, copy=True) if count else np.zeros(0, dtype)
+        self.n = n
+        self.request_id = arr(p.request_id, n, np.int64)
+        self.kind = arr(p.kind, n, np.int32)
+        self.start = arr(p.start, n, np.int32)
+        self.count = arr(p.count, n, np.int32)
+        self.token_offset = arr(p.token_offset, n + 1, np.int32) if n else np.zeros(1, np.int32)
+        self.tokens = arr(p.tokens, int(self.token_offset[-1]), np.int32)
+        self.block_tables = arr(p.block_tables, n * mb, np.int32).reshape(n, mb)
+        self.context_lens = arr(p.context_lens, n, np.int32)
+        self.copy_src = arr(p.copy_src, p.n_copies, np.int32)
+        self.copy_dst = arr(p.copy_dst, p.n_copies, np.int32)
+        self.preempted = arr(p.preempted, p.n_preempted, np.int64)
+
+    def tokens_of(self, i):
+        return self.tokens[self.token_offset[i]:self.token_offset[i + 1]]
+
+
+class Engine:
+    """Block manager + continuous-batching scheduler of the library (host only)."""
+
+    def __init__(self, num_blocks, block_size, max_blocks_per_seq, max_running, max_prefill_tokens,
+                 prefix_cache=True, pad_block=0):
+        self._lib = load_library()
+        cfg = EngineConfig(num_blocks, block_size, max_blocks_per_seq, max_running, max_prefill_tokens,
+                           int(bool(prefix_cache)), pad_block)
+        self._h = self._lib.pkv_engine_create(ctypes.byref(cfg))
+        if not self._h:
+            raise PkvError(PKV_EINVAL, "invalid engine configuration")
+
+    def _ok(self, status):
+        if status != PKV_OK:
+            raise PkvError(status, self._lib.pkv_engine_last_error(self._h).decode())
+
+    def add_request(self, request_id, prompt, max_new_tokens):
+        import numpy as np
+        a = np.ascontiguousarray(prompt, dtype=np.int32)
+        self._ok(self._lib.pkv_engine_add_request(self._h, int(request_id),
+                                                  a.ctypes.data_as(ctypes.c_void_p), len(a), int(max_new_tokens)))
+
+    def schedule(self) -> Plan:
+        p = EnginePlan()
+        self._ok(self._lib.pkv_engine_schedule(self._h, ctypes.byref(p)))
+        return Plan(p)
+
+    def commit(self, next_tokens):
+        import numpy as np
+        a = np.ascontiguousarray(next_tokens, dtype=np.int32)
+        self._ok(self._lib.pkv_engine_commit(self._h, a.ctypes.data_as(ctypes.c_void_p)))
+
+    def stats(self) -> dict:
+        st = EngineStats()
+        self._ok(self._lib.pkv_engine_get_stats(self._h, ctypes.byref(st)))
+        return {k: getattr(st, k) for k, _ in EngineStats._fields_}
+
+    def request_tokens(self, request_id):
+        import numpy as np
+        n = self._lib.pkv_engine_request_tokens(self._h, int(request_id), None, 0)
+        if n < 0:
+            raise KeyError(request_id)
+        out = np.zeros(n, dtype=np.int32)
+        self._lib.pkv_engine_request_tokens(self._h, int(request_id), out.ctypes.data_as(ctypes.c_void_p), n)
+        return out
+
+    def block_ref(self, block):
+        return self._lib.pkv_engine_block_ref(self._h, int(block))
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.pkv_engine_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
 
 
 def lse_reduce(part_out, part_lse, out, lse_out=None, stream=None):

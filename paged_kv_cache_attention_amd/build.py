@@ -20,7 +20,7 @@ CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 LIB = PKG / "libpkv.so"
 PROBE_LIB = PKG / "libpkv_probe.so"      # diagnostic read-bandwidth probe, not part of the pkv ABI
-SOURCES = ["pkv_api.hip", "pkv_decode.hip", "pkv_stream.hip", "pkv_verify.hip", "pkv_prefill.hip", "pkv_prefix.hip", "pkv_reduce.hip", "pkv_copy.hip", "pkv_rope.hip"]
+SOURCES = ["pkv_api.hip", "pkv_decode.hip", "pkv_stream.hip", "pkv_verify.hip", "pkv_prefill.hip", "pkv_prefix.hip", "pkv_reduce.hip", "pkv_copy.hip", "pkv_rope.hip", "pkv_engine.cpp"]
 ARCH = "gfx950"
 
 

@@ -146,6 +146,19 @@ pkv_status paged_kv_append_rope(void* q, int Hq, const void* k_new, const void* 
                   "paged_kv_append_rope launch");
 }
 
+pkv_status paged_kv_copy_blocks(void* k_pool, void* v_pool, const int32_t* src, const int32_t* dst, int n, int Hkv,
+                                int D, int block_size, int N_blocks, pkv_dtype dtype, void* stream) {
+  pkv_status st = check_dtype(dtype);
+  if (st != PKV_OK) return st;
+  if (n < 0) return fail(PKV_EINVAL, "n must be >= 0");
+  if ((st = check_pool_shape(Hkv, D, block_size, 1, N_blocks)) != PKV_OK) return st;
+  if (n == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !src || !dst) return fail(PKV_EINVAL, "null pointer argument");
+  return from_hip(pkv::launch_copy_blocks(k_pool, v_pool, src, dst, n, Hkv, D, block_size, N_blocks, elem_bytes(dtype),
+                                          static_cast<hipStream_t>(stream)),
+                  "paged_kv_copy_blocks launch");
+}
+
 pkv_status paged_kv_gather(const void* k_pool, const void* v_pool, const int32_t* block_tables,
                            const int32_t* context_lens, void* k_out, void* v_out, int B, int max_len, int Hkv, int D,
                            int block_size, int max_blocks, int N_blocks, pkv_dtype dtype, void* stream) {

@@ -87,6 +87,31 @@ hipError_t launch_append(const void* k_new, const void* v_new, void* k_pool, voi
   return hipGetLastError();
 }
 
+// Copy-on-write support: block dst[i] of both pools becomes a copy of block
+// src[i]; pairs with an id outside [0, N_blocks) are skipped.  One workgroup
+// per pair and 16-byte moves.  Sources must not be destinations of the same
+// call (the engine never plans that).
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_pool, uint4* __restrict__ v_pool,
+                                                          const int32_t* __restrict__ src,
+                                                          const int32_t* __restrict__ dst, int block_chunks,
+                                                          int N_blocks) {
+  const int s = src[blockIdx.x], d = dst[blockIdx.x];
+  if (s < 0 || s >= N_blocks || d < 0 || d >= N_blocks) return;
+  const size_t so = (size_t)s * block_chunks, dof = (size_t)d * block_chunks;
+  for (int c = threadIdx.x; c < block_chunks; c += blockDim.x) {
+    k_pool[dof + c] = k_pool[so + c];
+    v_pool[dof + c] = v_pool[so + c];
+  }
+}
+
+hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* src, const int32_t* dst, int n, int Hkv,
+                              int D, int block_size, int N_blocks, int elem_bytes, hipStream_t stream) {
+  const int block_chunks = block_size * Hkv * D * elem_bytes / 16;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(n), dim3(256), 0, stream, static_cast<uint4*>(k_pool),
+                     static_cast<uint4*>(v_pool), src, dst, block_chunks, N_blocks);
+  return hipGetLastError();
+}
+
 hipError_t launch_gather(const void* k_pool, const void* v_pool, const int32_t* block_tables, const int32_t* lens,
                          void* k_out, void* v_out, int B, int max_len, int Hkv, int D, int block_size, int max_blocks,
                          int N_blocks, int elem_bytes, hipStream_t stream) {

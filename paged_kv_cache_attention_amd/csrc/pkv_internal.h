@@ -122,6 +122,8 @@ hipError_t launch_append(const void* k_new, const void* v_new, void* k_pool, voi
                          int block_size, int max_blocks, int N_blocks, int elem_bytes, hipStream_t stream);
 // KV append with RoPE fused in: rotates k_new (and q in place when given) at
 // position lens_pre[b] + t, writes the rotated key and the value row.
+hipError_t launch_copy_blocks(void* k_pool, void* v_pool, const int32_t* src, const int32_t* dst, int n, int Hkv,
+                              int D, int block_size, int N_blocks, int elem_bytes, hipStream_t stream);
 hipError_t launch_append_rope(void* q, int Hq, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
                               const int32_t* block_tables, const int32_t* lens_pre, int B, int T, int Hkv, int D,
                               int block_size, int max_blocks, int N_blocks, double theta, bool bf16,

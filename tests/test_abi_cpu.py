@@ -9,14 +9,17 @@ import pytest
 
 import paged_kv_cache_attention_amd as pkv
 
-HEADER = pathlib.Path(__file__).resolve().parent.parent / "include" / "pkv.h"
+INCLUDE = pathlib.Path(__file__).resolve().parent.parent / "include"
 P = ctypes.c_void_p(256)      # non-null dummy pointers, never dereferenced on these paths
 Q, K, V, TAB, LENS, OUT = (ctypes.c_void_p(4096 * (i + 1)) for i in range(6))
 
 
 def declared_functions():
-    text = HEADER.read_text()
-    return re.findall(r"^(?:pkv_status|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+    names = []
+    for h in sorted(INCLUDE.glob("*.h")):
+        names += re.findall(r"^(?:pkv_status|size_t|const char\*|pkv_engine\*|void|int)\s+(\w+)\s*\(", h.read_text(),
+                            flags=re.M)
+    return names
 
 
 def test_library_exports_every_declared_symbol():
