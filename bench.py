@@ -138,6 +138,59 @@ def copy_ceiling(torch, dev, nbytes=1 << 30, reps=20):
             "GBps_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
+def serve_bench(torch, dev, iters=200):
+    """The host runtime: (1) schedule + commit cost per iteration of the native
+    engine with 256 running requests (CPU only); (2) a 16-request serving run
+    on the device through PagedExecutor (continuous batching with preemption,
+    prefix cache, RoPE append, prefill and decode kernels), wall clock."""
+    import paged_kv_cache_attention_amd as pkv
+    from paged_kv_cache_attention_amd.serve import PagedExecutor
+    rng = np.random.default_rng(9)
+    eng = pkv.Engine(num_blocks=40000, block_size=16, max_blocks_per_seq=512, max_running=256,
+                     max_prefill_tokens=1 << 22, prefix_cache=True)
+    for r in range(256):
+        eng.add_request(r, rng.integers(0, 32000, size=int(rng.integers(16, 2048))), 2000)
+    plan = eng.schedule()
+    eng.commit(np.zeros(plan.n, np.int32))
+    toks = np.arange(256, dtype=np.int32)
+    t0 = time.perf_counter()
+    for _ in range(iters):
+        plan = eng.schedule()
+        eng.commit(toks[:plan.n])
+    host_us = (time.perf_counter() - t0) * 1e6 / iters
+    eng.close()
+
+    V, HQ, HKV, D = 997, 8, 2, 64
+    g = torch.Generator().manual_seed(1234)
+    emb = [torch.randn(V, h, D, generator=g).to(torch.bfloat16).to(dev) for h in (HQ, HKV, HKV)]
+    reqs = []
+    for r in range(16):
+        reqs.append((r, rng.integers(0, V, size=int(rng.integers(5, 150))), int(rng.integers(3, 30))))
+    worst = sum(-(-(len(p) + m) // 16) for _, p, m in reqs)
+    eng = pkv.Engine(worst // 3, 16, max_blocks_per_seq=16, max_running=8, max_prefill_tokens=256, prefix_cache=True)
+    for rid, p, m in reqs:
+        eng.add_request(rid, p, m)
+    kp = torch.zeros(worst // 3, 16, HKV, D, dtype=torch.bfloat16, device=dev)
+    vp = torch.zeros_like(kp)
+    ex = PagedExecutor(eng, kp, vp, HQ, 10000.0, lambda t: tuple(e[t.long()] for e in emb),
+                       lambda plan, outs: ((plan.request_id * 7 + plan.context_lens) % V).astype(np.int32))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while ex.step() is not None:
+        pass
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = eng.stats()
+    eng.close()
+    gen = sum(m for _, _, m in reqs)
+    return {"engine_host_us_per_iteration_256_running": round(host_us, 2),
+            "serve16": {"iterations": st["iterations"], "preemptions": st["preemptions"],
+                        "prefix_hit_tokens": st["prefix_hit_tokens"], "cow_copies": st["cow_copies"],
+                        "generated_tokens": gen, "wall_s": round(wall, 4),
+                        "generated_tokens_per_s": round(gen / wall, 1),
+                        "ms_per_iteration": round(wall * 1e3 / st["iterations"], 3)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,6 +202,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rope-theta", type=float, default=None,
                     help="append workloads: fused RoPE append (paged_kv_append_rope, queries rotated too)")
+    ap.add_argument("--serve", action="store_true",
+                    help="measure the host runtime (engine) and a 16-request serving run instead of one batch")
     ap.add_argument("--cold-reps", type=int, default=20,
                     help="extra untimed-region reps, each after a 1 GiB cache flush, for the cold-cache figure")
     ap.add_argument("--ceiling", action="store_true",
@@ -160,6 +215,12 @@ def main():
 
     import torch
     import paged_kv_cache_attention_amd as pkv
+
+    if args.serve:
+        res = {"mode": "serve", "n_gpus": 1, "data": "synthetic"}
+        res.update(serve_bench(torch, torch.device("cuda:0")))
+        print(json.dumps(res), flush=True)
+        return
 
     t_gen = time.time()
     w = workload.WORKLOADS[args.workload](poison=False)

@@ -60,16 +60,10 @@ uint64_t block_key(uint64_t parent, const int32_t* tok, int n) {
 
 constexpr uint64_t kRootKey = 0x243f6a8885a308d3ull;
 
-struct CacheEntry {
-  int block;
-  uint64_t parent;
-  std::vector<int32_t> tokens;   // the block's first tokens.size() tokens
-};
-
 class BlockManager {
  public:
   BlockManager(int num_blocks, int block_size, bool prefix_cache)
-      : bs_(block_size), cache_on_(prefix_cache), ref_(num_blocks, 0), keys_(num_blocks), in_lru_(num_blocks, false),
+      : bs_(block_size), cache_on_(prefix_cache), ref_(num_blocks, 0), info_(num_blocks), in_lru_(num_blocks, false),
         lru_it_(num_blocks) {
     for (int b = num_blocks - 1; b >= 0; --b) free_.push_back(b);
   }
@@ -80,6 +74,7 @@ class BlockManager {
   int free_count() const { return (int)free_.size(); }
   int cached_count() const { return (int)lru_.size(); }
   int ref(int b) const { return ref_[b]; }
+  int cache_entries() const { return indexed_; }
 
   // A new block for exclusive use (reference count 1); -1 when none is left.
   int allocate() {
@@ -91,7 +86,7 @@ class BlockManager {
       b = lru_.front();
       lru_.pop_front();
       in_lru_[b] = false;
-      drop_keys(b);
+      unindex(b);
     } else {
       return -1;
     }
@@ -109,51 +104,96 @@ class BlockManager {
 
   void release(int b) {
     if (--ref_[b] > 0) return;
-    if (cache_on_ && !keys_[b].empty()) {
+    if (cache_on_ && info_[b].indexed) {
       lru_it_[b] = lru_.insert(lru_.end(), b);
       in_lru_[b] = true;
     } else {
-      drop_keys(b);
+      unindex(b);
       free_.push_back(b);
     }
   }
 
-  // Cached block holding `n` tokens `tok` after the chain key `parent`, or -1.
+  // Cached block whose first n tokens are tok[0..n) after the chain key
+  // `parent`, or -1.  Full blocks are found by their chained key, partly
+  // used prefixes by (parent, first token) and a comparison of the contents.
   int lookup(uint64_t parent, const int32_t* tok, int n) const {
-    if (!cache_on_) return -1;
-    auto it = cache_.find(block_key(parent, tok, n));
-    if (it == cache_.end()) return -1;
-    const CacheEntry& e = it->second;
-    if (e.parent != parent || (int)e.tokens.size() != n || !std::equal(tok, tok + n, e.tokens.begin())) return -1;
-    return e.block;
+    if (!cache_on_ || n < 1) return -1;
+    if (n == bs_) {
+      auto it = full_.find(block_key(parent, tok, n));
+      if (it == full_.end()) return -1;
+      const Info& f = info_[it->second];
+      return f.parent == parent && (int)f.content.size() == bs_ && std::equal(tok, tok + n, f.content.begin())
+                 ? it->second : -1;
+    }
+    auto range = part_.equal_range(head_key(parent, tok[0]));
+    for (auto it = range.first; it != range.second; ++it) {
+      const Info& f = info_[it->second];
+      if (f.parent == parent && (int)f.content.size() >= n && std::equal(tok, tok + n, f.content.begin()))
+        return it->second;
+    }
+    return -1;
   }
 
-  // Block b now holds tokens tok[0..n) after `parent`: make it findable.
-  void register_key(int b, uint64_t parent, const int32_t* tok, int n) {
-    if (!cache_on_ || n == 0) return;
-    const uint64_t k = block_key(parent, tok, n);
-    if (cache_.count(k)) return;   // first block with this content stays the cached one
-    cache_.emplace(k, CacheEntry{b, parent, std::vector<int32_t>(tok, tok + n)});
-    keys_[b].push_back(k);
+  // Block b now holds tokens tok[0..n) after `parent` (n grows as the owner
+  // appends; the first tokens never change while the block is allocated or
+  // cached).
+  void record(int b, uint64_t parent, const int32_t* tok, int n) {
+    if (!cache_on_ || n < 1) return;
+    Info& f = info_[b];
+    if (!f.indexed) {
+      f.parent = parent;
+      f.content.clear();
+      f.content.reserve(bs_);
+      f.head = head_key(parent, tok[0]);
+      part_.emplace(f.head, b);
+      f.indexed = true;
+      ++indexed_;
+    }
+    f.content.assign(tok, tok + n);
+    if (n == bs_ && !f.full) {
+      const uint64_t k = block_key(parent, tok, n);
+      if (!full_.count(k)) {   // the first block with this content stays the cached one
+        full_.emplace(k, b);
+        f.full = true;
+        f.full_key = k;
+      }
+    }
   }
-
-  int cache_entries() const { return (int)cache_.size(); }
 
  private:
-  void drop_keys(int b) {
-    for (uint64_t k : keys_[b]) cache_.erase(k);
-    keys_[b].clear();
+  struct Info {
+    bool indexed = false, full = false;
+    uint64_t parent = 0, head = 0, full_key = 0;
+    std::vector<int32_t> content;   // tokens in the block, in slot order
+  };
+
+  static uint64_t head_key(uint64_t parent, int32_t first) { return mix64(parent ^ ((uint64_t)(uint32_t)first << 1)); }
+
+  void unindex(int b) {
+    Info& f = info_[b];
+    if (!f.indexed) return;
+    auto range = part_.equal_range(f.head);
+    for (auto it = range.first; it != range.second; ++it)
+      if (it->second == b) {
+        part_.erase(it);
+        break;
+      }
+    if (f.full) full_.erase(f.full_key);
+    f = Info{};
+    --indexed_;
   }
 
   int bs_;
   bool cache_on_;
   std::vector<int> ref_;
-  std::vector<std::vector<uint64_t>> keys_;
+  std::vector<Info> info_;
   std::vector<int> free_;
   std::list<int> lru_;
   std::vector<bool> in_lru_;
   std::vector<std::list<int>::iterator> lru_it_;
-  std::unordered_map<uint64_t, CacheEntry> cache_;
+  std::unordered_map<uint64_t, int> full_;        // chained key of a full block -> block
+  std::unordered_multimap<uint64_t, int> part_;   // (parent, first token) -> blocks
+  int indexed_ = 0;
 };
 
 enum class State { kWaiting, kRunning, kFinished };
@@ -203,17 +243,16 @@ struct pkv_engine {
     r.computed = 0;
   }
 
-  // Keys for the blocks that tokens [from_token, computed) were written to:
-  // one per fill level reached, so a later prompt that ends anywhere inside
-  // the block can find it.
+  // Record the contents of the blocks that tokens [from_token, computed)
+  // were written to, so later prompts can find them (a prompt ending
+  // anywhere inside a block matches its first tokens).
   void register_blocks(Request& r, int from_token) {
     const int bs = bm.block_size();
     const int last = r.computed;   // tokens [0, last) are in the cache
     for (int j = from_token / bs; j * bs < last; ++j) {
       const int n = std::min(bs, last - j * bs);
       const uint64_t parent = parent_key(r, j);
-      for (int m = std::max(1, from_token - j * bs + 1); m <= n; ++m)
-        bm.register_key(r.table[j], parent, r.tokens.data() + j * bs, m);
+      bm.record(r.table[j], parent, r.tokens.data() + j * bs, n);
       if (n == bs && (int)r.chain.size() == j) r.chain.push_back(block_key(parent, r.tokens.data() + j * bs, bs));
     }
   }
