@@ -61,6 +61,31 @@ def algorithmic_bytes(w):
                 kv_unique=kv_unique, kv_logical=kv_logical)
 
 
+# Decode-kernel sources whose hash guards the committed traffic figures.
+TRAFFIC_SOURCES = ("pkv_stream.hip", "pkv_device.h", "pkv_internal.h", "pkv_group.h")
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary (FETCH_SIZE + WRITE_SIZE, calibrated), or None when there
+    is none for this workload or the kernel sources changed since."""
+    import hashlib
+    import re
+    prof = os.path.join(ROOT, "profiles", f"paged_decode_{workload_name}.md")
+    if not os.path.exists(prof):
+        return None
+    m = re.search(r"traffic-bytes: fetch=(\d+) write=(\d+) source-sha256=([0-9a-f]+)", open(prof).read())
+    if not m:
+        return None
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != m.group(3):
+        return None
+    return int(m.group(1)) + int(m.group(2))
+
+
 def attention_flops(w):
     """Useful flops of the attention: 4*D per (query row, visible key) pair
     (2*D for q.k, 2*D for p*v); masked pairs are not counted."""
@@ -163,9 +188,15 @@ def serve_bench(torch, dev, iters=200):
     V, HQ, HKV, D = 997, 8, 2, 64
     g = torch.Generator().manual_seed(1234)
     emb = [torch.randn(V, h, D, generator=g).to(torch.bfloat16).to(dev) for h in (HQ, HKV, HKV)]
+    common = rng.integers(0, V, size=37)   # one shared prompt ending inside a block
     reqs = []
     for r in range(16):
-        reqs.append((r, rng.integers(0, V, size=int(rng.integers(5, 150))), int(rng.integers(3, 30))))
+        p = rng.integers(0, V, size=int(rng.integers(5, 150)))
+        if r in (0, 5, 9, 13):
+            p = common.copy()
+        if r in (2, 7):
+            p = np.concatenate([common, p[: len(p) // 3]])
+        reqs.append((r, p, 40 if r == 0 else int(rng.integers(3, 30))))
     worst = sum(-(-(len(p) + m) // 16) for _, p, m in reqs)
     eng = pkv.Engine(worst // 3, 16, max_blocks_per_seq=16, max_running=8, max_prefill_tokens=256, prefix_cache=True)
     for rid, p, m in reqs:
@@ -318,7 +349,8 @@ def main():
                    "block_size": w.block_size, "partition_size": part, "total_tokens": int(w.context_lens.sum()),
                    "append": has_append},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(w.name) if part == 0 else None,
                      "kernel": ("paged_attention_decode call (plan + balanced decode + boundary merge)" if part == 0
                                 else "paged_attention_decode call (partition kernel + lse merge)"),
                      "bytes_per_launch": nb["decode"], "launch_ms": round(decode_ms, 5),
