@@ -26,7 +26,8 @@
 //     requests are preempted (blocks released, request back to the head of
 //     the queue; it is recomputed from its known tokens on re-admission);
 //   * waiting requests are then admitted in arrival order while blocks, the
-//     running-request limit and the per-iteration prefill-token budget allow;
+//     running-request limit and the per-iteration prefill-token budget allow
+//     (a request preempted in this iteration waits for the next one);
 //     an admitted request prefills every token not served by the prefix cache
 //     (at least its last token, whose output samples the next token).
 #include <algorithm>
@@ -372,11 +373,14 @@ struct pkv_engine {
       prepare_slot(*r, true);
       emit(*r, PKV_ENGINE_DECODE, r->computed, 1);
     }
-    // 2. admissions in arrival order
+    // 2. admissions in arrival order; a request preempted by this plan waits
+    //    for the next iteration (re-admitting it now would recompute it to
+    //    stand where it was)
     int budget = cfg.max_prefill_tokens;
     bool first = true;
     while (!waiting.empty() && (int)running.size() < cfg.max_running) {
       Request* r = waiting.front();
+      if (std::find(p_preempted.begin(), p_preempted.end(), r->id) != p_preempted.end()) break;
       if (!try_admit(*r, budget, first)) break;
       waiting.pop_front();
       r->state = State::kRunning;

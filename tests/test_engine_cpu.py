@@ -64,7 +64,7 @@ def make_requests(seed, n=16, shared=0, shared_len=40):
 
 
 def run(reqs, num_blocks, bs=16, prefix_cache=True, max_running=8, max_prefill=256, check_each_step=None):
-    eng = pkv.Engine(num_blocks, bs, max_blocks_per_seq=256 // bs * 2, max_running=max_running,
+    eng = pkv.Engine(num_blocks, bs, max_blocks_per_seq=512 // bs, max_running=max_running,
                      max_prefill_tokens=max_prefill, prefix_cache=prefix_cache)
     dev = FakeDevice(num_blocks, bs)
     for rid, p, m in reqs:
@@ -172,3 +172,32 @@ def test_engine_errors():
     tiny.close()
     with pytest.raises(pkv.PkvError):
         pkv.Engine(0, 16, 4, 1, 1)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_randomised_workloads_keep_every_invariant(seed):
+    """Random request mixes, block sizes, pool sizes, limits and cache
+    settings: every cache read matches its history, streams equal the solo
+    streams, and all blocks come back."""
+    rng = np.random.default_rng(1000 + seed)
+    bs = int(rng.choice([4, 8, 16]))
+    n = int(rng.integers(4, 24))
+    common = rng.integers(0, 997, size=int(rng.integers(1, 60)))
+    reqs = []
+    for r in range(n):
+        if rng.random() < 0.4:   # share a prefix of the common prompt, possibly all of it
+            p = np.concatenate([common[: int(rng.integers(1, len(common) + 1))],
+                                rng.integers(0, 997, size=int(rng.integers(0, 30)))])
+        else:
+            p = rng.integers(0, 997, size=int(rng.integers(1, 100)))
+        reqs.append((r, p.astype(np.int32), int(rng.integers(1, 25))))
+    need_max = max(-(-(len(p) + m) // bs) for _, p, m in reqs)
+    worst = sum(-(-(len(p) + m) // bs) for _, p, m in reqs)
+    pool = int(rng.integers(need_max + 1, max(need_max + 2, worst + 1)))
+    st, streams, refs = run(reqs, num_blocks=pool, bs=bs, prefix_cache=bool(rng.random() < 0.7),
+                            max_running=int(rng.integers(1, 9)), max_prefill=int(rng.integers(8, 300)))
+    assert st["finished"] == n
+    for rid, p, m in reqs:
+        assert np.array_equal(streams[rid], expected_stream(rid, p, m))
+    assert all(r == 0 for r in refs)
+    assert st["free_blocks"] + st["cached_blocks"] == pool

@@ -116,3 +116,23 @@ def test_llama8b_chunked_prefill_full():
                                               w.context_lens[b:b + 1], w.scale, w.block_size)
         check_attention(out[b:b + 1], ref, "bf16", f"8B prefill seq {b}", floor=mfma_floor(w))
         check_lse(lse[b:b + 1], ref_lse, f"8B prefill seq {b}")
+
+
+def test_prefill_long_chunk_many_row_groups():
+    """A 2048-token chunk after a 3000-token prefix and one with no prefix:
+    64 row groups per KV head, key ranges up to 5048 (several LDS table
+    windows of 512 blocks are not needed here, one window covers 8192 keys)."""
+    w = workload.uniform_batch("long-chunk", seed=121, B=2, T=2048, Hq=8, Hkv=2, D=64, dtype="bf16",
+                               lens=[2048 + 3000, 2048])
+    say("prefill long chunk")
+    out, lse = prefill(w, upload(w))
+    check_vs_oracle(w, out, lse, "prefill T=2048")
+
+
+def test_prefill_key_range_beyond_one_table_window():
+    """Keys past 512 blocks (8192 tokens) make the tile reload its LDS table
+    window mid-item."""
+    w = workload.uniform_batch("window", seed=131, B=1, T=64, Hq=8, Hkv=8, D=64, dtype="bf16", lens=[8192 + 700])
+    say("prefill table window")
+    out, lse = prefill(w, upload(w))
+    check_vs_oracle(w, out, lse, "prefill beyond a table window")
