@@ -80,10 +80,10 @@ struct PrefillArgs {
 };
 
 // Waves per SIMD the register budget is sized for: one tile per wave with
-// 32-key steps fits four at D = 64 and three at D = 128 (that many
-// workgroups per CU, 18 or 36 KB of LDS each); the other shapes two.
+// 32-key steps fits four (that many workgroups per CU, 20 or 39 KB of LDS
+// each); the other shapes two.
 template <int D, int TPW, int STEP>
-constexpr int prefill_waves_per_eu() { return TPW == 1 && STEP == 32 ? (D == 64 ? 4 : 3) : 2; }
+constexpr int prefill_waves_per_eu() { return TPW == 1 && STEP == 32 ? 4 : 2; }
 
 template <int D, int TPW, int STEP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefill_waves_per_eu<D, TPW, STEP>())))
@@ -141,12 +141,13 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
   }
 
   floatx4_t acc[TPW][DT];
-  float m_row[TPW], l_part[TPW];
+  float m_row[TPW], m_thr[TPW], l_part[TPW];   // m_thr = m_row + kSlack: a larger score rescales
 #pragma unroll
   for (int j = 0; j < TPW; ++j) {
 #pragma unroll
     for (int d = 0; d < DT; ++d) acc[j][d] = floatx4_t{0.f, 0.f, 0.f, 0.f};
     m_row[j] = kNegInf;
+    m_thr[j] = kNegInf;
     l_part[j] = 0.f;
   }
 
@@ -197,14 +198,17 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
     }
   };
   auto commit = [&](int s, int buf) {
-    const bool tail = (s + 1) * STEP > kv_len;   // the step holds keys past the group's last visible one
+    if ((s + 1) * STEP > kv_len) {   // the step holds keys past the group's last visible one:
+#pragma unroll                      // they may hold anything, so zero their V
+      for (int k = 0; k < PER_T; ++k)
+        if (s * STEP + (tid + k * kThreads) % STEP >= kv_len) vreg[k] = u32x4_t{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
     for (int k = 0; k < PER_T; ++k) {
       const int i = tid + k * kThreads;
       store16(kst(buf) + (i / RC) * PG::KROW + (i % RC) * 16, kreg[k]);
-      // keys past the group's last visible one may hold anything: zero their V
       const int vkey = i % STEP, vc = i / STEP;
-      const u32x4_t v = !tail || s * STEP + vkey < kv_len ? vreg[k] : u32x4_t{0u, 0u, 0u, 0u};
+      const u32x4_t v = vreg[k];
       const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
       uint16_t* vt = reinterpret_cast<uint16_t*>(vst(buf) + (8 * vc) * PG::VROW) + vkey;
 #pragma unroll
@@ -235,33 +239,35 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
       }
     }
     // softmax.  Score i of the lane (i = 4 h + k) is key 16 h + 4 quad + k of
-    // the step; k-slot 8 quad + e of P chunk kk holds score 8 kk + e.
+    // the step; k-slot 8 quad + e of P chunk kk holds score 8 kk + e.  The
+    // running max m is kept in scaled base-2 units; since the scale is
+    // positive, max(score) * scale is the max of the scaled scores, and each
+    // p is exp2(score * scale - m) with one rounding (an fma).
     u32x4_t phi[TPW][NK], plo[TPW][NK];
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
-      float sv[4 * NQ];
-      bool need = false;
+      float sv[4 * NQ];   // raw scores, masked ones -inf
 #pragma unroll
       for (int i = 0; i < 4 * NQ; ++i) {
         if constexpr (MASKED) {
           const int key = s * STEP + 16 * (i >> 2) + 4 * quad + (i & 3);
-          sv[i] = key < hi_row[j] ? sacc[j][i >> 2][i & 3] * scale_log2e : kNegInf;
+          sv[i] = key < hi_row[j] ? sacc[j][i >> 2][i & 3] : kNegInf;
         } else {
-          sv[i] = sacc[j][i >> 2][i & 3] * scale_log2e;
+          sv[i] = sacc[j][i >> 2][i & 3];
         }
-        need |= sv[i] > m_row[j] + kSlack;
       }
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        float mx = sv[0];
+      float mx = sv[0];
 #pragma unroll
-        for (int i = 1; i < 4 * NQ; ++i) mx = fmaxf(mx, sv[i]);
+      for (int i = 1; i < 4 * NQ; ++i) mx = fmaxf(mx, sv[i]);
+      if (__builtin_amdgcn_ballot_w64(mx * scale_log2e > m_thr[j])) {
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_row[j], mx);
+        const float m_new = fmaxf(m_row[j], mx * scale_log2e);
         // 1 while a row is still empty (both -inf), 0 on its first key
         const float alpha = m_row[j] == m_new ? 1.f : __builtin_amdgcn_exp2f(m_row[j] - m_new);
         l_part[j] *= alpha;
         m_row[j] = m_new;
+        m_thr[j] = m_new + kSlack;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const float ak = __shfl(alpha, 4 * quad + k);
@@ -269,11 +275,13 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
           for (int d = 0; d < DT; ++d) acc[j][d][k] *= ak;
         }
       }
+      const float neg_m = -m_row[j];
       float pv[4 * NQ];
 #pragma unroll
       for (int i = 0; i < 4 * NQ; ++i) {
-        // masked keys (and rows that have seen none) give p = 0
-        pv[i] = MASKED && sv[i] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(sv[i] - m_row[j]);
+        // masked keys (and rows that have seen none) give p = 0; in unmasked
+        // steps every row has seen a key, so m is finite
+        pv[i] = MASKED && sv[i] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], scale_log2e, neg_m));
         l_part[j] += pv[i];
       }
 #pragma unroll
@@ -314,7 +322,7 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
     issue(0);
     commit(0, 0);
     __syncthreads();
-    for (int s = 0; s < nsteps; ++s) {
+    auto step = [&](int s, auto masked_tag) {
       const int buf = s & 1;
       if (s + 1 < nsteps && (s + 1) % kStepsPerWin == 0) {   // step s + 1 opens a new table window
         __syncthreads();
@@ -322,13 +330,17 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
         __syncthreads();
       }
       if (s + 1 < nsteps) issue(s + 1);
-      if (wave_active) {
-        if ((s + 1) * STEP > hi_min) compute(s, buf, std::true_type{});
-        else compute(s, buf, std::false_type{});
-      }
+      if (wave_active) compute(s, buf, masked_tag);
       if (s + 1 < nsteps) commit(s + 1, buf ^ 1);
       __syncthreads();
-    }
+    };
+    // Steps before s_mask hold only keys every row of the wave sees; the
+    // rest are masked.  Two loops, one per kind, so each keeps its registers
+    // in place (the barrier count per step is the same for every wave).
+    const int s_mask = wave_active ? min(nsteps, hi_min / STEP) : nsteps;
+    int s = 0;
+    for (; s < s_mask; ++s) step(s, std::false_type{});
+    for (; s < nsteps; ++s) step(s, std::true_type{});
   }
 
   // ---- epilogue: O / l in bf16, lse in natural log ----
