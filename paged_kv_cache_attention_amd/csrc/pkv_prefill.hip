@@ -79,6 +79,92 @@ struct PrefillArgs {
   int groups;   // row groups per (sequence, KV head)
 };
 
+// Start order of the work items.  The workgroup of rank p = blockIdx / Hkv
+// takes the item (b, rg) with the p-th largest key count
+//   work(b, rg) = L_b - T + min(T, (rg + 1) * tpg)    (tpg = chunk tokens per row group)
+// (ties: smaller b first), so the longest items start first and never run
+// alone at the end of the grid.  work is strictly increasing in rg, so the
+// number of items of sequence b with work >= w has a closed form, and the
+// item of rank p follows from a binary search on w: a bijection from ranks to
+// items for any lengths.  Wave 0 computes it with the lengths in registers
+// (kOrderMaxB sequences at most; larger batches keep the plain order).
+constexpr int kOrderMaxB = 512;
+
+__device__ __forceinline__ int count_work_ge(int Lc, int w, int T, int tpg, int groups) {
+  const int x = w - Lc + T;   // rg counts iff min(T, (rg + 1) tpg) >= x
+  if (x > T) return 0;
+  if (x <= tpg) return groups;
+  return groups + 1 - (x + tpg - 1) / tpg;
+}
+
+__device__ __forceinline__ int wave_sum_int(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Wave 0 only: the item of rank p, written to item[0] (b) and item[1] (rg).
+__device__ void item_of_rank(const int32_t* lens, int B, int T, int max_tokens, int tpg, int groups, int p,
+                             int lane, int* item) {
+  constexpr int KB = kOrderMaxB / 64;
+  const int nk = (B + 63) / 64;
+  int lc[KB];
+  int lo = max_tokens, hi = 0;
+#pragma unroll
+  for (int k = 0; k < KB; ++k) {
+    lc[k] = 0;
+    if (k < nk) {
+      const int bb = lane + 64 * k;
+      if (bb < B) {
+        lc[k] = clampi(lens[bb], 0, max_tokens);
+        lo = min(lo, lc[k]);
+        hi = max(hi, lc[k]);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = min(lo, __shfl_xor(lo, o));
+    hi = max(hi, __shfl_xor(hi, o));
+  }
+  auto total_ge = [&](int w) {
+    int c = 0;
+#pragma unroll
+    for (int k = 0; k < KB; ++k)
+      if (k < nk && lane + 64 * k < B) c += count_work_ge(lc[k], w, T, tpg, groups);
+    return wave_sum_int(c);
+  };
+  // total_ge(lo) = B * groups > p >= total_ge(hi) = 0
+  lo -= T;
+  hi += 1;
+  while (hi - lo > 1) {
+    const int mid = lo + (hi - lo) / 2;
+    if (total_ge(mid) > p) lo = mid;
+    else hi = mid;
+  }
+  // the item has work lo; o = its rank among the items of that work, which
+  // are one per sequence at most, taken in order of b
+  int o = p - total_ge(hi);
+#pragma unroll
+  for (int k = 0; k < KB; ++k) {
+    if (k >= nk) break;
+    const int bb = lane + 64 * k;
+    const int ge = bb < B ? count_work_ge(lc[k], lo, T, tpg, groups) : 0;
+    const bool has = bb < B && ge > count_work_ge(lc[k], hi, T, tpg, groups);
+    const uint64_t m = __builtin_amdgcn_ballot_w64(has);
+    const int n = __builtin_popcountll(m);
+    if (o < n) {
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+      if (has && below == o) {
+        item[0] = bb;
+        item[1] = groups - ge;
+      }
+      break;
+    }
+    o -= n;
+  }
+}
+
 // Waves per SIMD the register budget is sized for: one tile per wave with
 // 32-key steps fits four (that many workgroups per CU, 20 or 39 KB of LDS
 // each); the other shapes two.
@@ -102,12 +188,26 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = a.Hq / a.Hkv;
   const int R = a.T * G;
-  // row groups with the most keys first: the last group of every (b, kv)
-  const int per_g = a.B * a.Hkv;
-  const int rg = pa.groups - 1 - (int)blockIdx.x / per_g;
-  const int rem = (int)blockIdx.x % per_g;
-  const int b = rem / a.Hkv, kv = rem - (rem / a.Hkv) * a.Hkv;
+  // items longest first (item_of_rank); the KV heads of one item are
+  // consecutive workgroups
   const int max_tokens = a.max_blocks * kBS;
+  const int kv = (int)blockIdx.x % a.Hkv;
+  const int p = (int)blockIdx.x / a.Hkv;
+  int b, rg;
+  if (a.B == 1) {
+    b = 0;
+    rg = pa.groups - 1 - p;
+  } else if (a.B > kOrderMaxB) {   // plain order: the last row group of every sequence first
+    b = p % a.B;
+    rg = pa.groups - 1 - p / a.B;
+  } else {
+    __shared__ int sitem[2];
+    if (tid < 64)
+      item_of_rank(a.context_lens, a.B, a.T, max_tokens, PG::ROWS / G, pa.groups, p, tid, sitem);
+    __syncthreads();
+    b = sitem[0];
+    rg = sitem[1];
+  }
   const int L = clampi(a.context_lens[b], 0, max_tokens);
   const int r0 = rg * PG::ROWS;
   const int t_last = (min(R, r0 + PG::ROWS) - 1) / G;

@@ -60,6 +60,21 @@ def test_prefill_shapes(D, Hq, Hkv, T, lens):
     check_vs_oracle(w, out, lse, f"prefill D={D} Hq={Hq} Hkv={Hkv} T={T}")
 
 
+@pytest.mark.parametrize("B,T,lmax", [(70, 40, 400), (520, 2, 60)])
+def test_prefill_many_sequences(B, T, lmax):
+    """Workgroups take their items longest first, the order searched over the
+    lengths of all sequences: 70 sequences (more than one wave's worth, with
+    repeated lengths, so ties in the order) and 520 (beyond the searched
+    order, the plain order).  Every row and LSE is checked."""
+    rng = np.random.default_rng(B)
+    lens = rng.integers(T, lmax, size=B)
+    lens[::7] = lens[0]
+    w = workload.uniform_batch("many", seed=91 + B, B=B, T=T, Hq=4, Hkv=1, D=64, dtype="bf16", lens=lens.tolist())
+    say("prefill many sequences", B, T)
+    out, lse = prefill(w, upload(w))
+    check_vs_oracle(w, out, lse, f"prefill B={B} T={T}")
+
+
 @pytest.mark.parametrize("factor", [4.0, 64.0])
 def test_prefill_sharp_and_overflowing_scores(factor):
     """q x4 sharpens the softmax; q x64 pushes scores far past the exp range."""
