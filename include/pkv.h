@@ -214,7 +214,7 @@ pkv_status paged_attention_decode(const void* q, const void* k_pool, const void*
  * Supported: bf16 only (PKV_EUNSUPPORTED for fp32), D in {64, 128},
  * Hq / Hkv in {1, 2, 4, 8}, 1 <= T <= 8192, block_size 16.  The device-side
  * contract T <= L <= max_blocks * block_size is the decode one (checked under
- * PKV_DEBUG=1).  Work is split into items of 64 query rows of one KV head;
+ * PKV_DEBUG=1).  Work is split into items of 128 query rows of one KV head;
  * K and V of the item's visible keys are read once per item.
  */
 pkv_status paged_attention_prefill(const void* q, const void* k_pool, const void* v_pool,

@@ -11,7 +11,7 @@
 //
 // Work item = (row group, sequence, KV head); rows are r = t * G + g
 // (G = Hq/Hkv).  A workgroup of kWaves waves owns one item; each wave holds
-// TPW 16-row MFMA tiles (one in the shipped configuration: 64 rows per item).
+// TPW 16-row MFMA tiles (two in the shipped configuration: 128 rows per item).
 // Keys advance STEP (32) at a time, staged once per workgroup through LDS
 // (double-buffered: the next step's global loads are in flight while the
 // tiles work on the current one), with the item's block-table entries cached
@@ -165,11 +165,11 @@ __device__ void item_of_rank(const int32_t* lens, int B, int T, int max_tokens, 
   }
 }
 
-// Waves per SIMD the register budget is sized for: one tile per wave with
-// 32-key steps fits four (that many workgroups per CU, 20 or 39 KB of LDS
-// each); the other shapes two.
+// Waves per SIMD the register budget is sized for (that many workgroups per
+// CU, 20 or 39 KB of LDS each at 32-key steps): four with one tile per wave,
+// or two tiles at D = 64; two otherwise.
 template <int D, int TPW, int STEP>
-constexpr int prefill_waves_per_eu() { return TPW == 1 && STEP == 32 ? 4 : 2; }
+constexpr int prefill_waves_per_eu() { return STEP == 32 && (TPW == 1 || D == 64) ? 4 : 2; }
 
 template <int D, int TPW, int STEP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefill_waves_per_eu<D, TPW, STEP>())))
@@ -481,13 +481,14 @@ hipError_t launch_pf(const PrefillArgs& pa0, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// One 16-row tile per wave and 32-key steps: measured fastest on the
-// chunked-prefill batch of the benchmark (three workgroups per CU); two tiles
-// per wave halve the LDS reads per flop but leave two workgroups per CU and
-// were slower, and so were 64-key steps.
+// Two 16-row tiles per wave and 32-key steps: measured fastest on the
+// chunked-prefill batch of the Llama-3-8B shape.  The tiles share each K and
+// V read from LDS, which outweighs the occupancy given up at D = 128 (two
+// workgroups per CU instead of four with one tile: 312 against 346 us);
+// 64-key steps and 8-wave workgroups of one tile per wave were slower.
 template <int D>
 hipError_t launch_pf_d(const PrefillArgs& pa, hipStream_t stream) {
-  return launch_pf<D, 1, 32>(pa, stream);
+  return launch_pf<D, 2, 32>(pa, stream);
 }
 
 }  // namespace
