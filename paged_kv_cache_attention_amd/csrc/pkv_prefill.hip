@@ -327,17 +327,35 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
     for (int j = 0; j < TPW; ++j)
 #pragma unroll
       for (int h = 0; h < NQ; ++h) sacc[j][h] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    // all of the step's K chunks first, so that the LDS latency is paid once
+    // and the NQ * TPW accumulation chains interleave
+    u32x4_t kc[NQ][KS];
 #pragma unroll
-    for (int h = 0; h < NQ; ++h) {
-      const unsigned char* kr = ks + (16 * h + row) * PG::KROW + quad * 16;
+    for (int h = 0; h < NQ; ++h)
 #pragma unroll
-      for (int c = 0; c < KS; ++c) {
-        const bf16x8_v kv8 = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kr + c * 64));
+      for (int c = 0; c < KS; ++c)
+        kc[h][c] = *reinterpret_cast<const u32x4_t*>(ks + (16 * h + row) * PG::KROW + quad * 16 + c * 64);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < KS; ++c)
+#pragma unroll
+      for (int h = 0; h < NQ; ++h)
 #pragma unroll
         for (int j = 0; j < TPW; ++j)
-          sacc[j][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv8, as_bf16x8(qreg[j][c]), sacc[j][h], 0, 0, 0);
+          sacc[j][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kc[h][c]), as_bf16x8(qreg[j][c]), sacc[j][h],
+                                                               0, 0, 0);
+    // the step's V^T chunks, in flight during the softmax
+    bf16x8_v vb[NK][DT];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+      for (int d = 0; d < DT; ++d) {
+        const unsigned char* vr = vs + (16 * d + row) * PG::VROW + 64 * kk + quad * 8;
+        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vr);
+        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vr + 32);
+        vb[kk][d] = as_bf16x8(u32x4_t{lo.x, lo.y, hi.x, hi.y});
       }
-    }
+    __builtin_amdgcn_sched_barrier(0);
     // softmax.  Score i of the lane (i = 4 h + k) is key 16 h + 4 quad + k of
     // the step; k-slot 8 quad + e of P chunk kk holds score 8 kk + e.  The
     // running max m is kept in scaled base-2 units; since the scale is
@@ -400,19 +418,18 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
     }
     // O += P V: B operand = V^T[d][keys 32 kk + 4 quad .. +3 and 32 kk + 16 + 4 quad .. +3]
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk)
+    for (int kk = 0; kk < NK; ++kk) {
 #pragma unroll
-      for (int d = 0; d < DT; ++d) {
-        const unsigned char* vr = vs + (16 * d + row) * PG::VROW + 64 * kk + quad * 8;
-        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vr);
-        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vr + 32);
-        const bf16x8_v bv = as_bf16x8(u32x4_t{lo.x, lo.y, hi.x, hi.y});
+      for (int d = 0; d < DT; ++d)
 #pragma unroll
-        for (int j = 0; j < TPW; ++j) {
-          acc[j][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(phi[j][kk]), bv, acc[j][d], 0, 0, 0);
-          acc[j][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(plo[j][kk]), bv, acc[j][d], 0, 0, 0);
-        }
-      }
+        for (int j = 0; j < TPW; ++j)
+          acc[j][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(phi[j][kk]), vb[kk][d], acc[j][d], 0, 0, 0);
+#pragma unroll
+      for (int d = 0; d < DT; ++d)
+#pragma unroll
+        for (int j = 0; j < TPW; ++j)
+          acc[j][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(plo[j][kk]), vb[kk][d], acc[j][d], 0, 0, 0);
+    }
   };
 
   constexpr int kStepsPerWin = kTblWin * kBS / STEP;
