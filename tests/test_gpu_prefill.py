@@ -151,3 +151,24 @@ def test_prefill_key_range_beyond_one_table_window():
     say("prefill table window")
     out, lse = prefill(w, upload(w))
     check_vs_oracle(w, out, lse, "prefill beyond a table window")
+
+
+def test_prefill_maximum_chunk_sampled_rows():
+    """The largest chunk the entry point takes (T = 8192) after an 8200-token
+    prefix: 64 row groups of 128 rows per KV head, key ranges up to 16392
+    (three LDS table windows).  Sampled rows, each checked as the
+    one-token query at its own position (row t sees keys 0 .. L - T + t),
+    with their LSE; every row must be finite."""
+    T, pre = 8192, 8200
+    w = workload.uniform_batch("max-chunk", seed=141, B=1, T=T, Hq=8, Hkv=8, D=64, dtype="bf16", lens=[pre + T])
+    say("prefill maximum chunk")
+    out, lse = prefill(w, upload(w))
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    rng = np.random.default_rng(7)
+    rows = sorted({0, 1, 15, 16, 127, 128, 4095, 8191 - pre % 16, T - 2, T - 1, *rng.integers(0, T, size=6).tolist()})
+    L = int(w.context_lens[0])
+    for t in rows:
+        ref, ref_lse = oracle.paged_attention(w.values(w.q)[:, t:t + 1], w.values(w.k_pool), w.values(w.v_pool),
+                                              w.block_tables, np.array([L - T + t + 1]), w.scale, w.block_size)
+        check_attention(out[:, t:t + 1], ref, "bf16", f"max chunk row {t}", floor=mfma_floor(w))
+        check_lse(lse[:, t:t + 1], ref_lse, f"max chunk row {t}")
