@@ -281,10 +281,15 @@ def main():
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     prefill = w.T > 16   # a chunked-prefill workload: paged_attention_prefill
+    if prefill:   # the library's key-piece choice for this shape, workspace allocated up front
+        pieces = pkv.pkv_prefill_piece_tokens(w.B, w.T, w.Hq, w.Hkv, w.D, w.block_size, w.max_blocks)
+        pneed = pkv.pkv_prefill_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.D, w.block_size, w.max_blocks, pieces)
+        pws = torch.empty(max(pneed, 16), dtype=torch.uint8, device=dev)
 
     def attention():
         if prefill:
-            pkv.paged_attention_prefill(q, kp, vp, tables, lens, out=out, scale=scale, stream=stream)
+            pkv.paged_attention_prefill(q, kp, vp, tables, lens, out=out, scale=scale, piece_tokens=pieces,
+                                        workspace=pws, stream=stream)
         else:
             pkv.paged_attention_decode(q, kp, vp, tables, lens, out=out, scale=scale, partition_size=part,
                                        workspace=ws, stream=stream)
@@ -364,7 +369,9 @@ def main():
         result["roofline"] = {
             "bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-            "kernel": "paged_attention_prefill (MFMA tiles, LDS-staged K/V)", "flops_per_launch": fl,
+            "kernel": ("paged_attention_prefill (MFMA tiles, LDS-staged K/V)" if not pieces else
+                       f"paged_attention_prefill (MFMA tiles, LDS-staged K/V; {pieces}-token key pieces + merge)"),
+            "piece_tokens": pieces, "flops_per_launch": fl,
             "launch_ms": round(decode_ms, 5),
             "launch_ms_p10_p50_p90": [round(float(np.percentile(warm, p)), 5) for p in (10, 50, 90)],
             "bytes_per_launch": nb["decode"], "hbm_GBps": round(achieved, 1)}

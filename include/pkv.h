@@ -209,19 +209,46 @@ pkv_status paged_attention_decode(const void* q, const void* k_pool, const void*
  * position L - T + t and attends causally to keys 0 .. L - T + t:
  *   out[b, t, h, :] = softmax_j(scale * q[b, t, h, :] . K_b[j, h / G, :]) V_b[j, h / G, :]
  * with G = Hq / Hkv.  Same layouts, ownership, lse_out and stream semantics as
- * paged_attention_decode; no workspace (every output row is finished by the
- * workgroup that owns it).
+ * paged_attention_decode.
  * Supported: bf16 only (PKV_EUNSUPPORTED for fp32), D in {64, 128},
  * Hq / Hkv in {1, 2, 4, 8}, 1 <= T <= 8192, block_size 16.  The device-side
  * contract T <= L <= max_blocks * block_size is the decode one (checked under
  * PKV_DEBUG=1).  Work is split into items of 128 query rows of one KV head;
  * K and V of the item's visible keys are read once per item.
+ *
+ * piece_tokens = 0: every item is finished by the workgroup that owns it; the
+ * workspace is not used (may be NULL).  piece_tokens > 0 (a multiple of 32)
+ * also splits each item's keys into pieces of that many tokens from position
+ * 0, one workgroup per piece, so that batches with few items (one sequence,
+ * a long cached prefix) occupy the whole device.  Each piece of an item with
+ * more than one leaves a normalised partial and its log-sum-exp in the
+ * workspace, and a second kernel merges them as lse_reduce does; items that
+ * fit in one piece are written directly.  The workspace must then hold
+ * pkv_prefill_workspace_bytes(...) bytes (else PKV_EWORKSPACE), be 16-byte
+ * aligned, and not overlap any other argument; its contents after the call
+ * are unspecified, and two calls in flight need two workspaces.  Results with
+ * and without pieces agree within rounding; each is deterministic.
  */
 pkv_status paged_attention_prefill(const void* q, const void* k_pool, const void* v_pool,
                                    const int32_t* block_tables, const int32_t* context_lens,
                                    void* out, float* lse_out,
                                    int B, int T, int Hq, int Hkv, int D, int block_size, int max_blocks,
-                                   int N_blocks, float scale, pkv_dtype dtype, void* stream);
+                                   int N_blocks, float scale, int piece_tokens,
+                                   void* workspace, size_t workspace_bytes, pkv_dtype dtype, void* stream);
+
+/* Workspace bytes paged_attention_prefill needs for these arguments (0 when
+ * piece_tokens = 0 or no item can have more than one piece, and for
+ * arguments it rejects). */
+size_t pkv_prefill_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int block_size, int max_blocks,
+                                   int piece_tokens);
+
+/* A piece length for paged_attention_prefill on the current device: 0 when
+ * the B * ceil(T * Hq / Hkv / 128) * Hkv items already give every workgroup
+ * slot one (two slots per CU at D = 128, four at D = 64), else the key bound
+ * max_blocks * block_size cut into enough pieces for that (rounded up to a
+ * multiple of 32, at least 512 tokens).  0 for arguments the prefill
+ * rejects. */
+int pkv_prefill_piece_tokens(int B, int T, int Hq, int Hkv, int D, int block_size, int max_blocks);
 
 /*
  * lse_reduce -- merge P_max normalised partial attention results per row by

@@ -18,7 +18,8 @@ PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP = range(5)
 PKV_FP32, PKV_BF16 = 0, 1
 STATUS_NAMES = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_EWORKSPACE", 4: "PKV_EHIP"}
 EXPORTS = ("paged_kv_append", "paged_kv_append_rope", "paged_kv_copy_blocks", "paged_kv_gather",
-           "pkv_decode_workspace_bytes", "paged_attention_decode", "paged_attention_prefill", "lse_reduce",
+           "pkv_decode_workspace_bytes", "paged_attention_decode", "paged_attention_prefill",
+           "pkv_prefill_workspace_bytes", "pkv_prefill_piece_tokens", "lse_reduce",
            "pkv_last_error",
            "pkv_engine_create", "pkv_engine_destroy", "pkv_engine_last_error", "pkv_engine_add_request",
            "pkv_engine_schedule", "pkv_engine_commit", "pkv_engine_get_stats", "pkv_engine_request_tokens",
@@ -78,8 +79,12 @@ def load_library(path: pathlib.Path = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_decode_workspace_bytes.restype = S
     lib.paged_attention_decode.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, S, I, P]
     lib.paged_attention_decode.restype = I
-    lib.paged_attention_prefill.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P]
+    lib.paged_attention_prefill.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, S, I, P]
     lib.paged_attention_prefill.restype = I
+    lib.pkv_prefill_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
+    lib.pkv_prefill_workspace_bytes.restype = S
+    lib.pkv_prefill_piece_tokens.argtypes = [I, I, I, I, I, I, I]
+    lib.pkv_prefill_piece_tokens.restype = I
     lib.lse_reduce.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
     lib.lse_reduce.restype = I
     lib.paged_kv_copy_blocks.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
@@ -217,10 +222,22 @@ def paged_attention_decode(q, k_pool, v_pool, block_tables, context_lens, out=No
     return out
 
 
+def pkv_prefill_workspace_bytes(B, T, Hq, Hkv, D, block_size, max_blocks, piece_tokens):
+    return int(load_library().pkv_prefill_workspace_bytes(B, T, Hq, Hkv, D, block_size, max_blocks, piece_tokens))
+
+
+def pkv_prefill_piece_tokens(B, T, Hq, Hkv, D, block_size, max_blocks):
+    return int(load_library().pkv_prefill_piece_tokens(B, T, Hq, Hkv, D, block_size, max_blocks))
+
+
 def paged_attention_prefill(q, k_pool, v_pool, block_tables, context_lens, out=None, lse_out=None, scale=None,
-                            stream=None):
+                            piece_tokens=None, workspace=None, stream=None):
     """Chunked-prefill attention of q [B,T,Hq,D] (bf16) over the paged cache;
-    query t of sequence b sees keys 0 .. context_lens[b] - T + t.  Returns out."""
+    query t of sequence b sees keys 0 .. context_lens[b] - T + t.  Returns out.
+
+    piece_tokens None takes the library's suggestion for this shape on the
+    current device (pkv_prefill_piece_tokens); 0 never splits keys.  When
+    pieces need workspace and none is given, one is allocated."""
     torch = _torch()
     lib = load_library()
     B, T, Hq, D = q.shape
@@ -230,9 +247,16 @@ def paged_attention_prefill(q, k_pool, v_pool, block_tables, context_lens, out=N
         out = torch.empty_like(q)
     if scale is None:
         scale = 1.0 / D ** 0.5
+    if piece_tokens is None:
+        piece_tokens = pkv_prefill_piece_tokens(B, T, Hq, Hkv, D, bs, max_blocks)
+    need = pkv_prefill_workspace_bytes(B, T, Hq, Hkv, D, bs, max_blocks, piece_tokens)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.paged_attention_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool), _i32(block_tables, "block_tables"),
                                        _i32(context_lens, "context_lens"), _ptr(out), _ptr(lse_out), B, T, Hq, Hkv, D,
-                                       bs, max_blocks, N, float(scale), _dtype_code(q), _stream(stream, q.device)))
+                                       bs, max_blocks, N, float(scale), int(piece_tokens), _ptr(workspace), ws_bytes,
+                                       _dtype_code(q), _stream(stream, q.device)))
     return out
 
 

@@ -101,6 +101,19 @@ size_t pkv_decode_workspace_bytes(int B, int T, int Hq, int D, int max_blocks, i
   return (size_t)(rows * P * (unsigned long long)(D + 1) * 4ull);
 }
 
+size_t pkv_prefill_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int block_size, int max_blocks,
+                                   int piece_tokens) {
+  if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || D < 1 || block_size != 16 || max_blocks < 1 ||
+      piece_tokens < 0)
+    return 0;
+  return pkv::prefill_workspace_bytes(B, T, Hq, Hkv, D, max_blocks, piece_tokens);
+}
+
+int pkv_prefill_piece_tokens(int B, int T, int Hq, int Hkv, int D, int block_size, int max_blocks) {
+  if (block_size != 16 || max_blocks < 1 || (D != 64 && D != 128)) return 0;
+  return pkv::prefill_piece_tokens(B, T, Hq, Hkv, D, max_blocks, pkv::device_cus());
+}
+
 pkv_status paged_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
                            const int32_t* block_tables, const int32_t* context_lens_pre, int B, int T, int Hkv, int D,
                            int block_size, int max_blocks, int N_blocks, pkv_dtype dtype, void* stream) {
@@ -237,8 +250,8 @@ pkv_status paged_attention_decode(const void* q, const void* k_pool, const void*
 
 pkv_status paged_attention_prefill(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
                                    const int32_t* context_lens, void* out, float* lse_out, int B, int T, int Hq, int Hkv,
-                                   int D, int block_size, int max_blocks, int N_blocks, float scale, pkv_dtype dtype,
-                                   void* stream) {
+                                   int D, int block_size, int max_blocks, int N_blocks, float scale, int piece_tokens,
+                                   void* workspace, size_t workspace_bytes, pkv_dtype dtype, void* stream) {
   pkv_status st = check_dtype(dtype);
   if (st != PKV_OK) return st;
   if (B < 0 || T < 1 || Hq < 1) return fail(PKV_EINVAL, "B must be >= 0, T and Hq >= 1");
@@ -249,10 +262,18 @@ pkv_status paged_attention_prefill(const void* q, const void* k_pool, const void
   if (dtype != PKV_BF16) return fail(PKV_EUNSUPPORTED, "paged_attention_prefill computes in bf16 only");
   if (T > pkv::kPrefillMaxT) return fail(PKV_EUNSUPPORTED, "T = %d unsupported (at most %d)", T, pkv::kPrefillMaxT);
   if (!std::isfinite(scale)) return fail(PKV_EINVAL, "scale must be finite");
+  if (piece_tokens < 0 || piece_tokens % pkv::kPrefillStep)
+    return fail(PKV_EINVAL, "piece_tokens (%d) must be 0 or a positive multiple of %d", piece_tokens,
+                pkv::kPrefillStep);
   if (B == 0) return PKV_OK;
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out) return fail(PKV_EINVAL, "null pointer argument");
   if (out == q || out == k_pool || out == v_pool) return fail(PKV_EINVAL, "out must not alias an input");
   if ((long long)B * T * Hq > (1LL << 30)) return fail(PKV_EINVAL, "B*T*Hq too large");
+  const size_t need = pkv::prefill_workspace_bytes(B, T, Hq, Hkv, D, max_blocks, piece_tokens);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(PKV_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+  if (need && reinterpret_cast<uintptr_t>(workspace) % 16)
+    return fail(PKV_EINVAL, "workspace must be 16-byte aligned");
 
   pkv::DecodeArgs a{};
   a.q = q; a.k_pool = k_pool; a.v_pool = v_pool; a.block_tables = block_tables; a.context_lens = context_lens;
@@ -263,7 +284,8 @@ pkv_status paged_attention_prefill(const void* q, const void* k_pool, const void
   if (debug_enabled() && (st = debug_validate(block_tables, context_lens, B, T, 0, block_size, max_blocks, N_blocks, s)) !=
                              PKV_OK)
     return st;
-  return from_hip(pkv::launch_prefill(a, s), "paged_attention_prefill launch");
+  return from_hip(pkv::launch_prefill(a, need ? piece_tokens : 0, static_cast<float*>(workspace), s),
+                  "paged_attention_prefill launch");
 }
 
 pkv_status lse_reduce(const float* part_out, const float* part_lse, void* out, float* lse_out, int B, int T, int Hq,

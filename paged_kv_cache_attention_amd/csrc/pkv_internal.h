@@ -68,7 +68,21 @@ struct GroupPlan {
 // Chunked-prefill attention (T up to kPrefillMaxT causal query rows per
 // sequence, bf16) on MFMA tiles with LDS-staged keys and values.
 constexpr int kPrefillMaxT = 8192;
-hipError_t launch_prefill(const DecodeArgs& a, hipStream_t stream);
+constexpr int kPrefillTPW = 2;                  // 16-row MFMA tiles per wave
+constexpr int kPrefillRows = 16 * kPrefillTPW * 4;   // query rows per work item (4 waves)
+constexpr int kPrefillStep = 32;                // keys per staged step; pieces are multiples of it
+constexpr int kPrefillMinPiece = 512;           // smallest piece the policy picks
+// Key pieces per item for piece_tokens (1: no split).
+int prefill_pieces(int max_blocks, int piece_tokens);
+// Workspace for the partials of split items (0 when nothing splits).
+size_t prefill_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int max_blocks, int piece_tokens);
+// Piece length the library suggests: 0 when the items already give every
+// workgroup slot of the chip one, else the table's key bound cut into enough
+// pieces for that.
+int prefill_piece_tokens(int B, int T, int Hq, int Hkv, int D, int max_blocks, int cus);
+// piece_tokens: 0 or a positive multiple of kPrefillStep; workspace holds
+// prefill_workspace_bytes(...) bytes when that is nonzero.
+hipError_t launch_prefill(const DecodeArgs& a, int piece_tokens, float* workspace, hipStream_t stream);
 
 bool groups_enabled();
 // Plan inside the decode kernel when the unit list fits in LDS (default;

@@ -74,9 +74,16 @@ struct PGeo {
   static_assert(PER_T * kThreads == STEP * RC, "even staging split");
 };
 
+static_assert(PGeo<64, kPrefillTPW, kPrefillStep>::ROWS == kPrefillRows &&
+                  PGeo<128, kPrefillTPW, kPrefillStep>::ROWS == kPrefillRows,
+              "work item rows shared with the host-side sizing");
+
 struct PrefillArgs {
   DecodeArgs a;
-  int groups;   // row groups per (sequence, KV head)
+  int groups;        // row groups per (sequence, KV head)
+  int pieces;        // key pieces per item in the grid (1: no split)
+  int piece_steps;   // keys per piece / STEP (0: no split)
+  float* part;       // split items' partials: [B][groups][Hkv][pieces] slots of ROWS x (D + 1) floats
 };
 
 // Start order of the work items.  The workgroup of rank p = blockIdx / Hkv
@@ -188,11 +195,12 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = a.Hq / a.Hkv;
   const int R = a.T * G;
-  // items longest first (item_of_rank); the KV heads of one item are
-  // consecutive workgroups
+  // items longest first (item_of_rank); the KV heads of one piece of an item
+  // are consecutive workgroups, and the pieces of an item follow each other
   const int max_tokens = a.max_blocks * kBS;
   const int kv = (int)blockIdx.x % a.Hkv;
-  const int p = (int)blockIdx.x / a.Hkv;
+  const int piece = ((int)blockIdx.x / a.Hkv) % pa.pieces;
+  const int p = (int)blockIdx.x / a.Hkv / pa.pieces;
   int b, rg;
   if (a.B == 1) {
     b = 0;
@@ -214,6 +222,15 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
   const int kv_len = clampi(L - a.T + t_last + 1, 0, L);   // keys any row of the group sees
   const int nsteps = (kv_len + STEP - 1) / STEP;
   const int nblk = (kv_len + kBS - 1) / kBS;
+  // This workgroup's steps [s0, s1): the whole item, or one piece of
+  // piece_steps steps.  An item of npc > 1 pieces leaves normalised partials.
+  int s0 = 0, s1 = nsteps, npc = 1;
+  if (pa.piece_steps > 0) {
+    npc = max(1, (nsteps + pa.piece_steps - 1) / pa.piece_steps);
+    if (piece >= npc) return;   // the item is shorter than this piece: whole workgroup
+    s0 = piece * pa.piece_steps;
+    s1 = min(nsteps, s0 + pa.piece_steps);
+  }
 
   // ---- this wave's rows: tile j holds rows rw + 16 j + (lane % 16) ----
   const int row = lane & 15, quad = lane >> 4;
@@ -433,36 +450,40 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
   };
 
   constexpr int kStepsPerWin = kTblWin * kBS / STEP;
-  if (nsteps > 0) {
-    load_window(0);
+  if (s1 > s0) {
+    load_window(s0 / kStepsPerWin);
     __syncthreads();
-    issue(0);
-    commit(0, 0);
+    issue(s0);
+    commit(s0, s0 & 1);
     __syncthreads();
     auto step = [&](int s, auto masked_tag) {
       const int buf = s & 1;
-      if (s + 1 < nsteps && (s + 1) % kStepsPerWin == 0) {   // step s + 1 opens a new table window
+      if (s + 1 < s1 && (s + 1) % kStepsPerWin == 0) {   // step s + 1 opens a new table window
         __syncthreads();
         load_window((s + 1) / kStepsPerWin);
         __syncthreads();
       }
-      if (s + 1 < nsteps) issue(s + 1);
+      if (s + 1 < s1) issue(s + 1);
       if (wave_active) compute(s, buf, masked_tag);
-      if (s + 1 < nsteps) commit(s + 1, buf ^ 1);
+      if (s + 1 < s1) commit(s + 1, buf ^ 1);
       __syncthreads();
     };
     // Steps before s_mask hold only keys every row of the wave sees; the
     // rest are masked.  Two loops, one per kind, so each keeps its registers
     // in place (the barrier count per step is the same for every wave).
-    const int s_mask = wave_active ? min(nsteps, hi_min / STEP) : nsteps;
-    int s = 0;
+    const int s_mask = wave_active ? clampi(hi_min / STEP, s0, s1) : s1;
+    int s = s0;
     for (; s < s_mask; ++s) step(s, std::false_type{});
-    for (; s < nsteps; ++s) step(s, std::true_type{});
+    for (; s < s1; ++s) step(s, std::true_type{});
   }
 
-  // ---- epilogue: O / l in bf16, lse in natural log ----
+  // ---- epilogue: O / l in bf16 (or, for a piece of a split item, in fp32
+  // to the item's slot), lse in natural log ----
   if (!wave_active) return;
   uint16_t* out = static_cast<uint16_t*>(a.out);
+  float* slot = npc > 1 ? pa.part + ((((size_t)b * pa.groups + rg) * a.Hkv + kv) * pa.pieces + piece) *
+                                        (size_t)(PG::ROWS * (D + 1))
+                        : nullptr;
 #pragma unroll
   for (int j = 0; j < TPW; ++j) {
     float l = l_part[j] + __shfl_xor(l_part[j], 16);
@@ -473,28 +494,103 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
       const float lr = __shfl(l, 4 * quad + k);
       const float mr = __shfl(m_row[j], 4 * quad + k);
       if (rr < R) {
-        const int t = rr / G, h = kv * G + (rr - (rr / G) * G);
-        const size_t orow = ((size_t)b * a.T + t) * a.Hq + h;
         const float inv = lr != 0.f ? 1.f / lr : 0.f;
+        const float lse = lr != 0.f ? (mr + log2f(lr)) * kLn2 : kNegInf;
+        if (slot) {   // partial of a piece: rows with no visible key here give (0, -inf)
+          float* o = slot + (size_t)(rr - r0) * D;
 #pragma unroll
-        for (int d = 0; d < DT; ++d) out[orow * D + 16 * d + row] = f32_to_bf16_rne(acc[j][d][k] * inv);
-        if (row == 0 && a.lse_out) a.lse_out[orow] = lr != 0.f ? (mr + log2f(lr)) * kLn2 : kNegInf;
+          for (int d = 0; d < DT; ++d) o[16 * d + row] = acc[j][d][k] * inv;
+          if (row == 0) slot[PG::ROWS * D + (rr - r0)] = lse;
+        } else {
+          const int t = rr / G, h = kv * G + (rr - (rr / G) * G);
+          const size_t orow = ((size_t)b * a.T + t) * a.Hq + h;
+#pragma unroll
+          for (int d = 0; d < DT; ++d) out[orow * D + 16 * d + row] = f32_to_bf16_rne(acc[j][d][k] * inv);
+          if (row == 0 && a.lse_out) a.lse_out[orow] = lse;
+        }
       }
     }
   }
 }
 
+// Merges the pieces of each split item.  Pieces cover disjoint key ranges of
+// the same rows and carry normalised partials with their log-sum-exp, so
+//   M = max_p lse_p,  w_p = exp(lse_p - M),
+//   out = sum_p w_p o_p / sum_p w_p,  lse = M + ln sum_p w_p
+// ("Inference From Scratch", ch. 8: softmax over pieces combined through the
+// running max and sum).  A piece where a row sees no key has lse = -inf,
+// weight 0 and o = 0.  One workgroup per kMergeRows rows of an item, D / 4
+// threads per row with 4 columns each; the loads of every piece are
+// independent and the sum runs in piece order.
+constexpr int kMergeThreads = 256;
+
+template <int D, int ROWS, int STEP>
+__global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArgs pa) {
+  constexpr int TPR = D / 4, RPW = kMergeThreads / TPR, CHUNKS = ROWS / RPW;
+  static_assert(CHUNKS * RPW == ROWS, "whole chunks of rows");
+  const DecodeArgs& a = pa.a;
+  const int item = (int)blockIdx.x / CHUNKS, chunk = (int)blockIdx.x % CHUNKS;
+  const int kv = item % a.Hkv, rest = item / a.Hkv;
+  const int rg = rest % pa.groups, b = rest / pa.groups;
+  const int G = a.Hq / a.Hkv, R = a.T * G;
+  const int L = clampi(a.context_lens[b], 0, a.max_blocks * kBS);
+  const int r0 = rg * ROWS;
+  const int t_last = (min(R, r0 + ROWS) - 1) / G;
+  const int kv_len = clampi(L - a.T + t_last + 1, 0, L);   // as the tile computes it
+  const int npc = max(1, ((kv_len + STEP - 1) / STEP + pa.piece_steps - 1) / pa.piece_steps);
+  if (npc <= 1) return;   // written directly by the tile
+  const int i = chunk * RPW + (int)threadIdx.x / TPR;   // row within the item
+  if (r0 + i >= R) return;
+  constexpr size_t SLOT = (size_t)ROWS * (D + 1);
+  const float* base = pa.part + (((size_t)b * pa.groups + rg) * a.Hkv + kv) * pa.pieces * SLOT;
+  const float* lp = base + (size_t)ROWS * D + i;
+  const float* opp = base + (size_t)i * D + ((int)threadIdx.x % TPR) * 4;
+  float M = kNegInf;
+  for (int q = 0; q < npc; ++q) M = fmaxf(M, lp[q * SLOT]);
+  float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f, wsum = 0.f;
+  if (M != kNegInf) {
+#pragma unroll 4
+    for (int q = 0; q < npc; ++q) {
+      const float lq = lp[q * SLOT];
+      const float4 v = *reinterpret_cast<const float4*>(opp + q * SLOT);
+      const float w = lq == kNegInf ? 0.f : __builtin_amdgcn_exp2f((lq - M) * kLog2e);
+      wsum += w;
+      o0 = fmaf(w, v.x, o0);
+      o1 = fmaf(w, v.y, o1);
+      o2 = fmaf(w, v.z, o2);
+      o3 = fmaf(w, v.w, o3);
+    }
+  }
+  const float inv = wsum != 0.f ? 1.f / wsum : 0.f;
+  const int rr = r0 + i, t = rr / G, h = kv * G + (rr - t * G);
+  const size_t orow = ((size_t)b * a.T + t) * a.Hq + h;
+  const int c = ((int)threadIdx.x % TPR) * 4;
+  uint16_t* op = static_cast<uint16_t*>(a.out) + orow * D + c;
+  op[0] = f32_to_bf16_rne(o0 * inv);
+  op[1] = f32_to_bf16_rne(o1 * inv);
+  op[2] = f32_to_bf16_rne(o2 * inv);
+  op[3] = f32_to_bf16_rne(o3 * inv);
+  if (c == 0 && a.lse_out) a.lse_out[orow] = wsum != 0.f ? M + logf(wsum) : kNegInf;
+}
+
 template <int D, int TPW, int STEP>
-hipError_t launch_pf(const PrefillArgs& pa0, hipStream_t stream) {
+hipError_t launch_pf(const PrefillArgs& pa0, int piece_tokens, hipStream_t stream) {
   using PG = PGeo<D, TPW, STEP>;
   PrefillArgs pa = pa0;
   const int G = pa.a.Hq / pa.a.Hkv;
   pa.groups = (pa.a.T * G + PG::ROWS - 1) / PG::ROWS;
   const long long items = (long long)pa.groups * pa.a.B * pa.a.Hkv;
   if (items <= 0) return hipSuccess;
-  if (items > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<D, TPW, STEP>), dim3((unsigned)items), dim3(kThreads), 0, stream, pa,
-                     pa.a.scale * kLog2e);
+  pa.pieces = prefill_pieces(pa.a.max_blocks, piece_tokens);
+  pa.piece_steps = pa.pieces > 1 ? piece_tokens / STEP : 0;
+  if (items * pa.pieces > 0x7fffffff || items * PG::ROWS > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prefill_kernel<D, TPW, STEP>), dim3((unsigned)(items * pa.pieces)), dim3(kThreads), 0, stream,
+                     pa, pa.a.scale * kLog2e);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pa.pieces <= 1) return e;
+  constexpr int kChunks = PG::ROWS / (kMergeThreads / (D / 4));
+  hipLaunchKernelGGL((prefill_merge_kernel<D, PG::ROWS, STEP>), dim3((unsigned)(items * kChunks)),
+                     dim3(kMergeThreads), 0, stream, pa);
   return hipGetLastError();
 }
 
@@ -504,16 +600,49 @@ hipError_t launch_pf(const PrefillArgs& pa0, hipStream_t stream) {
 // workgroups per CU instead of four with one tile: 312 against 346 us);
 // 64-key steps and 8-wave workgroups of one tile per wave were slower.
 template <int D>
-hipError_t launch_pf_d(const PrefillArgs& pa, hipStream_t stream) {
-  return launch_pf<D, 2, 32>(pa, stream);
+hipError_t launch_pf_d(const PrefillArgs& pa, int piece_tokens, hipStream_t stream) {
+  return launch_pf<D, kPrefillTPW, kPrefillStep>(pa, piece_tokens, stream);
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const DecodeArgs& a, hipStream_t stream) {
+int prefill_pieces(int max_blocks, int piece_tokens) {
+  if (piece_tokens <= 0) return 1;
+  const long long keys = (long long)max_blocks * kBS;
+  return (int)max(1LL, (keys + piece_tokens - 1) / piece_tokens);
+}
+
+size_t prefill_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int max_blocks, int piece_tokens) {
+  const int pieces = prefill_pieces(max_blocks, piece_tokens);
+  if (pieces <= 1 || B <= 0 || T <= 0 || Hkv <= 0) return 0;
+  const long long groups = ((long long)T * (Hq / Hkv) + kPrefillRows - 1) / kPrefillRows;
+  return (size_t)B * groups * Hkv * pieces * kPrefillRows * (D + 1) * sizeof(float);
+}
+
+int prefill_piece_tokens(int B, int T, int Hq, int Hkv, int D, int max_blocks, int cus) {
+  if (B <= 0 || T <= 0 || Hkv <= 0 || Hq % Hkv) return 0;
+  const long long groups = ((long long)T * (Hq / Hkv) + kPrefillRows - 1) / kPrefillRows;
+  const long long items = (long long)B * groups * Hkv;
+  // one workgroup per slot (prefill_waves_per_eu workgroups per CU): fewer
+  // items leave CUs idle.  More pieces than that only add partials to write
+  // and merge (measured on one sequence with an 8192-token prefix: 4 pieces
+  // 170-180 us, 2 about 208, 8 about 225, none 330).
+  const long long want = (long long)cus * (D == 64 ? prefill_waves_per_eu<64, kPrefillTPW, kPrefillStep>()
+                                                   : prefill_waves_per_eu<128, kPrefillTPW, kPrefillStep>());
+  if (items >= want) return 0;
+  const long long keys = (long long)max_blocks * kBS;
+  const long long pieces = (want + items - 1) / items;
+  long long tokens = (keys + pieces - 1) / pieces;
+  tokens = (tokens + kPrefillStep - 1) / kPrefillStep * kPrefillStep;
+  tokens = max(tokens, (long long)kPrefillMinPiece);
+  return tokens >= keys ? 0 : (int)tokens;
+}
+
+hipError_t launch_prefill(const DecodeArgs& a, int piece_tokens, float* workspace, hipStream_t stream) {
   PrefillArgs pa{};
   pa.a = a;
-  return a.D == 64 ? launch_pf_d<64>(pa, stream) : launch_pf_d<128>(pa, stream);
+  pa.part = workspace;
+  return a.D == 64 ? launch_pf_d<64>(pa, piece_tokens, stream) : launch_pf_d<128>(pa, piece_tokens, stream);
 }
 
 }  // namespace pkv

@@ -85,12 +85,13 @@ def test_decode_empty_batch_is_a_noop():
 
 def _prefill(**kw):
     args = dict(q=Q, k=K, v=V, tab=TAB, lens=LENS, out=OUT, lse=None, B=2, T=64, Hq=8, Hkv=2, D=128, bs=16, mb=8,
-                N=16, scale=0.088, dt=pkv.PKV_BF16)
+                N=16, scale=0.088, pt=0, ws=None, wsb=0, dt=pkv.PKV_BF16)
     args.update(kw)
     lib = pkv.load_library()
     st = lib.paged_attention_prefill(args["q"], args["k"], args["v"], args["tab"], args["lens"], args["out"],
                                      args["lse"], args["B"], args["T"], args["Hq"], args["Hkv"], args["D"], args["bs"],
-                                     args["mb"], args["N"], args["scale"], args["dt"], None)
+                                     args["mb"], args["N"], args["scale"], args["pt"], args["ws"], args["wsb"],
+                                     args["dt"], None)
     return st, lib.pkv_last_error().decode()
 
 
@@ -107,6 +108,11 @@ def _prefill(**kw):
     (dict(bs=8), pkv.PKV_EUNSUPPORTED),
     (dict(T=8193), pkv.PKV_EUNSUPPORTED),
     (dict(Hq=32, Hkv=2), pkv.PKV_EUNSUPPORTED),     # Hq/Hkv = 16
+    (dict(pt=-32), pkv.PKV_EINVAL),
+    (dict(pt=48), pkv.PKV_EINVAL),                   # not a multiple of 32
+    (dict(pt=32), pkv.PKV_EWORKSPACE),               # 128 keys in 4 pieces: partials need a workspace
+    (dict(pt=32, ws=ctypes.c_void_p(1 << 20), wsb=64), pkv.PKV_EWORKSPACE),   # too small
+    (dict(pt=32, ws=ctypes.c_void_p((1 << 20) + 4), wsb=1 << 30), pkv.PKV_EINVAL),   # misaligned
 ])
 def test_prefill_argument_errors(kw, status):
     st, msg = _prefill(**kw)
@@ -117,6 +123,27 @@ def test_prefill_argument_errors(kw, status):
 def test_prefill_empty_batch_is_a_noop():
     st, _ = _prefill(B=0, q=None, out=None)
     assert st == pkv.PKV_OK
+
+
+def test_prefill_workspace_and_piece_policy():
+    """Workspace: one 128-row slot of D + 1 floats per (sequence, row group,
+    KV head, piece) when any item can have more than one piece, else none.
+    The suggested piece length leaves grids that fill the device unsplit and
+    cuts the key bound of a one-sequence chunk into multiples of 32 tokens
+    (without a GPU the library assumes 256 CUs)."""
+    lib = pkv.load_library()
+    wsb = lib.pkv_prefill_workspace_bytes
+    # B=2, T=64, G=4: 256 rows, 2 row groups; 8 blocks = 128 keys in pieces of 32: 4 pieces
+    assert wsb(2, 64, 8, 2, 128, 16, 8, 32) == 2 * 2 * 2 * 4 * 128 * 129 * 4
+    assert wsb(2, 64, 8, 2, 128, 16, 8, 0) == 0
+    assert wsb(2, 64, 8, 2, 128, 16, 8, 128) == 0    # one piece covers every key
+    assert wsb(2, 64, 8, 2, 128, 16, 8, -32) == 0 and wsb(2, 64, 8, 2, 128, 8, 8, 32) == 0
+    pt = lib.pkv_prefill_piece_tokens
+    assert pt(8, 512, 32, 8, 128, 16, 256) == 0       # 1024 items for 512 slots: no split
+    assert pt(1, 512, 32, 8, 128, 16, 544) == 2176   # 128 items: 4 pieces of the 8704-token bound
+    assert pt(1, 512, 32, 8, 64, 16, 544) == 1088    # D = 64: 1024 slots, 8 pieces
+    assert pt(1, 512, 32, 8, 128, 16, 8) == 0        # 128 keys: never below 512 tokens
+    assert pt(1, 512, 32, 8, 80, 16, 544) == 0       # unsupported head dim
 
 
 def test_append_rope_argument_errors():

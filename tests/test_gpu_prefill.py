@@ -24,10 +24,11 @@ def say(*a):
     print(*a, flush=True)
 
 
-def prefill(w, d, lse=True):
+def prefill(w, d, lse=True, piece_tokens=0):
     lse_t = torch.full((w.B, w.T, w.Hq), float("nan"), device="cuda") if lse else None
-    out = pkv.paged_attention_prefill(d["q"], d["k"], d["v"], d["tables"], d["lens"], lse_out=lse_t,
-                                      scale=float(w.scale))
+    out = torch.full_like(d["q"], float("nan"))
+    pkv.paged_attention_prefill(d["q"], d["k"], d["v"], d["tables"], d["lens"], out=out, lse_out=lse_t,
+                                scale=float(w.scale), piece_tokens=piece_tokens)
     torch.cuda.synchronize()
     return host(out), (host(lse_t) if lse else None)
 
@@ -172,3 +173,60 @@ def test_prefill_maximum_chunk_sampled_rows():
                                               w.block_tables, np.array([L - T + t + 1]), w.scale, w.block_size)
         check_attention(out[:, t:t + 1], ref, "bf16", f"max chunk row {t}", floor=mfma_floor(w))
         check_lse(lse[:, t:t + 1], ref_lse, f"max chunk row {t}")
+
+
+PIECE_CASES = [  # (D, Hq, Hkv, T, lens, piece_tokens)
+    (128, 32, 8, 64, [64, 65, 80, 96, 200, 333], 32),   # up to 11 pieces; rows with no key in later pieces
+    (64, 16, 4, 129, [129, 161, 192, 2000], 96),        # pieces across 32-key steps and blocks
+    (64, 8, 8, 100, [100, 117, 260], 64),
+    (128, 16, 8, 37, [37, 38, 500], 160),               # some items in one piece, written directly
+]
+
+
+@pytest.mark.parametrize("D,Hq,Hkv,T,lens,piece_tokens", PIECE_CASES)
+def test_prefill_key_pieces(D, Hq, Hkv, T, lens, piece_tokens):
+    """Items split into key pieces of piece_tokens tokens, one workgroup each,
+    merged by log-sum-exp: the oracle's result, the unsplit call's within
+    rounding, and the same bits on a second call."""
+    w = workload.uniform_batch("pieces", seed=151 + T, B=len(lens), T=T, Hq=Hq, Hkv=Hkv, D=D, dtype="bf16",
+                               lens=lens)
+    say("prefill pieces", D, Hq, Hkv, T, lens, piece_tokens)
+    d = upload(w)
+    out, lse = prefill(w, d, piece_tokens=piece_tokens)
+    check_vs_oracle(w, out, lse, f"prefill pieces of {piece_tokens} D={D} T={T}")
+    out0, lse0 = prefill(w, d, piece_tokens=0)
+    ref_ulp = oracle.bf16_ulp(out0)
+    assert (np.abs(out - out0) <= 2 * ref_ulp + mfma_floor(w)).all(), "split and unsplit results differ"
+    assert np.allclose(lse, lse0, atol=1e-4, rtol=0)
+    out2, lse2 = prefill(w, d, piece_tokens=piece_tokens)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+
+
+def test_prefill_key_pieces_overflowing_scores():
+    """q x64: every piece has its own running max far from the others'."""
+    w = workload.uniform_batch("sharp-pieces", seed=161, B=3, T=48, Hq=16, Hkv=4, D=128, dtype="bf16",
+                               lens=[48, 90, 400])
+    w = workload.scaled_queries(w, 64.0)
+    say("prefill pieces q x64")
+    out, lse = prefill(w, upload(w), piece_tokens=64)
+    check_vs_oracle(w, out, lse, "prefill pieces q x64")
+
+
+def test_prefill_one_sequence_long_prefix_suggested_pieces():
+    """One 512-token chunk after an 8192-token prefix (the shape a serving
+    loop prefills a long prompt in): 128 items, so the library suggests key
+    pieces; sampled rows against the oracle, every row finite."""
+    T, pre = 512, 8192
+    w = workload.uniform_batch("one-long", seed=171, B=1, T=T, Hq=32, Hkv=8, D=128, dtype="bf16", lens=[pre + T])
+    pt = pkv.pkv_prefill_piece_tokens(w.B, w.T, w.Hq, w.Hkv, w.D, w.block_size, w.max_blocks)
+    say("prefill one long sequence, suggested pieces", pt)
+    assert pt > 0
+    out, lse = prefill(w, upload(w), piece_tokens=None)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    L = int(w.context_lens[0])
+    rng = np.random.default_rng(3)
+    for t in sorted({0, 1, 127, 128, 255, T - 1, *rng.integers(0, T, size=4).tolist()}):
+        ref, ref_lse = oracle.paged_attention(w.values(w.q)[:, t:t + 1], w.values(w.k_pool), w.values(w.v_pool),
+                                              w.block_tables, np.array([L - T + t + 1]), w.scale, w.block_size)
+        check_attention(out[:, t:t + 1], ref, "bf16", f"one long sequence row {t}", floor=mfma_floor(w))
+        check_lse(lse[:, t:t + 1], ref_lse, f"one long sequence row {t}")

@@ -37,6 +37,9 @@ def test_length_ranges():
     pf = workload.llama8b_chunked_prefill(structure_only=True)
     assert pf.T == 512 and (pf.context_lens == pf.lens_pre + 512).all()
     assert pf.lens_pre.min() >= 0 and pf.lens_pre.max() <= 3584 and pf.max_blocks == 256
+    lp = workload.llama8b_long_prompt_chunk(structure_only=True)
+    assert lp.B == 1 and lp.T == 512 and list(lp.lens_pre) == [8192] and list(lp.context_lens) == [8704]
+    assert lp.max_blocks == 544
 
 
 def test_private_blocks_are_not_shared():

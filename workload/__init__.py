@@ -340,6 +340,23 @@ def llama8b_chunked_prefill(poison=True, partition_size=0, structure_only=False)
                    structure_only=structure_only)
 
 
+def llama8b_long_prompt_chunk(poison=True, partition_size=0, structure_only=False):
+    """One sequence prefilling a 512-token chunk of a long prompt (GQA 32/8,
+    D=128, bf16) after 8192 cached tokens: the serving-loop shape of chunked
+    prefill, where one request's chunk is attended at a time."""
+    rng = np.random.Generator(np.random.PCG64(7))
+    T, pre = 512, 8192
+    lens = np.array([pre + T], dtype=np.int64)
+    nblk = [_cdiv(int(L), BLOCK_SIZE) for L in lens]
+    pool = _cdiv(11 * sum(nblk), 10)
+    perm = rng.permutation(pool)
+    per_seq = [[(0, i) for i in range(nblk[0])]]
+    return _finish("llama8b_long_prompt_chunk", rng=rng, B=1, T=T, Hq=32, Hkv=8, D=128, dtype="bf16",
+                   partition_size=partition_size, context_lens=lens, per_seq_blocks=per_seq,
+                   n_blocks_total=pool, perm=perm, max_blocks=nblk[0], poison=poison, append=True,
+                   structure_only=structure_only)
+
+
 WORKLOADS = {
     "tiny_fp32": tiny_fp32,
     "tinylm_mha_bf16": tinylm_mha_bf16,
@@ -347,6 +364,7 @@ WORKLOADS = {
     "llama8b_prefix_share": llama8b_prefix_share,
     "longctx_verify": longctx_verify,
     "llama8b_chunked_prefill": llama8b_chunked_prefill,
+    "llama8b_long_prompt_chunk": llama8b_long_prompt_chunk,
 }
 
 
