@@ -180,6 +180,8 @@ PIECE_CASES = [  # (D, Hq, Hkv, T, lens, piece_tokens)
     (64, 16, 4, 129, [129, 161, 192, 2000], 96),        # pieces across 32-key steps and blocks
     (64, 8, 8, 100, [100, 117, 260], 64),
     (128, 16, 8, 37, [37, 38, 500], 160),               # some items in one piece, written directly
+    (64, 32, 4, 17, [17, 40, 1000], 32),                # G = 8
+    (128, 32, 8, 1, [1, 30, 300], 64),                  # T = 1: one row group, decode rows in pieces
 ]
 
 
