@@ -219,3 +219,17 @@ def test_empty_batch_and_single_partition_identity():
     lib = pkv.load_library()
     assert lib.paged_attention_decode(None, None, None, None, None, None, None, 0, 1, 4, 4, 64, 16, 1, 1, 0.125, 0,
                                       None, 0, 0, None) == 0
+
+
+@pytest.mark.parametrize("T", [1, 2])
+def test_many_heads_long_batch(T):
+    """64 query heads (two decode workgroups per range) over a batch long
+    enough that ranges exceed their minimum length, so each XCD takes a
+    contiguous run of ranges: every row against the oracle."""
+    rng = np.random.default_rng(17)
+    lens = rng.integers(2000, 4000, size=16).tolist()
+    w = workload.uniform_batch("many-heads", seed=19 + T, B=16, T=T, Hq=64, Hkv=8, D=128, dtype="bf16", lens=lens)
+    say("many heads long batch", T)
+    d = upload(w)
+    out, lse = decode(w, d, 0)
+    oracle_check(w, out, lse, f"Hq=64 long batch T={T}")
