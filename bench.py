@@ -198,21 +198,28 @@ def serve_bench(torch, dev, iters=200):
             p = np.concatenate([common, p[: len(p) // 3]])
         reqs.append((r, p, 40 if r == 0 else int(rng.integers(3, 30))))
     worst = sum(-(-(len(p) + m) // 16) for _, p, m in reqs)
-    eng = pkv.Engine(worst // 3, 16, max_blocks_per_seq=16, max_running=8, max_prefill_tokens=256, prefix_cache=True)
-    for rid, p, m in reqs:
-        eng.add_request(rid, p, m)
     kp = torch.zeros(worst // 3, 16, HKV, D, dtype=torch.bfloat16, device=dev)
     vp = torch.zeros_like(kp)
-    ex = PagedExecutor(eng, kp, vp, HQ, 10000.0, lambda t: tuple(e[t.long()] for e in emb),
-                       lambda plan, outs: ((plan.request_id * 7 + plan.context_lens) % V).astype(np.int32))
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    while ex.step() is not None:
-        pass
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    st = eng.stats()
-    eng.close()
+
+    def serve_once():
+        eng = pkv.Engine(worst // 3, 16, max_blocks_per_seq=16, max_running=8, max_prefill_tokens=256,
+                         prefix_cache=True)
+        for rid, p, m in reqs:
+            eng.add_request(rid, p, m)
+        ex = PagedExecutor(eng, kp, vp, HQ, 10000.0, lambda t: tuple(e[t.long()] for e in emb),
+                           lambda plan, outs: ((plan.request_id * 7 + plan.context_lens) % V).astype(np.int32))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while ex.step() is not None:
+            pass
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        st = eng.stats()
+        eng.close()
+        return wall, st
+
+    serve_once()   # first launches of every kernel and torch op, untimed
+    wall, st = serve_once()
     gen = sum(m for _, _, m in reqs)
     return {"engine_host_us_per_iteration_256_running": round(host_us, 2),
             "serve16": {"iterations": st["iterations"], "preemptions": st["preemptions"],
