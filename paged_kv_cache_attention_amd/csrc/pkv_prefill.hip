@@ -25,6 +25,12 @@
 //     keys; P split into bf16 hi + lo so the product keeps about 16 bits of P
 // Keys at or past the group's last visible position are never used: their V
 // columns are zeroed when staged and their scores masked.
+//
+// Items start longest first (item_of_rank).  With key pieces (piece_tokens
+// > 0, for grids too small to fill the device) an item's keys are cut into
+// pieces from position 0, one workgroup each; the pieces of an item with more
+// than one leave normalised partials and log-sum-exps in a workspace, and
+// prefill_merge_kernel combines them.
 #include <type_traits>
 
 #include "pkv_device.h"
