@@ -26,11 +26,11 @@
 // Keys at or past the group's last visible position are never used: their V
 // columns are zeroed when staged and their scores masked.
 //
-// Items start longest first (item_of_rank).  With key pieces (piece_tokens
-// > 0, for grids too small to fill the device) an item's keys are cut into
-// pieces from position 0, one workgroup each; the pieces of an item with more
-// than one leave normalised partials and log-sum-exps in a workspace, and
-// prefill_merge_kernel combines them.
+// Items start longest first (piece_of_rank).  With key pieces (piece_tokens
+// > 0, for grids too small to fill the device) an item of n steps is cut into
+// ceil(n / piece_steps) pieces of near-equal length, one workgroup each; the
+// pieces of an item with more than one leave normalised partials and
+// log-sum-exps in a workspace, and prefill_merge_kernel combines them.
 #include <type_traits>
 
 #include "pkv_device.h"
@@ -92,78 +92,132 @@ struct PrefillArgs {
   float* part;       // split items' partials: [B][groups][Hkv][pieces] slots of ROWS x (D + 1) floats
 };
 
-// Start order of the work items.  The workgroup of rank p = blockIdx / Hkv
-// takes the item (b, rg) with the p-th largest key count
+// Start order of the work items.  Without key pieces the workgroup of rank
+// p = blockIdx / Hkv takes the item (b, rg) with the p-th largest key count
 //   work(b, rg) = L_b - T + min(T, (rg + 1) * tpg)    (tpg = chunk tokens per row group)
 // (ties: smaller b first), so the longest items start first and never run
 // alone at the end of the grid.  work is strictly increasing in rg, so the
 // number of items of sequence b with work >= w has a closed form, and the
 // item of rank p follows from a binary search on w: a bijection from ranks to
 // items for any lengths.  Wave 0 computes it with the lengths in registers
-// (kOrderMaxB sequences at most; larger batches keep the plain order).
+// (kOrderMaxB sequences at most; larger batches keep the plain order).  Every
+// workgroup pays for this search before its first load, so it avoids
+// cross-lane shuffles (LDS round trips) and integer division.
 constexpr int kOrderMaxB = 512;
 
-__device__ __forceinline__ int count_work_ge(int Lc, int w, int T, int tpg, int groups) {
+// floor(n / d) for 0 <= n < 2^20 and 0 < d, from inv = 1 / d in fp32: the
+// product is within 1/8 of n / d, so at most one step of correction either way.
+__device__ __forceinline__ int div_floor_small(int n, int d, float inv) {
+  int q = (int)((float)n * inv);
+  q -= q * d > n ? 1 : 0;
+  q += (q + 1) * d <= n ? 1 : 0;
+  return q;
+}
+
+// Branch-free: the division runs on x clamped to [1, T] (n < 2^14) and its
+// result is used only where tpg < x <= T.
+__device__ __forceinline__ int count_work_ge(int Lc, int w, int T, int tpg, float inv_tpg, int groups) {
   const int x = w - Lc + T;   // rg counts iff min(T, (rg + 1) tpg) >= x
-  if (x > T) return 0;
-  if (x <= tpg) return groups;
-  return groups + 1 - (x + tpg - 1) / tpg;
+  const int mid = groups + 1 - div_floor_small(min(max(x, 1), T) + tpg - 1, tpg, inv_tpg);
+  return x > T ? 0 : (x <= tpg ? groups : mid);
 }
 
-__device__ __forceinline__ int wave_sum_int(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+// Sum over the wave of values in [0, 2^bits): one ballot per bit.
+__device__ __forceinline__ int wave_sum_bits(int x, int bits) {
+  int s = 0;
+  for (int k = 0; k < bits; ++k) s += __builtin_popcountll(__builtin_amdgcn_ballot_w64((x >> k) & 1)) << k;
+  return s;
 }
 
-// Wave 0 only: the item of rank p, written to item[0] (b) and item[1] (rg).
-__device__ void item_of_rank(const int32_t* lens, int B, int T, int max_tokens, int tpg, int groups, int p,
-                             int lane, int* item) {
-  constexpr int KB = kOrderMaxB / 64;
-  const int nk = (B + 63) / 64;
-  int lc[KB];
-  int lo = max_tokens, hi = 0;
+// Launch order with key pieces.  Workgroups are handed to the XCDs and, in
+// each, to its shader engines in turn, and a full engine holds back the
+// launch of every later workgroup; so a grid whose pieces alternate between
+// heavy and empty would pile the heavy ones onto some engines.  The ranks
+// therefore run: piece 0 of every split item (longest first), then piece 1 of
+// them, piece 2 of those with three or more, and so on; then the unsplit
+// items, longest first; then ranks with no piece.  The split items are the
+// top-ranked ones (work > piece_keys), and the items with more than k pieces
+// are the top count(work > k * piece_keys) ones, so each rank maps to an item
+// rank and a piece with a few counts.
+//
+// Wave 0 only: for launch rank p, writes item[0] = b (or -1: no piece),
+// item[1] = rg, item[2] = L_b clamped to [0, max_tokens], item[3] = piece.
+// NK = 64-sequence chunks of the lengths held per lane (straight-line code
+// for batches of up to 64 sequences).
+template <int NK>
+__device__ __forceinline__ void piece_of_rank(const int32_t* lens, int B, int T, int max_tokens, int tpg, int groups,
+                                              int piece_keys, int pieces, int p, int lane, int* item) {
+  const float inv_tpg = 1.f / (float)tpg;
+  const bool one = B == 1;   // every lane then holds sequence 0, and counts need no sum
+  int lc[NK];
 #pragma unroll
-  for (int k = 0; k < KB; ++k) {
-    lc[k] = 0;
-    if (k < nk) {
-      const int bb = lane + 64 * k;
-      if (bb < B) {
-        lc[k] = clampi(lens[bb], 0, max_tokens);
-        lo = min(lo, lc[k]);
-        hi = max(hi, lc[k]);
-      }
-    }
+  for (int k = 0; k < NK; ++k) {
+    const int bb = one ? 0 : lane + 64 * k;
+    lc[k] = bb < B ? clampi(lens[bb], 0, max_tokens) : 0;
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    lo = min(lo, __shfl_xor(lo, o));
-    hi = max(hi, __shfl_xor(hi, o));
-  }
+  // a lane's count is at most NK * groups
+  const int bits = 32 - __builtin_clz((unsigned)(NK * groups));
   auto total_ge = [&](int w) {
     int c = 0;
 #pragma unroll
-    for (int k = 0; k < KB; ++k)
-      if (k < nk && lane + 64 * k < B) c += count_work_ge(lc[k], w, T, tpg, groups);
-    return wave_sum_int(c);
+    for (int k = 0; k < NK; ++k) {
+      const int ck = count_work_ge(lc[k], w, T, tpg, inv_tpg, groups);
+      c += one || lane + 64 * k < B ? ck : 0;
+    }
+    return one ? c : wave_sum_bits(c, bits);
   };
-  // total_ge(lo) = B * groups > p >= total_ge(hi) = 0
-  lo -= T;
-  hi += 1;
+  // item rank r and piece of launch rank p
+  int r = p, piece = 0;
+  if (piece_keys > 0) {
+    const int split = total_ge(piece_keys + 1);   // items of two or more pieces
+    if (p >= split) {
+      int q = p - split;
+      piece = -1;
+      for (int k = 1; k < pieces; ++k) {
+        const int ck = k == 1 ? split : total_ge(k * piece_keys + 1);   // items of more than k pieces
+        if (q < ck) {
+          r = q;
+          piece = k;
+          break;
+        }
+        q -= ck;
+        if (ck == 0) break;
+      }
+      if (piece < 0) {
+        r = split + q;
+        piece = 0;
+        if (r >= B * groups) {   // past the last piece
+          if (lane == 0) item[0] = -1;
+          return;
+        }
+      }
+    }
+  }
+  if (one) {   // work grows with rg
+    if (lane == 0) {
+      item[0] = 0;
+      item[1] = groups - 1 - r;
+      item[2] = lc[0];
+      item[3] = piece;
+    }
+    return;
+  }
+  // the item of rank r: binary search on its work w,
+  // total_ge(lo) = B * groups > r >= total_ge(hi) = 0
+  int lo = -T, hi = max_tokens + 1;
   while (hi - lo > 1) {
     const int mid = lo + (hi - lo) / 2;
-    if (total_ge(mid) > p) lo = mid;
+    if (total_ge(mid) > r) lo = mid;
     else hi = mid;
   }
   // the item has work lo; o = its rank among the items of that work, which
   // are one per sequence at most, taken in order of b
-  int o = p - total_ge(hi);
+  int o = r - total_ge(hi);
 #pragma unroll
-  for (int k = 0; k < KB; ++k) {
-    if (k >= nk) break;
+  for (int k = 0; k < NK; ++k) {
     const int bb = lane + 64 * k;
-    const int ge = bb < B ? count_work_ge(lc[k], lo, T, tpg, groups) : 0;
-    const bool has = bb < B && ge > count_work_ge(lc[k], hi, T, tpg, groups);
+    const int ge = count_work_ge(lc[k], lo, T, tpg, inv_tpg, groups);
+    const bool has = bb < B && ge > count_work_ge(lc[k], hi, T, tpg, inv_tpg, groups);
     const uint64_t m = __builtin_amdgcn_ballot_w64(has);
     const int n = __builtin_popcountll(m);
     if (o < n) {
@@ -171,6 +225,8 @@ __device__ void item_of_rank(const int32_t* lens, int B, int T, int max_tokens, 
       if (has && below == o) {
         item[0] = bb;
         item[1] = groups - ge;
+        item[2] = lc[k];
+        item[3] = piece;
       }
       break;
     }
@@ -201,41 +257,49 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = a.Hq / a.Hkv;
   const int R = a.T * G;
-  // items longest first (item_of_rank); the KV heads of one piece of an item
-  // are consecutive workgroups, and the pieces of an item follow each other
+  // the KV heads of one piece of an item are consecutive workgroups; pieces
+  // and items in the order of piece_of_rank
   const int max_tokens = a.max_blocks * kBS;
   const int kv = (int)blockIdx.x % a.Hkv;
-  const int piece = ((int)blockIdx.x / a.Hkv) % pa.pieces;
-  const int p = (int)blockIdx.x / a.Hkv / pa.pieces;
-  int b, rg;
-  if (a.B == 1) {
-    b = 0;
-    rg = pa.groups - 1 - p;
-  } else if (a.B > kOrderMaxB) {   // plain order: the last row group of every sequence first
+  int b, rg, L, piece;
+  if (a.B > kOrderMaxB) {   // plain order: the last row group of every sequence first, its pieces together
+    const int q = (int)blockIdx.x / a.Hkv;
+    const int p = q / pa.pieces;
+    piece = q % pa.pieces;
     b = p % a.B;
     rg = pa.groups - 1 - p / a.B;
+    L = clampi(a.context_lens[b], 0, max_tokens);
   } else {
-    __shared__ int sitem[2];
-    if (tid < 64)
-      item_of_rank(a.context_lens, a.B, a.T, max_tokens, PG::ROWS / G, pa.groups, p, tid, sitem);
+    __shared__ int sitem[4];
+    if (tid < 64) {
+      if (a.B <= 64)
+        piece_of_rank<1>(a.context_lens, a.B, a.T, max_tokens, PG::ROWS / G, pa.groups, pa.piece_steps * STEP,
+                         pa.pieces, (int)blockIdx.x / a.Hkv, tid, sitem);
+      else
+        piece_of_rank<kOrderMaxB / 64>(a.context_lens, a.B, a.T, max_tokens, PG::ROWS / G, pa.groups,
+                                       pa.piece_steps * STEP, pa.pieces, (int)blockIdx.x / a.Hkv, tid, sitem);
+    }
     __syncthreads();
     b = sitem[0];
+    if (b < 0) return;   // a rank past the last piece: whole workgroup
     rg = sitem[1];
+    L = sitem[2];
+    piece = sitem[3];
   }
-  const int L = clampi(a.context_lens[b], 0, max_tokens);
   const int r0 = rg * PG::ROWS;
   const int t_last = (min(R, r0 + PG::ROWS) - 1) / G;
   const int kv_len = clampi(L - a.T + t_last + 1, 0, L);   // keys any row of the group sees
   const int nsteps = (kv_len + STEP - 1) / STEP;
   const int nblk = (kv_len + kBS - 1) / kBS;
-  // This workgroup's steps [s0, s1): the whole item, or one piece of
-  // piece_steps steps.  An item of npc > 1 pieces leaves normalised partials.
+  // This workgroup's steps [s0, s1): the whole item, or piece `piece` of
+  // npc = ceil(nsteps / piece_steps) near-equal pieces.  An item of npc > 1
+  // pieces leaves normalised partials.
   int s0 = 0, s1 = nsteps, npc = 1;
   if (pa.piece_steps > 0) {
     npc = max(1, (nsteps + pa.piece_steps - 1) / pa.piece_steps);
     if (piece >= npc) return;   // the item is shorter than this piece: whole workgroup
-    s0 = piece * pa.piece_steps;
-    s1 = min(nsteps, s0 + pa.piece_steps);
+    s0 = piece * nsteps / npc;
+    s1 = (piece + 1) * nsteps / npc;
   }
 
   // ---- this wave's rows: tile j holds rows rw + 16 j + (lane % 16) ----
@@ -484,38 +548,56 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
   }
 
   // ---- epilogue: O / l in bf16 (or, for a piece of a split item, in fp32
-  // to the item's slot), lse in natural log ----
-  if (!wave_active) return;
-  uint16_t* out = static_cast<uint16_t*>(a.out);
+  // to the item's slot), lse in natural log.  bf16 rows are staged in LDS
+  // (free after the loop's last barrier) and leave as 16-byte row chunks:
+  // the rows of one query token are consecutive heads, so the stores cover
+  // contiguous runs of G * D * 2 bytes. ----
+  constexpr int OROW = 2 * D + 16;   // staged row bytes (the 4 rows a quad writes sit 16 banks apart)
+  static_assert(PG::ROWS * OROW <= PG::LDS, "output tile fits the staging buffers");
   float* slot = npc > 1 ? pa.part + ((((size_t)b * pa.groups + rg) * a.Hkv + kv) * pa.pieces + piece) *
                                         (size_t)(PG::ROWS * (D + 1))
                         : nullptr;
+  if (wave_active) {
 #pragma unroll
-  for (int j = 0; j < TPW; ++j) {
-    float l = l_part[j] + __shfl_xor(l_part[j], 16);
-    l += __shfl_xor(l, 32);
+    for (int j = 0; j < TPW; ++j) {
+      float l = l_part[j] + __shfl_xor(l_part[j], 16);
+      l += __shfl_xor(l, 32);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int rr = rw + 16 * j + 4 * quad + k;   // O row held in acc[j][*][k]
-      const float lr = __shfl(l, 4 * quad + k);
-      const float mr = __shfl(m_row[j], 4 * quad + k);
-      if (rr < R) {
+      for (int k = 0; k < 4; ++k) {
+        const int rr = rw + 16 * j + 4 * quad + k;   // O row held in acc[j][*][k]
+        const float lr = __shfl(l, 4 * quad + k);
+        const float mr = __shfl(m_row[j], 4 * quad + k);
         const float inv = lr != 0.f ? 1.f / lr : 0.f;
         const float lse = lr != 0.f ? (mr + log2f(lr)) * kLn2 : kNegInf;
         if (slot) {   // partial of a piece: rows with no visible key here give (0, -inf)
-          float* o = slot + (size_t)(rr - r0) * D;
+          if (rr < R) {
+            float* o = slot + (size_t)(rr - r0) * D;
 #pragma unroll
-          for (int d = 0; d < DT; ++d) o[16 * d + row] = acc[j][d][k] * inv;
-          if (row == 0) slot[PG::ROWS * D + (rr - r0)] = lse;
-        } else {
-          const int t = rr / G, h = kv * G + (rr - (rr / G) * G);
-          const size_t orow = ((size_t)b * a.T + t) * a.Hq + h;
+            for (int d = 0; d < DT; ++d) o[16 * d + row] = acc[j][d][k] * inv;
+            if (row == 0) slot[PG::ROWS * D + (rr - r0)] = lse;
+          }
+        } else {   // rows at or past R are staged but never copied out
+          uint16_t* o = reinterpret_cast<uint16_t*>(lds + (rr - r0) * OROW);
 #pragma unroll
-          for (int d = 0; d < DT; ++d) out[orow * D + 16 * d + row] = f32_to_bf16_rne(acc[j][d][k] * inv);
-          if (row == 0 && a.lse_out) a.lse_out[orow] = lse;
+          for (int d = 0; d < DT; ++d) o[16 * d + row] = f32_to_bf16_rne(acc[j][d][k] * inv);
+          if (rr < R && row == 0 && a.lse_out) {
+            const int t = rr / G;
+            a.lse_out[((size_t)b * a.T + t) * a.Hq + kv * G + (rr - t * G)] = lse;
+          }
         }
       }
     }
+  }
+  if (slot) return;
+  __syncthreads();
+  constexpr int CPR = D / 8;   // 16-byte chunks per row
+  unsigned char* out = static_cast<unsigned char*>(a.out);
+  const int nrows = min(R, r0 + PG::ROWS) - r0;
+  for (int i = tid; i < nrows * CPR; i += kThreads) {
+    const int rl = i / CPR, c = i % CPR;
+    const int r = r0 + rl, t = r / G;
+    const size_t orow = ((size_t)b * a.T + t) * a.Hq + kv * G + (r - t * G);
+    store16(out + orow * (D * 2) + c * 16, *reinterpret_cast<const u32x4_t*>(lds + rl * OROW + c * 16));
   }
 }
 

@@ -182,6 +182,11 @@ PIECE_CASES = [  # (D, Hq, Hkv, T, lens, piece_tokens)
     (128, 16, 8, 37, [37, 38, 500], 160),               # some items in one piece, written directly
     (64, 32, 4, 17, [17, 40, 1000], 32),                # G = 8
     (128, 32, 8, 1, [1, 30, 300], 64),                  # T = 1: one row group, decode rows in pieces
+    # grids of several waves of workgroups, pieces of mixed-length items ranked
+    # ahead of the unsplit items: 40 and 70 sequences (the latter past 64, the
+    # lengths in more than one register per lane)
+    (128, 32, 8, 64, [64 + (i * 37) % 637 for i in range(40)], 64),
+    (64, 16, 8, 8, [8 + (i * 53) % 300 for i in range(70)], 32),
 ]
 
 
