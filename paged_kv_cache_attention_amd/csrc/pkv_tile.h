@@ -34,6 +34,24 @@ __device__ __forceinline__ bf16x8_v as_bf16x8(u32x4_t v) {
 }
 __device__ __forceinline__ uint32_t pack_bf16(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
 
+// B operand of v_mfma_f32_16x16x16bf16_1k for column tile d of V (lane
+// (row, quad) gets V[4 quad + k][16 d + row], k = 0..3) from a row-major LDS
+// tile of 16 tokens, ROW bytes apart, with one ds_read_b64_tr_b16.  That
+// read works on groups of 16 lanes: lane i of a group receives element i % 4
+// of the 8-byte chunk addressed by lane 4 k + i / 4 of the group, for
+// k = 0..3 (measured on gfx950 with an index-coded LDS tile).  So lane j of
+// group quad addresses token 4 quad + j / 4, columns 16 d + 4 (j % 4) .. +3.
+typedef short i16x4_v __attribute__((ext_vector_type(4)));
+template <int ROW>
+__device__ __forceinline__ bf16x4_v vt_operand(const unsigned char* tile, int d, int row, int quad) {
+  const unsigned char* p = tile + (4 * quad + (row >> 2)) * ROW + (16 * d + 4 * (row & 3)) * 2;
+  const i16x4_v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_v*)(const_cast<unsigned char*>(p)));
+  bf16x4_v v;
+  __builtin_memcpy(&v, &r, 8);
+  return v;
+}
+
 template <int D>
 struct State {
   floatx4_t acc[D / 16];   // O rows 4*(lane/16) + k, column 16*d + lane%16
@@ -137,16 +155,9 @@ __device__ __forceinline__ void run(State<D>& st, const u32x4_t (&qreg)[D / 32],
       __builtin_memcpy(&plo, l2, 8);
     }
     __asm__ volatile("" ::: "memory");
-    const uint16_t* vt16 = reinterpret_cast<const uint16_t*>(vtile);
 #pragma unroll
     for (int d = 0; d < DT; ++d) {
-      const int col = 16 * d + row;
-      uint16_t vv[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) vv[k] = vt16[((4 * quad + k) * kVRow) / 2 + col];
-      bf16x4_v bv;
-      const uint32_t v2[2] = {pack_bf16(vv[0], vv[1]), pack_bf16(vv[2], vv[3])};
-      __builtin_memcpy(&bv, v2, 8);
+      const bf16x4_v bv = vt_operand<kVRow>(vtile, d, row, quad);
       st.acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, st.acc[d], 0, 0, 0);
       st.acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, st.acc[d], 0, 0, 0);
     }
@@ -226,16 +237,9 @@ __device__ __forceinline__ void run_lds(State<D>& st, const u32x4_t (&qreg)[D / 
       __builtin_memcpy(&phi, h2, 8);
       __builtin_memcpy(&plo, l2, 8);
     }
-    const uint16_t* vt16 = reinterpret_cast<const uint16_t*>(vs + j * kBS * ROW);
 #pragma unroll
     for (int d = 0; d < DT; ++d) {
-      const int col = 16 * d + row;
-      uint16_t vv[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) vv[k] = vt16[((4 * quad + k) * ROW) / 2 + col];
-      bf16x4_v bv;
-      const uint32_t v2[2] = {pack_bf16(vv[0], vv[1]), pack_bf16(vv[2], vv[3])};
-      __builtin_memcpy(&bv, v2, 8);
+      const bf16x4_v bv = vt_operand<ROW>(vs + j * kBS * ROW, d, row, quad);
       st.acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, st.acc[d], 0, 0, 0);
       st.acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, st.acc[d], 0, 0, 0);
     }
