@@ -17,7 +17,8 @@
 // tiles work on the current one), with the item's block-table entries cached
 // in LDS 512 at a time:
 //   K[token][d]  row-major, padded rows        -> A operand of S^T = K Q^T
-//   V^T[d][token] transposed when staged        -> B operand of O += P V
+//   V[token][d]  row-major, padded rows, read back transposed (gfx950
+//                ds_read_b64_tr_b16)            -> B operand of O += P V
 // Per wave and step, for each row tile:
 //   S^T[token][row] = K . Q^T   v_mfma_f32_16x16x32_bf16, two 16-token halves
 //   online softmax per row (base 2, running max raised lazily)
@@ -48,7 +49,7 @@ constexpr float kSlack = 8.f;
 typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
 typedef float f32x2_v __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8_v as_bf16x8(u32x4_t v) {
   bf16x8_v r;
@@ -71,9 +72,10 @@ struct PGeo {
   static constexpr int NQ = STEP / 16;               // 16-key quarters per step (S^T tiles)
   static constexpr int NK = STEP / 32;               // 32-key MFMA k-chunks per step (P.V)
   static constexpr int KROW = 2 * D + 16;            // K row bytes (conflict-free 16-byte reads)
-  static constexpr int VROW = 2 * STEP + 8;          // V^T row bytes: one d, STEP keys
+  static constexpr int VROW = 2 * D + 32;            // V row bytes (token-major; the transposing reads of
+                                                     // 4 rows x 4 8-byte chunks hit 32 distinct banks)
   static constexpr int KBYTES = STEP * KROW;
-  static constexpr int VBYTES = D * VROW;
+  static constexpr int VBYTES = STEP * VROW;
   static constexpr int LDS = 2 * (KBYTES + VBYTES);
   static constexpr int RC = D * 2 / 16;              // 16-byte chunks per token row
   static constexpr int PER_T = STEP * RC / kThreads;  // staged chunks per thread (K, and again V)
@@ -338,11 +340,10 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
     l_part[j] = 0.f;
   }
 
-  // ---- staging: chunk i = tid + k * kThreads.  K: key i / RC, columns
-  // 8 (i % RC) .. +7 (a row's chunks on consecutive lanes: coalesced, and the
-  // rows land as 16-byte LDS writes).  V: key i % STEP, columns 8 (i / STEP)
-  // .. +7 (consecutive lanes on consecutive keys, so each 16-bit write of the
-  // transpose covers one contiguous run of V^T: few bank conflicts). ----
+  // ---- staging: chunk i = tid + k * kThreads is key i / RC, columns
+  // 8 (i % RC) .. +7, for K and V alike (a row's chunks on consecutive
+  // lanes: coalesced, and the rows land as 16-byte LDS writes).  V is read
+  // back transposed by the P.V products. ----
   const size_t kv_row_bytes = (size_t)a.Hkv * D * 2;
   const size_t block_bytes = (size_t)kBS * kv_row_bytes;
   const int nmax = a.N_blocks - 1;
@@ -362,44 +363,36 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
   // to the step's first block) and its byte offset inside a physical block;
   // only the physical id changes from step to step.
   constexpr int NB = STEP / kBS;                      // blocks per step
-  int kblk[PER_T], vblk[PER_T];
-  uint32_t koff[PER_T], voff[PER_T];
+  int kblk[PER_T];
+  uint32_t koff[PER_T];
 #pragma unroll
   for (int k = 0; k < PER_T; ++k) {
     const int i = tid + k * kThreads;
-    const int key = i / RC, vkey = i % STEP;
+    const int key = i / RC;
     kblk[k] = key / kBS;
-    vblk[k] = vkey / kBS;
     koff[k] = (uint32_t)((key % kBS) * kv_row_bytes + (i % RC) * 16);
-    voff[k] = (uint32_t)((vkey % kBS) * kv_row_bytes + (i / STEP) * 16);
   }
   u32x4_t kreg[PER_T], vreg[PER_T];
   auto issue = [&](int s) {
     const int b0 = s * NB;
 #pragma unroll
     for (int k = 0; k < PER_T; ++k) {
-      const uint32_t kph = (uint32_t)stbl[(uint32_t)min(b0 + kblk[k], nblk - 1) % kTblWin];
-      const uint32_t vph = (uint32_t)stbl[(uint32_t)min(b0 + vblk[k], nblk - 1) % kTblWin];
-      kreg[k] = load16(kpool + (uint64_t)kph * block_bytes + koff[k]);
-      vreg[k] = load16(vpool + (uint64_t)vph * block_bytes + voff[k]);
+      const uint32_t ph = (uint32_t)stbl[(uint32_t)min(b0 + kblk[k], nblk - 1) % kTblWin];
+      kreg[k] = load16(kpool + (uint64_t)ph * block_bytes + koff[k]);
+      vreg[k] = load16(vpool + (uint64_t)ph * block_bytes + koff[k]);
     }
   };
   auto commit = [&](int s, int buf) {
     if ((s + 1) * STEP > kv_len) {   // the step holds keys past the group's last visible one:
 #pragma unroll                      // they may hold anything, so zero their V
       for (int k = 0; k < PER_T; ++k)
-        if (s * STEP + (tid + k * kThreads) % STEP >= kv_len) vreg[k] = u32x4_t{0u, 0u, 0u, 0u};
+        if (s * STEP + (tid + k * kThreads) / RC >= kv_len) vreg[k] = u32x4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int k = 0; k < PER_T; ++k) {
       const int i = tid + k * kThreads;
       store16(kst(buf) + (i / RC) * PG::KROW + (i % RC) * 16, kreg[k]);
-      const int vkey = i % STEP, vc = i / STEP;
-      const u32x4_t v = vreg[k];
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-      uint16_t* vt = reinterpret_cast<uint16_t*>(vst(buf) + (8 * vc) * PG::VROW) + vkey;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vt[e * (PG::VROW / 2)] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+      store16(vst(buf) + (i / RC) * PG::VROW + (i % RC) * 16, vreg[k]);
     }
   };
 
@@ -437,10 +430,19 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
     for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
       for (int d = 0; d < DT; ++d) {
-        const unsigned char* vr = vs + (16 * d + row) * PG::VROW + 64 * kk + quad * 8;
-        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vr);
-        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vr + 32);
-        vb[kk][d] = as_bf16x8(u32x4_t{lo.x, lo.y, hi.x, hi.y});
+        // keys 32 kk + 4 quad .. +3, then 16 keys further, for column
+        // 16 d + row: two transposing reads (ds_read_b64_tr_b16: lane i of
+        // each 16-lane group receives element i % 4 of the 8-byte chunk that
+        // lane 4 k + i / 4 of the group addresses, k = 0..3)
+        const unsigned char* vr = vs + (32 * kk + 4 * quad + (row >> 2)) * PG::VROW + (16 * d + 4 * (row & 3)) * 2;
+        const i16x4_v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_v*)(const_cast<unsigned char*>(vr)));
+        const i16x4_v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_v*)(const_cast<unsigned char*>(vr + 16 * PG::VROW)));
+        u32x4_t w;
+        __builtin_memcpy(&w, &lo, 8);
+        __builtin_memcpy(reinterpret_cast<unsigned char*>(&w) + 8, &hi, 8);
+        vb[kk][d] = as_bf16x8(w);
       }
     __builtin_amdgcn_sched_barrier(0);
     // softmax.  Score i of the lane (i = 4 h + k) is key 16 h + 4 quad + k of
