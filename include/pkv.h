@@ -14,6 +14,9 @@
  *  - Every array argument is a DEVICE pointer to dense, row-major memory
  *    owned by the caller.  The library never allocates, frees or keeps any
  *    caller memory.  Scalars are passed by value.
+ *  - q, out, k_pool, v_pool, k_new, v_new and the gather outputs are read
+ *    and written with 16-byte vector accesses: each must be 16-byte aligned
+ *    (device allocations are), else the call returns PKV_EINVAL.
  *  - Layouts (element type given by `dtype`):
  *      q, out         [B, T, Hq, D]
  *      k_pool, v_pool [N_blocks, block_size, Hkv, D]

@@ -2,9 +2,11 @@
 // The contract of every entry point is documented in include/pkv.h.
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <string>
 
@@ -86,6 +88,14 @@ int partitions_max(int max_blocks, int block_size, int partition_size) {
 
 }  // namespace
 
+// K/V rows, queries and outputs move with 16-byte vector loads and stores.
+static bool all_aligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p && (reinterpret_cast<uintptr_t>(p) & 15)) return false;
+  return true;
+}
+static pkv_status misaligned() { return fail(PKV_EINVAL, "tensor arguments must be 16-byte aligned"); }
+
 extern "C" {
 
 const char* pkv_last_error(void) { return g_last_error.c_str(); }
@@ -124,6 +134,7 @@ pkv_status paged_kv_append(const void* k_new, const void* v_new, void* k_pool, v
   if (B == 0) return PKV_OK;
   if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !context_lens_pre)
     return fail(PKV_EINVAL, "null pointer argument");
+  if (!all_aligned16({k_new, v_new, k_pool, v_pool})) return misaligned();
   if ((long long)B * T > (1LL << 30)) return fail(PKV_EINVAL, "B*T too large");
   hipStream_t s = static_cast<hipStream_t>(stream);
   // The append targets positions lens_pre .. lens_pre+T-1: check them as a context of lens_pre+T.
@@ -148,6 +159,7 @@ pkv_status paged_kv_append_rope(void* q, int Hq, const void* k_new, const void* 
   if (B == 0) return PKV_OK;
   if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !context_lens_pre)
     return fail(PKV_EINVAL, "null pointer argument");
+  if (!all_aligned16({q, k_new, v_new, k_pool, v_pool})) return misaligned();
   if ((long long)B * T > (1LL << 30)) return fail(PKV_EINVAL, "B*T too large");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (debug_enabled() &&
@@ -167,6 +179,7 @@ pkv_status paged_kv_copy_blocks(void* k_pool, void* v_pool, const int32_t* src, 
   if ((st = check_pool_shape(Hkv, D, block_size, 1, N_blocks)) != PKV_OK) return st;
   if (n == 0) return PKV_OK;
   if (!k_pool || !v_pool || !src || !dst) return fail(PKV_EINVAL, "null pointer argument");
+  if (!all_aligned16({k_pool, v_pool})) return misaligned();
   return from_hip(pkv::launch_copy_blocks(k_pool, v_pool, src, dst, n, Hkv, D, block_size, N_blocks, elem_bytes(dtype),
                                           static_cast<hipStream_t>(stream)),
                   "paged_kv_copy_blocks launch");
@@ -182,6 +195,7 @@ pkv_status paged_kv_gather(const void* k_pool, const void* v_pool, const int32_t
   if (B == 0 || max_len == 0) return PKV_OK;
   if (!k_pool || !v_pool || !block_tables || !context_lens || !k_out || !v_out)
     return fail(PKV_EINVAL, "null pointer argument");
+  if (!all_aligned16({k_pool, v_pool, k_out, v_out})) return misaligned();
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (debug_enabled() && (st = debug_validate(block_tables, context_lens, B, 0, 0, block_size, max_blocks, N_blocks, s)) !=
                              PKV_OK)
@@ -211,6 +225,7 @@ pkv_status paged_attention_decode(const void* q, const void* k_pool, const void*
     return fail(PKV_EINVAL, "partition_size must be 0 or a positive multiple of block_size");
   if (B == 0) return PKV_OK;
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out) return fail(PKV_EINVAL, "null pointer argument");
+  if (!all_aligned16({q, k_pool, v_pool, out})) return misaligned();
   if (out == q || out == k_pool || out == v_pool) return fail(PKV_EINVAL, "out must not alias an input");
 
   pkv::DecodeArgs a{};
@@ -267,6 +282,7 @@ pkv_status paged_attention_prefill(const void* q, const void* k_pool, const void
                 pkv::kPrefillStep);
   if (B == 0) return PKV_OK;
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out) return fail(PKV_EINVAL, "null pointer argument");
+  if (!all_aligned16({q, k_pool, v_pool, out})) return misaligned();
   if (out == q || out == k_pool || out == v_pool) return fail(PKV_EINVAL, "out must not alias an input");
   if ((long long)B * T * Hq > (1LL << 30)) return fail(PKV_EINVAL, "B*T*Hq too large");
   const size_t need = pkv::prefill_workspace_bytes(B, T, Hq, Hkv, D, max_blocks, piece_tokens);

@@ -175,3 +175,20 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(pkv, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         pkv.load_library(tmp_path / "missing.so")
+
+
+def test_misaligned_tensors_rejected():
+    """Rows move with 16-byte vector accesses: a tensor argument that is not
+    16-byte aligned is an argument error, reported before any launch."""
+    lib = pkv.load_library()
+    odd = ctypes.c_void_p(4096 * 9 + 8)
+    st, msg = _decode(q=odd)
+    assert st == pkv.PKV_EINVAL and "16-byte" in msg
+    st, msg = _decode(out=odd)
+    assert st == pkv.PKV_EINVAL and "16-byte" in msg
+    st, msg = _prefill(k=odd)
+    assert st == pkv.PKV_EINVAL and "16-byte" in msg
+    assert lib.paged_kv_append(odd, P, P, P, P, P, 2, 1, 8, 64, 16, 4, 8, pkv.PKV_BF16, None) == pkv.PKV_EINVAL
+    assert lib.paged_kv_copy_blocks(P, odd, P, P, 1, 8, 64, 16, 8, pkv.PKV_BF16, None) == pkv.PKV_EINVAL
+    assert lib.paged_kv_gather(P, P, P, P, odd, P, 2, 64, 8, 64, 16, 4, 8, pkv.PKV_BF16, None) == pkv.PKV_EINVAL
+    assert "16-byte" in lib.pkv_last_error().decode()
