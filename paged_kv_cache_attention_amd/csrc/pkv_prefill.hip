@@ -12,13 +12,13 @@
 // Work item = (row group, sequence, KV head); rows are r = t * G + g
 // (G = Hq/Hkv).  A workgroup of kWaves waves owns one item; each wave holds
 // TPW 16-row MFMA tiles (two in the shipped configuration: 128 rows per item).
-// Keys advance STEP (32) at a time, staged once per workgroup through LDS
-// (double-buffered: the next step's global loads are in flight while the
-// tiles work on the current one), with the item's block-table entries cached
-// in LDS 512 at a time:
-//   K[token][d]  row-major, padded rows        -> A operand of S^T = K Q^T
-//   V[token][d]  row-major, padded rows, read back transposed (gfx950
-//                ds_read_b64_tr_b16)            -> B operand of O += P V
+// Keys advance STEP (32) at a time, loaded straight into LDS once per
+// workgroup (global_load_lds_dwordx4, double-buffered: the next step's loads
+// are in flight while the tiles work on the current one), with the item's
+// block-table entries cached in LDS 512 at a time:
+//   K[token][d]  row-major, chunks XOR-swizzled by row -> A operand of S^T = K Q^T
+//   V[token][d]  row-major, chunks XOR-swizzled by row, read back transposed
+//                (gfx950 ds_read_b64_tr_b16)          -> B operand of O += P V
 // Per wave and step, for each row tile:
 //   S^T[token][row] = K . Q^T   v_mfma_f32_16x16x32_bf16, two 16-token halves
 //   online softmax per row (base 2, running max raised lazily)
@@ -45,6 +45,14 @@ constexpr int kTblWin = 512;   // block-table entries cached in LDS at a time
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kSlack = 8.f;
+// K/V steps staged in LDS at once: loads run kStages - 1 steps ahead of the
+// tiles (straight into LDS, so deeper staging costs no registers).  Three
+// stages measured slower than two on the Llama-3-8B-shaped chunked batch
+// (235.3 against 222.6 us) and on one long prompt (123.0 against 117.7 us).
+#ifndef PKV_PREFILL_STAGES
+#define PKV_PREFILL_STAGES 2
+#endif
+constexpr int kStages = PKV_PREFILL_STAGES;
 
 typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
@@ -55,6 +63,12 @@ __device__ __forceinline__ bf16x8_v as_bf16x8(u32x4_t v) {
   bf16x8_v r;
   __builtin_memcpy(&r, &v, sizeof(r));
   return r;
+}
+
+// 16 bytes from global memory straight to LDS (global_load_lds_dwordx4):
+// lane l of the wave writes lds_run + 16 l, lds_run being wave-uniform.
+__device__ __forceinline__ void load_lds16(const void* g, unsigned char* lds_run) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_run, 16, 0, 0);
 }
 
 // Two floats to packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
@@ -71,15 +85,23 @@ struct PGeo {
   static constexpr int ROWS = 16 * TPW * kWaves;     // query rows per item
   static constexpr int NQ = STEP / 16;               // 16-key quarters per step (S^T tiles)
   static constexpr int NK = STEP / 32;               // 32-key MFMA k-chunks per step (P.V)
-  static constexpr int KROW = 2 * D + 16;            // K row bytes (conflict-free 16-byte reads)
-  static constexpr int VROW = 2 * D + 32;            // V row bytes (token-major; the transposing reads of
-                                                     // 4 rows x 4 8-byte chunks hit 32 distinct banks)
-  static constexpr int KBYTES = STEP * KROW;
-  static constexpr int VBYTES = STEP * VROW;
-  static constexpr int LDS = 2 * (KBYTES + VBYTES);
+  static constexpr int ROWB = 2 * D;                 // staged K or V row bytes (unpadded: loads land
+                                                     // in LDS as whole 1 KB runs per wave)
+  static constexpr int KBYTES = STEP * ROWB;
+  static constexpr int VBYTES = STEP * ROWB;
+  static constexpr int OROW = 2 * D + 16;            // epilogue row bytes (the 4 rows a quad writes sit 16
+                                                     // banks apart)
+  static constexpr int LDS = kStages * (KBYTES + VBYTES) > ROWS * OROW ? kStages * (KBYTES + VBYTES) : ROWS * OROW;
   static constexpr int RC = D * 2 / 16;              // 16-byte chunks per token row
   static constexpr int PER_T = STEP * RC / kThreads;  // staged chunks per thread (K, and again V)
   static_assert(PER_T * kThreads == STEP * RC, "even staging split");
+  // Chunk c of staged row r sits in slot c ^ swz(r) of the row (an XOR
+  // swizzle instead of padding).  K: the 16 rows a 16-lane group reads at one
+  // chunk fall on 16 distinct 4-bank slots.  V: the 4 rows x 2 chunks of one
+  // transposing read of a 16-lane group fall on 8 distinct slots.  At D = 64
+  // a row is half the 64 banks, so its parity picks the half.
+  static __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  static __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 2 * (r & 3) : 2 * ((r >> 1) & 1); }
 };
 
 static_assert(PGeo<64, kPrefillTPW, kPrefillStep>::ROWS == kPrefillRows &&
@@ -252,7 +274,7 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[PG::LDS];
   __shared__ int stbl[kTblWin];   // physical ids of blocks [win * kTblWin, (win + 1) * kTblWin)
   auto kst = [&](int buf) { return lds + buf * PG::KBYTES; };
-  auto vst = [&](int buf) { return lds + 2 * PG::KBYTES + buf * PG::VBYTES; };
+  auto vst = [&](int buf) { return lds + kStages * PG::KBYTES + buf * PG::VBYTES; };
 
   const DecodeArgs& a = pa.a;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -340,10 +362,12 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
     l_part[j] = 0.f;
   }
 
-  // ---- staging: chunk i = tid + k * kThreads is key i / RC, columns
-  // 8 (i % RC) .. +7, for K and V alike (a row's chunks on consecutive
-  // lanes: coalesced, and the rows land as 16-byte LDS writes).  V is read
-  // back transposed by the P.V products. ----
+  // ---- staging: straight from global memory into LDS
+  // (global_load_lds_dwordx4: lane l of a wave writes bytes 16 l .. 16 l + 15
+  // of the instruction's 1 KB run).  Tile position i = tid + k * kThreads is
+  // row i / RC, slot i % RC; the lane loads the chunk that belongs there
+  // (chunk = slot ^ swizzle(row)): columns 8 chunk .. +7 of that key.  V is
+  // read back transposed by the P.V products. ----
   const size_t kv_row_bytes = (size_t)a.Hkv * D * 2;
   const size_t block_bytes = (size_t)kBS * kv_row_bytes;
   const int nmax = a.N_blocks - 1;
@@ -364,35 +388,38 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
   // only the physical id changes from step to step.
   constexpr int NB = STEP / kBS;                      // blocks per step
   int kblk[PER_T];
-  uint32_t koff[PER_T];
+  uint32_t koff[PER_T], voff[PER_T];
 #pragma unroll
   for (int k = 0; k < PER_T; ++k) {
     const int i = tid + k * kThreads;
-    const int key = i / RC;
+    const int key = i / RC, slot = i % RC;
     kblk[k] = key / kBS;
-    koff[k] = (uint32_t)((key % kBS) * kv_row_bytes + (i % RC) * 16);
+    koff[k] = (uint32_t)((key % kBS) * kv_row_bytes + (slot ^ PG::swz_k(key)) * 16);
+    voff[k] = (uint32_t)((key % kBS) * kv_row_bytes + (slot ^ PG::swz_v(key)) * 16);
   }
-  u32x4_t kreg[PER_T], vreg[PER_T];
-  auto issue = [&](int s) {
+  auto issue = [&](int s, int buf) {
     const int b0 = s * NB;
 #pragma unroll
     for (int k = 0; k < PER_T; ++k) {
       const uint32_t ph = (uint32_t)stbl[(uint32_t)min(b0 + kblk[k], nblk - 1) % kTblWin];
-      kreg[k] = load16(kpool + (uint64_t)ph * block_bytes + koff[k]);
-      vreg[k] = load16(vpool + (uint64_t)ph * block_bytes + koff[k]);
+      const int run = (k * kThreads + 64 * wave) * 16;   // this wave's 1 KB run of the tile
+      load_lds16(kpool + (uint64_t)ph * block_bytes + koff[k], kst(buf) + run);
+      load_lds16(vpool + (uint64_t)ph * block_bytes + voff[k], vst(buf) + run);
     }
   };
-  auto commit = [&](int s, int buf) {
+  // After this the step's K and V are in LDS as far as this wave's loads go
+  // (the barrier that follows covers the other waves).  `later`: steps whose
+  // loads were issued after this one's (1 or 0 with three stages): their
+  // 2 * PER_T loads may stay in flight (vmcnt counts in issue order).
+  auto land = [&](int s, int buf, int later) {
+    if (later > 0) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * PER_T));   // vmcnt <= 2 PER_T; no exp/lgkm wait
+    else __builtin_amdgcn_s_waitcnt(0);
     if ((s + 1) * STEP > kv_len) {   // the step holds keys past the group's last visible one:
-#pragma unroll                      // they may hold anything, so zero their V
-      for (int k = 0; k < PER_T; ++k)
-        if (s * STEP + (tid + k * kThreads) / RC >= kv_len) vreg[k] = u32x4_t{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int k = 0; k < PER_T; ++k) {
-      const int i = tid + k * kThreads;
-      store16(kst(buf) + (i / RC) * PG::KROW + (i % RC) * 16, kreg[k]);
-      store16(vst(buf) + (i / RC) * PG::VROW + (i % RC) * 16, vreg[k]);
+#pragma unroll                      // they may hold anything, so zero their V (each lane its own chunk)
+      for (int k = 0; k < PER_T; ++k) {
+        const int i = tid + k * kThreads;
+        if (s * STEP + i / RC >= kv_len) store16(vst(buf) + i * 16, u32x4_t{0u, 0u, 0u, 0u});
+      }
     }
   };
 
@@ -414,7 +441,8 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
     for (int h = 0; h < NQ; ++h)
 #pragma unroll
       for (int c = 0; c < KS; ++c)
-        kc[h][c] = *reinterpret_cast<const u32x4_t*>(ks + (16 * h + row) * PG::KROW + quad * 16 + c * 64);
+        kc[h][c] = *reinterpret_cast<const u32x4_t*>(ks + (16 * h + row) * PG::ROWB +
+                                                     ((quad + 4 * c) ^ PG::swz_k(16 * h + row)) * 16);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < KS; ++c)
@@ -434,11 +462,13 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
         // 16 d + row: two transposing reads (ds_read_b64_tr_b16: lane i of
         // each 16-lane group receives element i % 4 of the 8-byte chunk that
         // lane 4 k + i / 4 of the group addresses, k = 0..3)
-        const unsigned char* vr = vs + (32 * kk + 4 * quad + (row >> 2)) * PG::VROW + (16 * d + 4 * (row & 3)) * 2;
+        const int vrow = 32 * kk + 4 * quad + (row >> 2);
+        const unsigned char* vr = vs + vrow * PG::ROWB + (((2 * d + ((row & 3) >> 1)) ^ PG::swz_v(vrow)) * 16) +
+                                  8 * (row & 1);
         const i16x4_v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) i16x4_v*)(const_cast<unsigned char*>(vr)));
         const i16x4_v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4_v*)(const_cast<unsigned char*>(vr + 16 * PG::VROW)));
+            (__attribute__((address_space(3))) i16x4_v*)(const_cast<unsigned char*>(vr + 16 * PG::ROWB)));
         u32x4_t w;
         __builtin_memcpy(&w, &lo, 8);
         __builtin_memcpy(reinterpret_cast<unsigned char*>(&w) + 8, &hi, 8);
@@ -523,21 +553,29 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
 
   constexpr int kStepsPerWin = kTblWin * kBS / STEP;
   if (s1 > s0) {
-    load_window(s0 / kStepsPerWin);
-    __syncthreads();
-    issue(s0);
-    commit(s0, s0 & 1);
-    __syncthreads();
-    auto step = [&](int s, auto masked_tag) {
-      const int buf = s & 1;
-      if (s + 1 < s1 && (s + 1) % kStepsPerWin == 0) {   // step s + 1 opens a new table window
+    static_assert(kStages == 2 || kStages == 3, "two or three staged steps");
+    static_assert(2 * PER_T < 16, "pending loads fit vmcnt's low bits");
+    // Loads of step sa start kStages - 1 steps before it is computed.  A step
+    // that opens a new table window reloads it first (every load of earlier
+    // steps has its address by then).
+    auto start = [&](int sa) {
+      if (sa > s0 && sa % kStepsPerWin == 0) {
         __syncthreads();
-        load_window((s + 1) / kStepsPerWin);
+        load_window(sa / kStepsPerWin);
         __syncthreads();
       }
-      if (s + 1 < s1) issue(s + 1);
+      issue(sa, sa % kStages);
+    };
+    load_window(s0 / kStepsPerWin);
+    __syncthreads();
+    for (int q = 0; q < kStages - 1 && s0 + q < s1; ++q) start(s0 + q);
+    land(s0, s0 % kStages, min(kStages - 2, s1 - 1 - s0));
+    __syncthreads();
+    auto step = [&](int s, auto masked_tag) {
+      const int buf = s % kStages;
+      if (s + kStages - 1 < s1) start(s + kStages - 1);
       if (wave_active) compute(s, buf, masked_tag);
-      if (s + 1 < s1) commit(s + 1, buf ^ 1);
+      if (s + 1 < s1) land(s + 1, (s + 1) % kStages, min(kStages - 2, s1 - 2 - s));
       __syncthreads();
     };
     // Steps before s_mask hold only keys every row of the wave sees; the
@@ -554,7 +592,7 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
   // (free after the loop's last barrier) and leave as 16-byte row chunks:
   // the rows of one query token are consecutive heads, so the stores cover
   // contiguous runs of G * D * 2 bytes. ----
-  constexpr int OROW = 2 * D + 16;   // staged row bytes (the 4 rows a quad writes sit 16 banks apart)
+  constexpr int OROW = PG::OROW;
   static_assert(PG::ROWS * OROW <= PG::LDS, "output tile fits the staging buffers");
   float* slot = npc > 1 ? pa.part + ((((size_t)b * pa.groups + rg) * a.Hkv + kv) * pa.pieces + piece) *
                                         (size_t)(PG::ROWS * (D + 1))
