@@ -10,9 +10,11 @@
 //   online softmax per row (running max in base-2 units, raised lazily)
 //   O[row][d] += P[row][token] . V[token][d]       v_mfma_f32_16x16x16_bf16
 //     A = P in exactly the S^T layout, split into bf16 hi + lo parts so the
-//     product keeps about 16 bits of P; B = V transposed through a padded
-//     LDS tile (272-byte rows: writes and reads are bank-conflict free).
-// K and V of the next PD blocks are in flight while a block is processed.
+//     product keeps about 16 bits of P; B = V, loaded straight into an LDS
+//     tile of the wave (global_load_lds_dwordx4, rows XOR-swizzled) and read
+//     back transposed (ds_read_b64_tr_b16).
+// K and V of the next PD blocks are in flight while a block is processed
+// (K in registers, V in PD + 1 LDS tiles per wave).
 #pragma once
 
 #include "pkv_device.h"
@@ -21,7 +23,9 @@ namespace pkv {
 namespace tile {
 
 constexpr int kBS = 16;
-constexpr int kVRow = 272;   // padded LDS row (bytes) of a staged token: conflict-free for D <= 128
+// LDS bytes of the V tiles of one wave in run<D, PD>.
+template <int D, int PD>
+constexpr int run_tile_bytes() { return (PD + 1) * kBS * 2 * D; }
 constexpr float kSlack = 8.f;
 
 typedef __bf16 bf16x4_v __attribute__((ext_vector_type(4)));
@@ -50,6 +54,38 @@ __device__ __forceinline__ bf16x4_v vt_operand(const unsigned char* tile, int d,
   bf16x4_v v;
   __builtin_memcpy(&v, &r, 8);
   return v;
+}
+
+// V tiles of run<D, PD>: 16 unpadded token rows of 2 D bytes, 16-byte chunk c
+// of row r in slot c ^ vswz(r), so that the 4 rows x 2 chunks of one
+// transposing read of a 16-lane group sit on 8 distinct 4-bank slots (at
+// D = 64 a row covers half the banks and its parity picks the half).
+template <int D>
+__device__ __forceinline__ int vswz(int r) { return D == 128 ? 2 * (r & 3) : 2 * ((r >> 1) & 1); }
+
+template <int D>
+__device__ __forceinline__ bf16x4_v vt_operand_swz(const unsigned char* tile, int d, int row, int quad) {
+  const int r = 4 * quad + (row >> 2);
+  const unsigned char* p = tile + r * (2 * D) + (((2 * d + ((row & 3) >> 1)) ^ vswz<D>(r)) * 16) + 8 * (row & 1);
+  const i16x4_v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_v*)(const_cast<unsigned char*>(p)));
+  bf16x4_v v;
+  __builtin_memcpy(&v, &x, 8);
+  return v;
+}
+
+// 16 bytes from global memory straight to LDS (global_load_lds_dwordx4):
+// lane l of the wave writes lds_run + 16 l, lds_run being wave-uniform.
+__device__ __forceinline__ void load_lds16(const void* g, unsigned char* lds_run) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_run, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) (no wait on the other counters): N of the wave's latest
+// memory loads may still be in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | 0x0F70 | (N & 15));
 }
 
 template <int D>
@@ -87,14 +123,32 @@ __device__ __forceinline__ void load_q(u32x4_t (&qreg)[D / 32], const uint16_t* 
 template <int D, int PD>
 __device__ __forceinline__ void run(State<D>& st, const u32x4_t (&qreg)[D / 32], int hi_row, int vlimit,
                                     const int32_t* trow, int kb0, int nb, int nmax, const unsigned char* kpool,
-                                    const unsigned char* vpool, size_t block_bytes, unsigned char* vtile,
-                                    float scale_log2e, int lane) {
+                                    const unsigned char* vhead, size_t kv_row_bytes, size_t block_bytes,
+                                    unsigned char* vtiles, float scale_log2e, int lane) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
+  constexpr int TILE = kBS * 2 * D;
   const int row = lane & 15, quad = lane >> 4;
   hi_row = min(hi_row, (kb0 + nb) * kBS);   // pad steps past the range stay masked
-  u32x4_t kbuf[PD][KS], vbuf[PD][KS];
+  u32x4_t kbuf[PD][KS];
   int tbl = 0, cn = 0;
+  // V load c of a block: lane -> tile byte 1024 c + 16 lane = token row vr[c],
+  // slot (chunk ^ vswz(row)); voff: that chunk's offset in a physical block
+  int vr[KS];
+  uint32_t voff[KS];
+#pragma unroll
+  for (int c = 0; c < KS; ++c) {
+    const int pos = 1024 * c + 16 * lane;
+    vr[c] = pos / (2 * D);
+    voff[c] = (uint32_t)(vr[c] * kv_row_bytes + (((pos % (2 * D)) / 16) ^ vswz<D>(vr[c])) * 16);
+  }
+  auto load_v = [&](int t, int ph) {
+    const unsigned char* base = vhead + (size_t)ph * block_bytes;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < KS; ++c) load_lds16(base + voff[c], vtiles + t * TILE + 1024 * c);
+    __builtin_amdgcn_sched_barrier(0);
+  };
   auto load_block = [&](u32x4_t (&dst)[KS], const unsigned char* pool, int ph) {
     const unsigned char* base = pool + (size_t)ph * block_bytes;
     __builtin_amdgcn_sched_barrier(0);
@@ -104,17 +158,14 @@ __device__ __forceinline__ void run(State<D>& st, const u32x4_t (&qreg)[D / 32],
   };
   auto phys = [&](int i) { return __builtin_amdgcn_readlane(tbl, i < cn ? i : cn - 1); };
 
-  auto body = [&](u32x4_t (&kcur)[KS], u32x4_t (&vcur)[KS], int kb, int i) {
+  auto body = [&](u32x4_t (&kcur)[KS], int kb, int i) {
     const int ph_ahead = phys(i + PD);
-    const bool vok = kb * kBS + row < vlimit;
-#pragma unroll
-    for (int c = 0; c < KS; ++c)
-      store16(vtile + row * kVRow + (32 * c + 8 * quad) * 2, vok ? vcur[c] : u32x4_t{0u, 0u, 0u, 0u});
+    unsigned char* vtile = vtiles + (i % (PD + 1)) * TILE;
     floatx4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < KS; ++c) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kcur[c]), as_bf16x8(qreg[c]), s, 0, 0, 0);
     load_block(kcur, kpool, ph_ahead);
-    load_block(vcur, vpool, ph_ahead);
+    load_v((i + PD) % (PD + 1), ph_ahead);
     const int tok0 = kb * kBS + 4 * quad;
     float sv[4];
     bool need = false;
@@ -154,10 +205,19 @@ __device__ __forceinline__ void run(State<D>& st, const u32x4_t (&qreg)[D / 32],
       __builtin_memcpy(&phi, h2, 8);
       __builtin_memcpy(&plo, l2, 8);
     }
+    // this block's V has landed once the 2 KS PD loads issued after it are
+    // all that may be in flight; rows at or past the length are then zeroed
+    // (each lane the chunks it loaded: they may hold anything)
+    wait_vmcnt<2 * KS * PD>();
+    if ((kb + 1) * kBS > vlimit) {
+#pragma unroll
+      for (int c = 0; c < KS; ++c)
+        if (kb * kBS + vr[c] >= vlimit) store16(vtile + 1024 * c + 16 * lane, u32x4_t{0u, 0u, 0u, 0u});
+    }
     __asm__ volatile("" ::: "memory");
 #pragma unroll
     for (int d = 0; d < DT; ++d) {
-      const bf16x4_v bv = vt_operand<kVRow>(vtile, d, row, quad);
+      const bf16x4_v bv = vt_operand_swz<D>(vtile, d, row, quad);
       st.acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, bv, st.acc[d], 0, 0, 0);
       st.acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, bv, st.acc[d], 0, 0, 0);
     }
@@ -167,16 +227,20 @@ __device__ __forceinline__ void run(State<D>& st, const u32x4_t (&qreg)[D / 32],
   for (int c0 = 0; c0 < nb; c0 += 64) {
     cn = min(64, nb - c0);
     tbl = lane < cn ? clampi(trow[c0 + lane], 0, nmax) : 0;
+    // the previous chunk's last steps prefetched pad blocks into the tiles:
+    // let them land before the tiles are loaded again
+    __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
     for (int s = 0; s < PD; ++s) {
       load_block(kbuf[s], kpool, phys(s));
-      load_block(vbuf[s], vpool, phys(s));
+      load_v(s, phys(s));
     }
     for (int i = 0; i < cn; i += PD) {
 #pragma unroll
-      for (int s = 0; s < PD; ++s) body(kbuf[s], vbuf[s], kb0 + c0 + i + s, i + s);
+      for (int s = 0; s < PD; ++s) body(kbuf[s], kb0 + c0 + i + s, i + s);
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);   // no load into the tiles outlives the call
 }
 
 // Same tile step with K and V already staged in LDS by the workgroup:

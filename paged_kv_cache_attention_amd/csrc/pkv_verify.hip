@@ -107,8 +107,9 @@ __global__ __launch_bounds__(64 * kMaxWpg) void verify_mfma_kernel(VerifyArgs va
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kv = (blockIdx.x % (a.Hkv / wpg)) * wpg + wave;
   extern __shared__ __attribute__((aligned(16))) unsigned char vlds[];
-  unsigned char* vtile = vlds + wave * (kBS * tile::kVRow);
-  int* sprefix = reinterpret_cast<int*>(vlds + wpg * (kBS * tile::kVRow));
+  constexpr int kTileBytes = tile::run_tile_bytes<D, PD>();
+  unsigned char* vtiles = vlds + wave * kTileBytes;
+  int* sprefix = reinterpret_cast<int*>(vlds + wpg * kTileBytes);
   __shared__ int wsc[16];
   int total, per;
   if constexpr (INL) {
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(64 * kMaxWpg) void verify_mfma_kernel(VerifyArgs va
   const size_t block_bytes = (size_t)kBS * kv_row_bytes;
   const uint32_t lane_off = (uint32_t)((size_t)row * kv_row_bytes + (size_t)kv * D * 2 + quad * 16);
   const unsigned char* kpool = static_cast<const unsigned char*>(a.k_pool) + lane_off;
-  const unsigned char* vpool = static_cast<const unsigned char*>(a.v_pool) + lane_off;
+  const unsigned char* vhead = static_cast<const unsigned char*>(a.v_pool) + (size_t)kv * D * 2;
   const int nmax = a.N_blocks - 1;
   const int max_tokens = a.max_blocks * kBS;
 
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(64 * kMaxWpg) void verify_mfma_kernel(VerifyArgs va
       tile::State<D> st;
       tile::init(st);
       tile::run<D, PD>(st, qreg, hi_row, L, a.block_tables + (size_t)b * a.max_blocks + js, js, je - js, nmax, kpool,
-                       vpool, block_bytes, vtile, scale_log2e, lane);
+                       vhead, kv_row_bytes, block_bytes, vtiles, scale_log2e, lane);
 
       // ---- finish the piece ----
       const float l_row = tile::row_sum(st);
@@ -294,8 +295,12 @@ hipError_t launch_verify_mfma(const DecodeArgs& a, void* workspace, hipStream_t 
   float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(udesc) +
                                          (((size_t)a.B + 1) * 16 + 255) / 256 * 256);
   va.hdr = hdr; va.prefix = prefix; va.first = first; va.udesc = udesc; va.part = part;
-  const int wpg = a.Hkv < kMaxWpg ? a.Hkv : kMaxWpg;
-  const size_t tiles = (size_t)wpg * kBS * tile::kVRow;
+  // the V tiles of every wave of a workgroup share its LDS: fewer waves per
+  // workgroup where they would not fit (the grid then has more workgroups)
+  const size_t tile_bytes = a.D == 64 ? tile::run_tile_bytes<64, 2>() : tile::run_tile_bytes<128, 2>();
+  int wpg = a.Hkv < kMaxWpg ? a.Hkv : kMaxWpg;
+  while (wpg % 2 == 0 && (size_t)wpg * tile_bytes + 64 > (size_t)device_lds_per_block()) wpg /= 2;
+  const size_t tiles = (size_t)wpg * tile_bytes;
   const size_t lds_inl = tiles + (size_t)kInlinePerWave * wpg * 4;
   const bool inl = inline_plan_enabled() && a.B + 1 <= kInlinePerWave * wpg &&
                    lds_inl + 64 <= (size_t)device_lds_per_block();
