@@ -61,8 +61,25 @@ def algorithmic_bytes(w):
                 kv_unique=kv_unique, kv_logical=kv_logical)
 
 
-# Decode-kernel sources whose hash guards the committed traffic figures.
-TRAFFIC_SOURCES = ("pkv_stream.hip", "pkv_device.h", "pkv_internal.h", "pkv_group.h")
+# Decode-kernel sources whose hash guards the committed traffic figures (both
+# single-pass kernels: a change to either retires every figure).
+TRAFFIC_SOURCES = ("pkv_stream.hip", "pkv_verify.hip", "pkv_tile.h", "pkv_device.h", "pkv_internal.h", "pkv_group.h")
+
+
+def decode_uses_tile(w):
+    """Which single-pass kernel paged_attention_decode runs for w (the
+    library's choice, restated: the MFMA tile for bf16 with T * G <= 16 rows
+    when T >= 2, or at T = 1 unless PKV_DECODE_TILE=0, shared-prefix groups
+    are on, or the table holds fewer blocks than the 2048 waves of the grid)."""
+    G = w.Hq // w.Hkv
+    if w.dtype != "bf16" or w.D not in (64, 128) or w.T * G > 16:
+        return False
+    if w.T >= 2:
+        return True
+    mode = os.environ.get("PKV_DECODE_TILE", "")
+    if mode:
+        return mode[0] != "0"
+    return os.environ.get("PKV_PREFIX_GROUPS", "") != "1" and w.B * w.max_blocks >= 2048
 
 
 def measured_traffic(workload_name):
@@ -363,8 +380,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(w.name) if part == 0 else None,
-                     "kernel": ("paged_attention_decode call (plan + balanced decode + boundary merge)" if part == 0
-                                else "paged_attention_decode call (partition kernel + lse merge)"),
+                     "kernel": ("paged_attention_decode call (partition kernel + lse merge)" if part
+                                else "paged_attention_decode call (balanced MFMA tile + piece merge)" if decode_uses_tile(w)
+                                else "paged_attention_decode call (plan + balanced decode + boundary merge)"),
                      "bytes_per_launch": nb["decode"], "launch_ms": round(decode_ms, 5),
                      "launch_ms_p10_p50_p90": [round(float(np.percentile(warm, p)), 5) for p in (10, 50, 90)],
                      "logical_GBps": round(nb["logical"] / (decode_ms * 1e-3) / 1e9, 1)},

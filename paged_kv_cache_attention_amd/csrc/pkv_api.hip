@@ -241,7 +241,7 @@ pkv_status paged_attention_decode(const void* q, const void* k_pool, const void*
                              PKV_OK)
     return st;
   const bool fixed_split = partition_size > 0 && partition_size < max_blocks * block_size;
-  if (partition_size == 0 && pkv::verify_mfma_supported(a))
+  if (partition_size == 0 && pkv::verify_tile_for(a))
     return from_hip(pkv::launch_verify_mfma(a, workspace, s), "paged_attention_decode verify launch");
   if (partition_size == 0 && pkv::stream_supported(a))
     return from_hip(pkv::launch_decode_stream(a, workspace, s), "paged_attention_decode launch");

@@ -85,6 +85,10 @@ int prefill_piece_tokens(int B, int T, int Hq, int Hkv, int D, int max_blocks, i
 hipError_t launch_prefill(const DecodeArgs& a, int piece_tokens, float* workspace, hipStream_t stream);
 
 bool groups_enabled();
+// Single-token decode kernel choice, read on each call: PKV_DECODE_TILE=0
+// always takes the VALU stream kernel, =1 always the MFMA tile (where its
+// shapes allow), unset the policy of verify_tile_for.  Returns 0, 1 or -1.
+int decode_tile_mode();
 // Plan inside the decode kernel when the unit list fits in LDS (default;
 // PKV_INLINE_PLAN=0 launches the planning kernel instead).
 bool inline_plan_enabled();
@@ -119,9 +123,12 @@ hipError_t launch_plan(const int32_t* lens, int B, int T, int ranges, int max_bl
                        const int32_t* tables = nullptr, int G = 1, const PlanFinish* fin = nullptr,
                        int4* mdesc = nullptr);
 
-// MFMA verify tile for bf16 with 2 <= T and T * (Hq/Hkv) <= 16 query rows per
-// KV head; balanced like the VALU path, with its own workspace layout.
+// MFMA tile for bf16 with T * (Hq/Hkv) <= 16 query rows per KV head (the
+// verify step, and single-token decode when verify_tile_for says so);
+// balanced like the VALU path, with its own workspace layout.
 bool verify_mfma_supported(const DecodeArgs& a);
+// Whether paged_attention_decode (single pass) runs the MFMA tile for a.
+bool verify_tile_for(const DecodeArgs& a);
 size_t verify_workspace_bytes(int B, int T, int Hq, int D);
 hipError_t launch_verify_mfma(const DecodeArgs& a, void* workspace, hipStream_t stream);
 

@@ -14,6 +14,12 @@ bool groups_enabled() {
   return v && v[0] == '1';
 }
 
+int decode_tile_mode() {
+  const char* v = std::getenv("PKV_DECODE_TILE");
+  if (!v || !v[0]) return -1;
+  return v[0] == '0' ? 0 : 1;
+}
+
 bool groups_supported(const DecodeArgs& a) {
   const int G = a.Hq / a.Hkv;
   // four waves per decode workgroup (Hq >= 16) so that group workgroups match

@@ -103,9 +103,7 @@ __global__ __launch_bounds__(64 * kMaxWpg) void verify_mfma_kernel(VerifyArgs va
   const DecodeArgs& a = va.a;
   const int lane = threadIdx.x & 63;
   const int wpg = blockDim.x >> 6;
-  const int rng = blockIdx.x / (a.Hkv / wpg);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kv = (blockIdx.x % (a.Hkv / wpg)) * wpg + wave;
   extern __shared__ __attribute__((aligned(16))) unsigned char vlds[];
   constexpr int kTileBytes = tile::run_tile_bytes<D, PD>();
   unsigned char* vtiles = vlds + wave * kTileBytes;
@@ -123,6 +121,14 @@ __global__ __launch_bounds__(64 * kMaxWpg) void verify_mfma_kernel(VerifyArgs va
     if constexpr (INL) return sprefix[i];
     else return va.prefix[i];
   };
+  // Workgroup -> range: as in the decode stream, each XCD takes a
+  // contiguous run of ranges when they are longer than the minimum, so that
+  // neighbouring sequences sharing prefix blocks re-read them through one L2.
+  const bool contiguous = INL && gridDim.x % 8 == 0 && per > kMinBlocksPerRange;
+  const int wid = __builtin_amdgcn_readfirstlane(contiguous ? (int)xcd_logical_id(blockIdx.x, gridDim.x / 8)
+                                                            : (int)blockIdx.x);
+  const int rng = wid / (a.Hkv / wpg);
+  const int kv = (wid % (a.Hkv / wpg)) * wpg + wave;
   const int F0 = rng * per;
   if (F0 >= total) return;
   const int F1 = min(total, F0 + per);
@@ -268,8 +274,26 @@ int verify_ranges(int Hkv) { return kStreamWaves / Hkv; }   // one wave per KV h
 
 bool verify_mfma_supported(const DecodeArgs& a) {
   const int G = a.Hq / a.Hkv;
-  return a.bf16 && (a.D == 64 || a.D == 128) && a.T >= 2 && a.T * G <= 16 && a.B <= kStreamMaxTB &&
+  return a.bf16 && (a.D == 64 || a.D == 128) && a.T >= 1 && a.T * G <= 16 && a.B <= kStreamMaxTB &&
          (a.Hkv <= kMaxWpg || a.Hkv % kMaxWpg == 0) && (long long)a.B * a.max_blocks < (1ll << 30);
+}
+
+// Multi-token steps always take the tile.  Single-token decode takes it too
+// (its T = 1 rows are the G query heads of a KV head, 1 to 8 of the 16 tile
+// rows) unless the shared-prefix groups are switched on, which live in the
+// stream kernel, or the batch's table holds fewer blocks than the grid has
+// waves.  Measured against the VALU stream kernel at T = 1: faster for every
+// head group size at D = 64 (Llama-3.2-1B shape 57.0 -> 55.1 us; 64 query
+// heads over 8 KV heads 97.0 -> 66.5 us) and for the 8B shared-prefix batch
+// (222.7 -> 217.9 us); about 3 % slower on a 64-sequence D = 128, G = 4 batch
+// without shared blocks, and slower on an 8-sequence batch of 1,681 tokens
+// (hence the size floor).
+bool verify_tile_for(const DecodeArgs& a) {
+  if (!verify_mfma_supported(a)) return false;
+  if (a.T >= 2) return true;
+  const int mode = decode_tile_mode();
+  if (mode >= 0) return mode == 1;
+  return !groups_enabled() && (long long)a.B * a.max_blocks >= kStreamWaves;
 }
 
 size_t verify_workspace_bytes(int B, int T, int Hq, int D) {

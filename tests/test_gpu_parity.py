@@ -21,6 +21,14 @@ def say(*a):
     print(*a, flush=True)
 
 
+
+@pytest.fixture(autouse=True, params=["tile", "stream"])
+def decode_kernel(request, monkeypatch):
+    """Single-token decode through the MFMA tile and through the VALU stream
+    kernel (PKV_DECODE_TILE, read by the library on each call)."""
+    monkeypatch.setenv("PKV_DECODE_TILE", "1" if request.param == "tile" else "0")
+    return request.param
+
 @pytest.fixture(scope="module")
 def c1():
     return workload.tiny_fp32()
