@@ -170,8 +170,11 @@ size_t pkv_decode_workspace_bytes(int B, int T, int Hq, int D, int max_blocks, i
  * boundaries leaves one normalised partial per piece and a merge kernel
  * combines them by log-sum-exp weights.  Shapes: bf16 with D in {64, 128} or
  * fp32 with D = 64, Hq a multiple of 4 with Hq/4 <= 8 or a multiple of 8,
- * Hq/Hkv in {1, 2, 4, 8}, B*T <= 8192.  bf16 with 2 <= T and T*Hq/Hkv <= 16
- * (multi-query verify) runs 16-row MFMA tiles instead, split the same way.
+ * Hq/Hkv in {1, 2, 4, 8}, B*T <= 8192.  bf16 with D in {64, 128} and
+ * T*Hq/Hkv <= 16 runs 16-row MFMA tiles instead (the T*Hq/Hkv query rows of a
+ * KV head), split the same way: always for T >= 2 (multi-query verify), and
+ * for T = 1 unless B*max_blocks < 2048, the shared-prefix groups below are
+ * on, or the environment variable PKV_DECODE_TILE=0 (=1 forces the tile).
  * Other shapes run the partitioned kernel below with one partition.
  * With T = 1, bf16 and the environment variable PKV_PREFIX_GROUPS=1, adjacent
  * sequences whose tables start with the same physical block are grouped and
