@@ -30,6 +30,11 @@ namespace {
 
 constexpr int kBS = 16;
 constexpr int kMaxWpg = 8;
+// Blocks whose K and V are in flight while a wave works on one.  One measured
+// faster than two and three on the 8B shared-prefix decode batch (216.1,
+// 218.2, 222.3 us), the 1B batch (53.8, 54.8, 57.3 us) and the long-context
+// verify batch (432.6, 436.6, 439.8 us).
+constexpr int kTilePD = 1;
 
 constexpr int kInlinePerWave = 512;            // LDS prefix entries per wave
 constexpr int kInlinePT = kInlinePerWave / 64;  // sequences per thread
@@ -321,7 +326,7 @@ hipError_t launch_verify_mfma(const DecodeArgs& a, void* workspace, hipStream_t 
   va.hdr = hdr; va.prefix = prefix; va.first = first; va.udesc = udesc; va.part = part;
   // the V tiles of every wave of a workgroup share its LDS: fewer waves per
   // workgroup where they would not fit (the grid then has more workgroups)
-  const size_t tile_bytes = a.D == 64 ? tile::run_tile_bytes<64, 2>() : tile::run_tile_bytes<128, 2>();
+  const size_t tile_bytes = a.D == 64 ? tile::run_tile_bytes<64, kTilePD>() : tile::run_tile_bytes<128, kTilePD>();
   int wpg = a.Hkv < kMaxWpg ? a.Hkv : kMaxWpg;
   while (wpg % 2 == 0 && (size_t)wpg * tile_bytes + 64 > (size_t)device_lds_per_block()) wpg /= 2;
   const size_t tiles = (size_t)wpg * tile_bytes;
@@ -335,11 +340,11 @@ hipError_t launch_verify_mfma(const DecodeArgs& a, void* workspace, hipStream_t 
   const float sl2 = a.scale * kLog2e;
   const dim3 grid(va.ranges * (a.Hkv / wpg)), block(64 * wpg);
   if (a.D == 64) {
-    if (inl) hipLaunchKernelGGL((verify_mfma_kernel<64, 2, true>), grid, block, lds_inl, stream, va, sl2);
-    else hipLaunchKernelGGL((verify_mfma_kernel<64, 2, false>), grid, block, tiles, stream, va, sl2);
+    if (inl) hipLaunchKernelGGL((verify_mfma_kernel<64, kTilePD, true>), grid, block, lds_inl, stream, va, sl2);
+    else hipLaunchKernelGGL((verify_mfma_kernel<64, kTilePD, false>), grid, block, tiles, stream, va, sl2);
   } else {
-    if (inl) hipLaunchKernelGGL((verify_mfma_kernel<128, 2, true>), grid, block, lds_inl, stream, va, sl2);
-    else hipLaunchKernelGGL((verify_mfma_kernel<128, 2, false>), grid, block, tiles, stream, va, sl2);
+    if (inl) hipLaunchKernelGGL((verify_mfma_kernel<128, kTilePD, true>), grid, block, lds_inl, stream, va, sl2);
+    else hipLaunchKernelGGL((verify_mfma_kernel<128, kTilePD, false>), grid, block, tiles, stream, va, sl2);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int waves = a.B * a.T * (a.Hq / 4);
