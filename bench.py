@@ -63,23 +63,16 @@ def algorithmic_bytes(w):
 
 # Decode-kernel sources whose hash guards the committed traffic figures (both
 # single-pass kernels: a change to either retires every figure).
-TRAFFIC_SOURCES = ("pkv_stream.hip", "pkv_verify.hip", "pkv_tile.h", "pkv_device.h", "pkv_internal.h", "pkv_group.h")
+TRAFFIC_SOURCES = ("pkv_stream.hip", "pkv_verify.hip", "pkv_tile.h", "pkv_device.h", "pkv_internal.h")
 
 
 def decode_uses_tile(w):
     """Which single-pass kernel paged_attention_decode runs for w (the
-    library's choice, restated: the MFMA tile for bf16 with T * G <= 16 rows
-    when T >= 2, or at T = 1 unless PKV_DECODE_TILE=0, shared-prefix groups
-    are on, or the table holds fewer blocks than the 2048 waves of the grid)."""
+    library's choice, restated: the MFMA tile for bf16, D in {64, 128},
+    T * G <= 16 query rows per KV head and Hkv <= 8 or a multiple of 8)."""
     G = w.Hq // w.Hkv
-    if w.dtype != "bf16" or w.D not in (64, 128) or w.T * G > 16:
-        return False
-    if w.T >= 2:
-        return True
-    mode = os.environ.get("PKV_DECODE_TILE", "")
-    if mode:
-        return mode[0] != "0"
-    return os.environ.get("PKV_PREFIX_GROUPS", "") != "1" and w.B * w.max_blocks >= 2048
+    return (w.dtype == "bf16" and w.D in (64, 128) and w.T * G <= 16 and (w.Hkv <= 8 or w.Hkv % 8 == 0)
+            and w.B <= 8192)
 
 
 def measured_traffic(workload_name):
@@ -111,27 +104,100 @@ def attention_flops(w):
     return int(vis.sum()) * w.Hq * 4 * w.D
 
 
-def cpu_baseline(w, budget_s):
-    """The fp64 oracle, untuned, one BLAS thread, on a bounded sample of the same batch.
+def host_cores():
+    """Cores this process may run on, capped at the 16-core share of one GPU."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
 
-    Sequences are evaluated one call at a time, cycling through the batch,
-    until budget_s seconds of oracle time have been spent."""
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(w, budget_s, repeats=3):
+    """The fp64 oracle, untuned, on a bounded sample of the same batch, on the
+    host's cores.
+
+    The oracle evaluates one sequence per call (the whole batch of its query
+    rows); the sample is the first n sequences in batch order, n chosen from a
+    one-sequence calibration so that one pass takes about budget_s / repeats
+    seconds on `cores` threads, each thread taking whole sequences with one
+    BLAS thread of its own.  The pass is timed `repeats` times (median
+    reported, all listed); a one-thread pass over a smaller sample is reported
+    beside it."""
     import oracle
+    from concurrent.futures import ThreadPoolExecutor
     from threadpoolctl import threadpool_limits
 
     q_all, kp, vp = w.values(w.q), w.values(w.k_pool), w.values(w.v_pool)
-    done, spent = 0, 0.0
+    cores = host_cores()
+
+    def one(b):
+        oracle.paged_attention(q_all[b:b + 1], kp, vp, w.block_tables[b:b + 1], w.context_lens[b:b + 1],
+                               w.scale, w.block_size)
+
+    def timed_pass(seqs, threads):
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(one, seqs))
+        return time.perf_counter() - t0
+
     with threadpool_limits(limits=1):
-        while spent < budget_s:
-            b = done % w.B
-            t0 = time.perf_counter()
-            oracle.paged_attention(q_all[b:b + 1], kp, vp, w.block_tables[b:b + 1], w.context_lens[b:b + 1],
-                                   w.scale, w.block_size)
-            spent += time.perf_counter() - t0
-            done += 1
-    return {"value": round(done / spent, 2), "unit": "seq-steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} sequence-steps of {w.name} taken in batch order ({min(done, w.B)} distinct "
-                      f"sequences), fp64 NumPy oracle, 1 BLAS thread, {spent:.1f} s"}
+        t_one = timed_pass([0], 1)   # calibration, untimed in the result
+        per_tok = t_one / max(1, int(w.context_lens[0]))
+        order = [b % w.B for b in range(64 * w.B)]
+        cum = np.cumsum([int(w.context_lens[b]) for b in order]) * per_tok
+
+        def sample(seconds):
+            return order[:max(1, int(np.searchsorted(cum, seconds)) + 1)]
+        seqs = sample(budget_s / repeats * cores * 0.8)
+        times = [timed_pass(seqs, cores) for _ in range(repeats)]
+        seqs1 = sample(budget_s / (2 * repeats))
+        t1 = timed_pass(seqs1, 1)
+    med = float(np.median(times))
+    return {"value": round(len(seqs) / med, 2), "unit": "seq-steps/s", "cores": cores, "kind": "oracle",
+            "repeats_s": [round(t, 3) for t in times],
+            "one_thread": {"value": round(len(seqs1) / t1, 2), "sequences": len(seqs1), "s": round(t1, 3)},
+            "cpu_model": cpu_model(),
+            "sample": f"{len(seqs)} sequence-steps of {w.name} in batch order ({min(len(seqs), w.B)} distinct "
+                      f"sequences), fp64 NumPy oracle, {cores} threads over sequences with 1 BLAS thread each, "
+                      f"median of {repeats} passes"}
+
+
+def hipcc_version():
+    """hipcc's version line (a child process; taken before the GPU is touched)."""
+    import subprocess
+    try:
+        out = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True, timeout=60).stdout
+        return next((l.strip() for l in out.splitlines() if "version" in l.lower()), None)
+    except (OSError, subprocess.SubprocessError):
+        return None
+
+
+def provenance(torch, w, hipcc):
+    """What produced the numbers: device, ROCm and hipcc versions, commit, seed, host CPU."""
+    from paged_kv_cache_attention_amd import build as pkv_build
+    info = {"gpu": torch.cuda.get_device_name(0), "torch": torch.__version__, "torch_hip": torch.version.hip,
+            "hipcc": hipcc, "seed": workload.WORKLOAD_SEEDS.get(w.name), "host_cpu": cpu_model(),
+            "host_cores": host_cores()}
+    try:
+        info["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        info["rocm"] = None
+    info["sources_sha256"] = pkv_build.sources_sha256()
+    info["commit"] = None
+    try:   # the commit the library was built from, recorded by the build while the sources still match
+        bi = json.loads(pkv_build.BUILD_INFO.read_text())
+        if bi.get("sources_sha256") == info["sources_sha256"]:
+            info["commit"] = bi.get("commit")
+    except (OSError, ValueError):
+        pass
+    return info
 
 
 def read_ceiling(torch, dev, nbytes=2 << 30, reps=10):
@@ -253,7 +319,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(workload.WORKLOADS))
     ap.add_argument("--partition", type=int, default=None, help="split-KV partition size (tokens); 0 = single pass")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=24.0,
+                    help="oracle time budget of the cpu_baseline leg (its passes together)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rope-theta", type=float, default=None,
                     help="append workloads: fused RoPE append (paged_kv_append_rope, queries rotated too)")
@@ -261,13 +328,12 @@ def main():
                     help="measure the host runtime (engine) and a 16-request serving run instead of one batch")
     ap.add_argument("--cold-reps", type=int, default=20,
                     help="extra untimed-region reps, each after a 1 GiB cache flush, for the cold-cache figure")
-    ap.add_argument("--ceiling", action="store_true",
-                    help="also time a plain 1 GiB device copy (torch) and the random-slice read probe")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
+    hipcc = hipcc_version()
     import torch
     import paged_kv_cache_attention_amd as pkv
 
@@ -418,9 +484,11 @@ def main():
             cc["GBps_at_median"] = round(nb["decode"] / (cold_med * 1e-3) / 1e9, 1)
             cc["frac_at_median"] = round(nb["decode"] / (cold_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
         result["roofline"]["cold_cache"] = cc
-    if args.ceiling:
-        result["copy_ceiling"] = copy_ceiling(torch, dev)
-        result["read_ceiling"] = read_ceiling(torch, dev)
+    # the practical ceilings, measured in the same run: the read probe (the
+    # decode kernels' access pattern, no arithmetic) and a plain device copy
+    result["read_ceiling"] = read_ceiling(torch, dev)
+    result["copy_ceiling"] = copy_ceiling(torch, dev)
+    result["provenance"] = provenance(torch, w, hipcc)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)

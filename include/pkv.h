@@ -35,8 +35,10 @@
  *    speculative-decoding verify step ("LLM Inference from Scratch", M7).
  *  - `stream` is a hipStream_t passed as void*; NULL is the null stream.
  *    Every launch is asynchronous on that stream; no call synchronises,
- *    except that PKV_DEBUG=1 in the environment adds a device-side check of
- *    table entries and lengths, followed by a stream synchronisation.
+ *    except that PKV_DEBUG=1 in the environment (read once, at the first
+ *    call) adds a device-side check of table entries and lengths, followed by
+ *    a stream synchronisation.  No other environment variable is read: which
+ *    kernels a call runs depends only on its arguments and the device.
  *  - Errors: argument errors are detected on the host before any launch and
  *    return a status; nothing is launched then.  Launch failures return
  *    PKV_EHIP.  pkv_last_error() gives a message for the last non-OK status
@@ -129,9 +131,12 @@ pkv_status paged_kv_append_rope(void* q, int Hq, const void* k_new, const void* 
                                 float rope_theta, pkv_dtype dtype, void* stream);
 
 /*
- * paged_kv_copy_blocks -- copy-on-write support ("vLLM and PagedAttention":
- * memory sharing; a sequence that appends into a block other sequences also
- * reference writes to its own copy): for i < n, block dst[i] of both pools
+ * paged_kv_copy_blocks -- copy-on-write support for prefix caching
+ * ("Inference From Scratch", Chapters table, ch. 10-11: block tables, and
+ * prefix caching by hash-based block reuse across requests).  A sequence that
+ * appends into a block other sequences also reference writes to a private
+ * copy of it (this library's rule for reused, partly filled blocks): for
+ * i < n, block dst[i] of both pools
  * becomes a byte copy of block src[i].  src and dst are device arrays of n
  * block ids; pairs with an id outside [0, N_blocks) are skipped; no id may be
  * both a source and a destination in one call.  n = 0 is a no-op.
@@ -171,15 +176,10 @@ size_t pkv_decode_workspace_bytes(int B, int T, int Hq, int D, int max_blocks, i
  * combines them by log-sum-exp weights.  Shapes: bf16 with D in {64, 128} or
  * fp32 with D = 64, Hq a multiple of 4 with Hq/4 <= 8 or a multiple of 8,
  * Hq/Hkv in {1, 2, 4, 8}, B*T <= 8192.  bf16 with D in {64, 128} and
- * T*Hq/Hkv <= 16 runs 16-row MFMA tiles instead (the T*Hq/Hkv query rows of a
- * KV head), split the same way: always for T >= 2 (multi-query verify), and
- * for T = 1 unless B*max_blocks < 2048, the shared-prefix groups below are
- * on, or the environment variable PKV_DECODE_TILE=0 (=1 forces the tile).
- * Other shapes run the partitioned kernel below with one partition.
- * With T = 1, bf16 and the environment variable PKV_PREFIX_GROUPS=1, adjacent
- * sequences whose tables start with the same physical block are grouped and
- * their common blocks are attended once per group on MFMA (off by default:
- * on MI355X the last-level cache already serves most shared-prefix re-reads).
+ * T*Hq/Hkv <= 16 (with Hkv <= 8 or a multiple of 8) runs 16-row MFMA tiles
+ * instead (the T*Hq/Hkv query rows of a KV head), split the same way, for
+ * single-token decode and multi-query verify alike.  Other shapes run the
+ * partitioned kernel below with one partition.
  * The partitioned path and the balanced path give results that agree within
  * rounding; each is deterministic: equal inputs give equal bits.
  * partition_size > 0 (a multiple of block_size) splits every sequence into

@@ -156,6 +156,60 @@ def _stream(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _alloc(shape, dtype, device, stream):
+    """Device memory for the library (a workspace, or an output it was not
+    given), owned by torch's caching allocator.
+
+    It is allocated on `stream` (torch's current stream when None), the stream
+    the library launches on, so the allocator does not hand it to other work
+    while those kernels may still use it after this call returns."""
+    torch = _torch()
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
+def check_attention_args(q, k_pool, v_pool, block_tables, context_lens, out=None, lse_out=None):
+    """Shape, dtype and device agreement of the attention arguments.
+
+    The C ABI takes raw pointers and sizes, so a pool of another dtype or head
+    size than q, or an out or lse_out of the wrong size, would make the
+    kernels read or write past the end of a buffer: the binding checks here,
+    from the tensors' metadata only (it runs on any tensor, without a GPU).
+    Raises ValueError or TypeError."""
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B, T, Hq, D], got shape {tuple(q.shape)}")
+    B, T, Hq, D = q.shape
+    if k_pool.dim() != 4 or tuple(k_pool.shape) != tuple(v_pool.shape):
+        raise ValueError(f"k_pool and v_pool must both be [N_blocks, block_size, Hkv, D], got "
+                         f"{tuple(k_pool.shape)} and {tuple(v_pool.shape)}")
+    if k_pool.shape[3] != D:
+        raise ValueError(f"pool head size {k_pool.shape[3]} differs from q's {D}")
+    if Hq % k_pool.shape[2]:
+        raise ValueError(f"Hq = {Hq} is not a multiple of the pool's Hkv = {k_pool.shape[2]}")
+    for name, t in (("k_pool", k_pool), ("v_pool", v_pool), ("out", out)):
+        if t is not None and t.dtype != q.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, q has {q.dtype}")
+    if out is not None and tuple(out.shape) != tuple(q.shape):
+        raise ValueError(f"out must have q's shape {tuple(q.shape)}, got {tuple(out.shape)}")
+    if lse_out is not None:
+        if lse_out.dtype != torch.float32 or tuple(lse_out.shape) != (B, T, Hq):
+            raise ValueError(f"lse_out must be float32 [B, T, Hq] = {(B, T, Hq)}, got {lse_out.dtype} "
+                             f"{tuple(lse_out.shape)}")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError(f"block_tables must be [B = {B}, max_blocks], got {tuple(block_tables.shape)}")
+    if context_lens.dim() != 1 or context_lens.shape[0] != B:
+        raise ValueError(f"context_lens must be [B = {B}], got {tuple(context_lens.shape)}")
+    for name, t in (("block_tables", block_tables), ("context_lens", context_lens)):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32, got {t.dtype}")
+    devs = {t.device for t in (q, k_pool, v_pool, block_tables, context_lens, out, lse_out) if t is not None}
+    if len(devs) != 1:
+        raise ValueError(f"all tensors must be on one device, got {sorted(map(str, devs))}")
+
+
 def pkv_decode_workspace_bytes(B, T, Hq, D, max_blocks, block_size, partition_size) -> int:
     return int(load_library().pkv_decode_workspace_bytes(B, T, Hq, D, max_blocks, block_size, partition_size))
 
@@ -202,18 +256,18 @@ def paged_attention_decode(q, k_pool, v_pool, block_tables, context_lens, out=No
     When the library needs workspace (pkv_decode_workspace_bytes > 0) and none
     is given, one is allocated with torch (device memory only; all computation
     is in the library)."""
-    torch = _torch()
     lib = load_library()
+    check_attention_args(q, k_pool, v_pool, block_tables, context_lens, out, lse_out)
     B, T, Hq, D = q.shape
     N, bs, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
     max_blocks = block_tables.shape[1]
     if out is None:
-        out = torch.empty_like(q)
+        out = _alloc(q.shape, q.dtype, q.device, stream)
     if scale is None:
         scale = 1.0 / D ** 0.5
     need = pkv_decode_workspace_bytes(B, T, Hq, D, max_blocks, bs, partition_size)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _alloc(need, _torch().uint8, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.paged_attention_decode(_ptr(q), _ptr(k_pool), _ptr(v_pool), _i32(block_tables, "block_tables"),
                                       _i32(context_lens, "context_lens"), _ptr(out), _ptr(lse_out), B, T, Hq, Hkv, D,
@@ -238,20 +292,20 @@ def paged_attention_prefill(q, k_pool, v_pool, block_tables, context_lens, out=N
     piece_tokens None takes the library's suggestion for this shape on the
     current device (pkv_prefill_piece_tokens); 0 never splits keys.  When
     pieces need workspace and none is given, one is allocated."""
-    torch = _torch()
     lib = load_library()
+    check_attention_args(q, k_pool, v_pool, block_tables, context_lens, out, lse_out)
     B, T, Hq, D = q.shape
     N, bs, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
     max_blocks = block_tables.shape[1]
     if out is None:
-        out = torch.empty_like(q)
+        out = _alloc(q.shape, q.dtype, q.device, stream)
     if scale is None:
         scale = 1.0 / D ** 0.5
     if piece_tokens is None:
         piece_tokens = pkv_prefill_piece_tokens(B, T, Hq, Hkv, D, bs, max_blocks)
     need = pkv_prefill_workspace_bytes(B, T, Hq, Hkv, D, bs, max_blocks, piece_tokens)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _alloc(need, _torch().uint8, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.paged_attention_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool), _i32(block_tables, "block_tables"),
                                        _i32(context_lens, "context_lens"), _ptr(out), _ptr(lse_out), B, T, Hq, Hkv, D,

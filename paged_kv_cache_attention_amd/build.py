@@ -20,7 +20,7 @@ CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 LIB = PKG / "libpkv.so"
 PROBE_LIB = PKG / "libpkv_probe.so"      # diagnostic read-bandwidth probe, not part of the pkv ABI
-SOURCES = ["pkv_api.hip", "pkv_decode.hip", "pkv_stream.hip", "pkv_verify.hip", "pkv_prefill.hip", "pkv_prefix.hip", "pkv_reduce.hip", "pkv_copy.hip", "pkv_rope.hip", "pkv_engine.cpp"]
+SOURCES = ["pkv_api.hip", "pkv_decode.hip", "pkv_stream.hip", "pkv_verify.hip", "pkv_prefill.hip", "pkv_devattr.hip", "pkv_reduce.hip", "pkv_copy.hip", "pkv_rope.hip", "pkv_engine.cpp"]
 ARCH = "gfx950"
 
 
@@ -31,11 +31,50 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; ROCm is required to build libpkv")
 
 
+OBJ_DIR = ROOT / "_build"
+FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wno-unused-command-line-argument"]
+
+
 def command(out: pathlib.Path = LIB, extra=()) -> list:
-    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wno-unused-command-line-argument",
-            f"-I{INCLUDE}", f"-I{CSRC}", *extra, "-o", str(out), *[str(CSRC / s) for s in SOURCES]]
+    """One hipcc line that compiles and links every source (what build() runs, file by file)."""
+    return [hipcc(), *FLAGS, "-shared", f"-I{INCLUDE}", f"-I{CSRC}", *extra, "-o", str(out),
+            *[str(CSRC / s) for s in SOURCES]]
+
+
+def object_command(src: str, extra=()) -> list:
+    return [hipcc(), *FLAGS, "-c", f"-I{INCLUDE}", f"-I{CSRC}", *extra, "-o", str(OBJ_DIR / (src + ".o")),
+            str(CSRC / src)]
+
+
+BUILD_INFO = PKG / "build_info.json"   # commit and source hash of the last build (not tracked)
+
+
+def sources_sha256() -> str:
+    """Hash of every kernel/host source and the public headers."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(CSRC.iterdir()):
+        if f.is_file():
+            h.update(f.read_bytes())
+    for f in ("pkv.h", "pkv_engine.h"):
+        h.update((INCLUDE / f).read_bytes())
+    return h.hexdigest()
+
+
+def _write_build_info():
+    import json
+    commit = None
+    try:
+        head = subprocess.run(["git", "-C", str(ROOT), "rev-parse", "HEAD"], capture_output=True, text=True)
+        if head.returncode == 0:
+            dirty = subprocess.run(["git", "-C", str(ROOT), "status", "--porcelain", "--", "paged_kv_cache_attention_amd",
+                                    "include"], capture_output=True, text=True).stdout.strip()
+            commit = head.stdout.strip() + ("-dirty" if dirty else "")
+    except OSError:
+        pass
+    BUILD_INFO.write_text(json.dumps({"commit": commit, "sources_sha256": sources_sha256()}) + "\n")
 
 
 def _compile(cmd, verbose):
@@ -57,10 +96,17 @@ def build(verbose: bool = False) -> pathlib.Path:
               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument",
               "-o", str(ptmp), str(CSRC / "probe_read.hip")], verbose)
     os.replace(ptmp, PROBE_LIB)
+    # each source compiles to its own object (its kernels and their host
+    # launchers live in one file), in parallel; then one link
+    OBJ_DIR.mkdir(exist_ok=True)
+    from concurrent.futures import ThreadPoolExecutor
+    jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(jobs) as ex:
+        list(ex.map(lambda src: _compile(object_command(src), verbose), SOURCES))
     tmp = LIB.with_suffix(".so.tmp")
-    cmd = command(tmp)
-    _compile(cmd, verbose)
+    _compile([hipcc(), *FLAGS, "-shared", "-o", str(tmp), *[str(OBJ_DIR / (src + ".o")) for src in SOURCES]], verbose)
     os.replace(tmp, LIB)
+    _write_build_info()
     return LIB
 
 

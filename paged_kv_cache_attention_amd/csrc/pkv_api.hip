@@ -32,9 +32,14 @@ pkv_status from_hip(hipError_t e, const char* what) {
   return fail(PKV_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// PKV_DEBUG=1 in the environment turns on the device-side contract check;
+// read once, at the first call that could run it.
 bool debug_enabled() {
-  const char* v = std::getenv("PKV_DEBUG");
-  return v && v[0] == '1';
+  static const bool on = [] {
+    const char* v = std::getenv("PKV_DEBUG");
+    return v && v[0] == '1';
+  }();
+  return on;
 }
 
 int elem_bytes(pkv_dtype dt) { return dt == PKV_BF16 ? 2 : 4; }

@@ -84,10 +84,7 @@ template <> __device__ __forceinline__ void chunk_widen<float>(u32x4_t v, float*
   f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y); f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
 }
 
-#ifndef PKV_PD
-#define PKV_PD 2
-#endif
-constexpr int PD = PKV_PD;   // blocks in flight per wave
+constexpr int PD = 2;   // blocks in flight per wave
 
 template <typename ET, int D, int GW, int NW>
 __global__ __launch_bounds__(64 * NW) void decode_valu_kernel(DecodeArgs a, float scale_log2e, uint32_t n_items) {

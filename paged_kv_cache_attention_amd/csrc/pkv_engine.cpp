@@ -2,9 +2,9 @@
 // manager with prefix caching and copy-on-write, and a continuous-batching
 // scheduler with recompute preemption.
 //
-// Block manager ("Inference From Scratch", ch. 10 and ch. 11: block tables,
-// hash-based block reuse across requests; "vLLM and PagedAttention": memory
-// sharing, copy-on-write):
+// Block manager ("Inference From Scratch", Chapters table, ch. 10 and ch. 11:
+// block tables, prefix caching by hash-based block reuse across requests; the
+// copy-on-write rule for shared, partly filled blocks is this library's own):
 //   * a pool of num_blocks physical blocks, each with a reference count;
 //   * a prefix cache mapping a block's content key to its physical block.
 //     The key of logical block j of a sequence chains the key of block j - 1
@@ -232,6 +232,11 @@ struct pkv_engine {
   std::vector<int64_t> p_id;
   std::vector<int32_t> p_kind, p_start, p_count, p_tok_off, p_tokens, p_tables, p_lens, p_src, p_dst;
   std::vector<int64_t> p_preempted;
+  // Sources of this plan's block copies, released only once the plan is
+  // complete: a source that dropped to no users mid-plan would be evictable,
+  // and a later allocation of the same plan could take it as a copy
+  // destination (the plan would then copy into a block it also copies from).
+  std::vector<int> p_release;
   bool plan_open = false;
   pkv_engine_stats stats{};
 
@@ -276,7 +281,7 @@ struct pkv_engine {
     const int b = bm.allocate();
     p_src.push_back(last);
     p_dst.push_back(b);
-    bm.release(last);
+    p_release.push_back(last);
     r.table[p / bs] = b;
     ++stats.cow_copies;
     return 1;
@@ -326,7 +331,7 @@ struct pkv_engine {
       const int b = bm.allocate();
       p_src.push_back(r.table[j]);
       p_dst.push_back(b);
-      bm.release(r.table[j]);
+      p_release.push_back(r.table[j]);
       r.table[j] = b;
       ++stats.cow_copies;
     }
@@ -352,7 +357,7 @@ struct pkv_engine {
     if (plan_open) return set_error(PKV_EINVAL, "the previous plan has not been committed");
     planned.clear();
     p_id.clear(); p_kind.clear(); p_start.clear(); p_count.clear(); p_tok_off.clear(); p_tokens.clear();
-    p_tables.clear(); p_lens.clear(); p_src.clear(); p_dst.clear(); p_preempted.clear();
+    p_tables.clear(); p_lens.clear(); p_src.clear(); p_dst.clear(); p_preempted.clear(); p_release.clear();
 
     // 1. decode slots for the running requests; preempt the latest arrivals until they fit
     while (!running.empty()) {
@@ -391,6 +396,8 @@ struct pkv_engine {
       first = false;
       emit(*r, PKV_ENGINE_PREFILL, r->computed, count);
     }
+    for (int b : p_release) bm.release(b);
+    p_release.clear();
     plan_open = !planned.empty();
     if (!plan_open && !waiting.empty())
       return set_error(PKV_EINVAL, "request %lld cannot be admitted: the pool is too small for it alone",

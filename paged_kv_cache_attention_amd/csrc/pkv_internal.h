@@ -29,42 +29,12 @@ struct DecodeArgs {
 // Balanced persistent VALU path: a fixed grid of kStreamWaves waves splits
 // the flattened block list of all (head group, query token, sequence) units
 // evenly; pieces of units cut by wave ranges are merged by a second kernel.
-#ifndef PKV_STREAM_WAVES
-#define PKV_STREAM_WAVES 2048
-#endif
-constexpr int kStreamWaves = PKV_STREAM_WAVES;
+constexpr int kStreamWaves = 2048;   // 8 waves per CU of a 256-CU device
 constexpr int kStreamMaxTB = 8192;   // B * T limit of the planning kernel
 bool stream_supported(const DecodeArgs& a);
 size_t stream_workspace_bytes(int B, int T, int Hq, int D);
 hipError_t launch_decode_stream(const DecodeArgs& a, void* workspace, hipStream_t stream);
 
-// Shared-prefix groups (single-token decode, bf16): runs of consecutive
-// sequences whose tables start with the same physical block, cut into groups
-// of at most group_members(G) members inside aligned windows of kGroupWindow
-// sequences.  The blocks a member has in common with the group's longest
-// member are attended once per group on MFMA (all members' query rows
-// together); the rest goes through the balanced path and the two are merged.
-constexpr int kGroupWindow = 16;
-constexpr int kGroupChunks = 4;      // partials per member (chunks of a group's prefix)
-constexpr int kGroupMinShare = 4;    // blocks in common before a group pays off
-constexpr int kGroupMaxB = 1024;     // detection runs inside the planning workgroup
-inline int group_members(int G) { return 64 / G < kGroupWindow ? 64 / G : kGroupWindow; }   // G <= 32
-__host__ __device__ inline int group_chunk_blocks(int d) {
-  const int c = (d + kGroupChunks - 1) / kGroupChunks;
-  return c > 8 ? c : 8;
-}
-
-struct GroupPlan {
-  int* sfx;        // [B] blocks of the sequence attended by its group (0: not grouped)
-  int* nch;        // [B] chunk partials of the sequence's group (0: not grouped)
-  int4* desc;      // [B] leader: {canonical, members, shared blocks, V row limit}
-  int* clist;      // [B * kGroupChunks / 2] leader * kGroupChunks + chunk
-  float* part;     // [B][kGroupChunks][Hq][D + 1] normalised partials and lse
-};
-// Off unless PKV_PREFIX_GROUPS=1 (read on every call): on MI355X the 256 MB
-// last-level cache already serves most re-reads of a shared prefix, and the
-// detection and the group workgroups cost more than they save on the
-// prefix-sharing 8B-shaped batch (measured 243 us with groups, 238 us without).
 // Chunked-prefill attention (T up to kPrefillMaxT causal query rows per
 // sequence, bf16) on MFMA tiles with LDS-staged keys and values.
 constexpr int kPrefillMaxT = 8192;
@@ -84,19 +54,8 @@ int prefill_piece_tokens(int B, int T, int Hq, int Hkv, int D, int max_blocks, i
 // prefill_workspace_bytes(...) bytes when that is nonzero.
 hipError_t launch_prefill(const DecodeArgs& a, int piece_tokens, float* workspace, hipStream_t stream);
 
-bool groups_enabled();
-// Single-token decode kernel choice, read on each call: PKV_DECODE_TILE=0
-// always takes the VALU stream kernel, =1 always the MFMA tile (where its
-// shapes allow), unset the policy of verify_tile_for.  Returns 0, 1 or -1.
-int decode_tile_mode();
-// Plan inside the decode kernel when the unit list fits in LDS (default;
-// PKV_INLINE_PLAN=0 launches the planning kernel instead).
-bool inline_plan_enabled();
-int device_lds_per_block();
-bool groups_supported(const DecodeArgs& a);
-size_t group_workspace_bytes(int B, int Hq, int D);
-GroupPlan group_plan_layout(void* base, int B, int Hq, int D);
-int device_cus();   // compute units of the current device (cached)
+int device_lds_per_block();   // LDS bytes a workgroup may use on the current device (cached)
+int device_cus();             // compute units of the current device (cached)
 
 // VALU decode kernel: any T (one query token per work item), Hq/Hkv in {1,2,4,8}.
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
@@ -105,11 +64,7 @@ hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
 // the causal limit of query token t, their prefix sums, the range length, the
 // compact list of non-empty pairs (udesc, nu + 1 entries with a sentinel) and
 // each range's first non-empty pair as an index into that list
-// (B*T <= kStreamMaxTB).  hdr = {total, per range, total, group chunks, nu}.
-// With `gp` non-null (T = 1 only) the planning workgroup first detects the
-// shared-prefix groups (gp->sfx, nch, desc), leaves the first sfx[b] blocks of
-// sequence b out of its unit and lists the chunks of every group in
-// gp->clist; hdr[3] receives the number of listed chunks.
+// (B*T <= kStreamMaxTB).  hdr = {total, per range, total, 0, nu}.
 // With `fin` the planning kernel also writes the result of every unit with
 // no visible token (out = 0, lse = -inf), which no decode wave visits.
 struct PlanFinish {
@@ -119,9 +74,7 @@ struct PlanFinish {
   bool bf16;
 };
 hipError_t launch_plan(const int32_t* lens, int B, int T, int ranges, int max_blocks, int* hdr, int* prefix, int* first,
-                       int4* udesc, hipStream_t stream, const GroupPlan* gp = nullptr,
-                       const int32_t* tables = nullptr, int G = 1, const PlanFinish* fin = nullptr,
-                       int4* mdesc = nullptr);
+                       int4* udesc, hipStream_t stream, const PlanFinish* fin = nullptr, int4* mdesc = nullptr);
 
 // MFMA tile for bf16 with T * (Hq/Hkv) <= 16 query rows per KV head (the
 // verify step, and single-token decode when verify_tile_for says so);

@@ -49,10 +49,7 @@ constexpr float kSlack = 8.f;
 // tiles (straight into LDS, so deeper staging costs no registers).  Three
 // stages measured slower than two on the Llama-3-8B-shaped chunked batch
 // (235.3 against 222.6 us) and on one long prompt (123.0 against 117.7 us).
-#ifndef PKV_PREFILL_STAGES
-#define PKV_PREFILL_STAGES 2
-#endif
-constexpr int kStages = PKV_PREFILL_STAGES;
+constexpr int kStages = 2;
 
 typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));

@@ -27,7 +27,6 @@
 #include <type_traits>
 
 #include "pkv_device.h"
-#include "pkv_group.h"
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -36,29 +35,21 @@ namespace {
 constexpr int kBS = 16;
 constexpr int kHPW = 4;              // query heads per work unit
 constexpr int kWaves = kStreamWaves;   // about 8 waves per CU
-#ifndef PKV_STREAM_WPG
-#define PKV_STREAM_WPG 8
-#endif
 // Head groups (waves) per decode workgroup: one workgroup per range and CU
 // (a second workgroup on a CU measured about 8 % slower than the first).
-// The group-capable instantiation uses workgroups of grp::kTiles waves so
-// that a group workgroup fits beside two decode ones.
-constexpr int kMaxU = PKV_STREAM_WPG;
-template <bool GROUPS> constexpr int stream_wpg() { return GROUPS ? grp::kTiles : kMaxU; }
+constexpr int kMaxU = 8;
 constexpr int kMinBlocksPerRange = 16;
 constexpr float kSlack = 8.f;
 
 struct StreamArgs {
   DecodeArgs a;
-  int* hdr;            // [total, per, total, group chunks, nu]
+  int* hdr;            // [total, per, total, unused, nu]
   int* prefix;         // [TB + 1] (written by the planning kernel only)
   int* first;          // [ranges] first non-empty unit (compact index) of each range, -1 if idle
   int4* mdesc;         // [ranges] merge at boundary r: {unit, first range, last range} or x = -1
   int4* udesc;         // [nu + 1] non-empty units: {tb, flat start, table offset, visible tokens}
   float* part;         // partial slots [(ranges + TB)][Hq][D + 1]
-  GroupPlan gp;        // shared-prefix groups (when `groups`)
-  bool groups;
-  int stream_wgs;      // decode workgroups; any further workgroups run group items
+  int stream_wgs;      // decode workgroups
   int TB;
   int ranges;          // workgroups splitting the block list
   bool inl;            // plan computed inside the decode kernel (no planning kernel)
@@ -204,72 +195,48 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
                                                             int ranges, int max_blocks, int TB, int* __restrict__ hdr,
                                                             int* __restrict__ prefix, int* __restrict__ first,
                                                             int4* __restrict__ udesc, int4* __restrict__ mdesc,
-                                                            GroupPlan gp, bool groups,
-                                                            const int32_t* __restrict__ tables, int GM,
                                                             PlanFinish fin, bool finish) {
   __shared__ int part[kPlanThreads];
   __shared__ int npart[kPlanThreads];
-  __shared__ int cpart[kPlanThreads];
   __shared__ int spref[kStreamMaxTB + 1];   // flat start of each non-empty unit
   __shared__ int sid[kStreamMaxTB];         // its unit index
-  __shared__ int ssfx[kGroupMaxB], snch[kGroupMaxB], scnt[kGroupMaxB];
   const int tid = threadIdx.x;
   const int max_tokens = max_blocks * kBS;
-  if (groups) {   // T = 1 and B <= kGroupMaxB: one wave per window of sequences
-    for (int w0 = (tid >> 6) * kGroupWindow; w0 < B; w0 += (kPlanThreads / 64) * kGroupWindow)
-      grp::detect_window(w0, tables, lens, B, max_blocks, GM, gp, ssfx, snch, scnt);
-    __syncthreads();
-  }
   const int per_t = (TB + kPlanThreads - 1) / kPlanThreads;
   const int s0 = min(TB, tid * per_t), s1 = min(TB, s0 + per_t);
-  auto blocks_of = [&](int i, int vis) {
-    const int nb = (vis + kBS - 1) / kBS;
-    return groups ? nb - ssfx[i] : nb;   // groups only with T = 1 (i = b)
-  };
-  int sum = 0, ne = 0, csum = 0;
+  auto blocks_of = [&](int vis) { return (vis + kBS - 1) / kBS; };
+  int sum = 0, ne = 0;
   for (int i = s0; i < s1; ++i) {
-    const int nb = blocks_of(i, unit_visible(lens, i, B, T, max_tokens));
+    const int nb = blocks_of(unit_visible(lens, i, B, T, max_tokens));
     sum += nb;
     ne += nb > 0;
-    if (groups) csum += scnt[i];
   }
   part[tid] = sum;
   npart[tid] = ne;
-  cpart[tid] = csum;
   __syncthreads();
   for (int off = 1; off < kPlanThreads; off <<= 1) {
     const int v = tid >= off ? part[tid - off] : 0;
     const int nv = tid >= off ? npart[tid - off] : 0;
-    const int cv = tid >= off ? cpart[tid - off] : 0;
     __syncthreads();
     part[tid] += v;
     npart[tid] += nv;
-    cpart[tid] += cv;
     __syncthreads();
   }
   int run = tid ? part[tid - 1] : 0;
   int krun = tid ? npart[tid - 1] : 0;
-  int crun = tid ? cpart[tid - 1] : 0;
   for (int i = s0; i < s1; ++i) {
     prefix[i] = run;
     const int vis = unit_visible(lens, i, B, T, max_tokens);
-    const int nb = blocks_of(i, vis);
+    const int nb = blocks_of(vis);
     if (nb > 0) {
       const int b = i % B;
-      const int sb = groups ? ssfx[i] : 0;
-      const bool grouped = groups && snch[i] > 0;
-      // {unit, flat start, table offset of its first block, visible tokens (negative: merged with a group)}
-      udesc[krun] = make_int4(i, run, b * max_blocks + sb, grouped ? -vis : vis);
+      // {unit, flat start, table offset of its first block, visible tokens}
+      udesc[krun] = make_int4(i, run, b * max_blocks, vis);
       spref[krun] = run;
       sid[krun] = i;
       ++krun;
     }
     run += nb;
-    if (groups) {
-      const int c = scnt[i];
-      for (int k = 0; k < c; ++k) gp.clist[crun + k] = i * kGroupChunks + k;
-      crun += c;
-    }
   }
   const int tbtot = part[kPlanThreads - 1];
   const int nu = npart[kPlanThreads - 1];
@@ -284,13 +251,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     hdr[0] = tbtot;
     hdr[1] = per;
     hdr[2] = tbtot;
-    hdr[3] = cpart[kPlanThreads - 1];
+    hdr[3] = 0;
     hdr[4] = nu;
   }
   if (finish) {
     // units with nothing visible: out = 0, lse = -inf
     for (int i = s0; i < s1; ++i) {
-      const int nb = blocks_of(i, unit_visible(lens, i, B, T, max_tokens));
+      const int nb = blocks_of(unit_visible(lens, i, B, T, max_tokens));
       if (nb > 0) continue;
       const int t = i / B, b = i - t * B;
       const size_t row = ((size_t)b * T + t) * fin.Hq;
@@ -434,10 +401,9 @@ constexpr int kResolveAt = 4;   // step of a full chunk at which the next chunk 
 // h, D/16 elements each.  Pieces come from the partial slots of ranges w0 .. w1
 // (slot of range w: w + tb), loaded in batches of BATCH with all loads issued
 // together and merged online (running max, rescaled sum and accumulator).
-// gch > 0 adds that many group partials of sequence b first.
 template <typename ET, int D, int BATCH>
 __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, const float* part, int tb, int u, int w0, int w1,
-                                             int lane, const float* gpart = nullptr, int gch = 0) {
+                                             int lane) {
   constexpr int EPL = D / 16;
   using OT = typename Storage<ET>::T;
   const int t = tb / a.B, b = tb - t * a.B;
@@ -458,21 +424,6 @@ __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, const float* p
     for (int e = 0; e < EPL; ++e) acc[e] = acc[e] * sa_ + sb * ov[e];
     m = nm;
   };
-  if (gch > 0) {
-    float lv[kGroupChunks], ov[kGroupChunks][EPL];
-#pragma unroll
-    for (int k = 0; k < kGroupChunks; ++k) {
-      lv[k] = kNegInf;
-      if (k < gch) {
-        const float* slot = gpart + (((size_t)b * kGroupChunks + k) * a.Hq + u * kHPW + h) * (D + 1);
-        lv[k] = slot[D];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) ov[k][e] = slot[d0 + e];
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kGroupChunks; ++k) absorb(lv[k], ov[k]);
-  }
   for (int w = w0; w <= w1; w += BATCH) {
     float lv[BATCH], ov[BATCH][EPL];
 #pragma unroll
@@ -496,48 +447,23 @@ __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, const float* p
 
 constexpr int kStage = 8;   // units whose descriptors and queries are staged at a time
 
-// GROUPS: the instantiation also runs shared-prefix group items on the
-// workgroups past stream_wgs (bf16, D in {64, 128}, four waves per workgroup).
-template <typename ET, int D, int GW, bool GROUPS>
+template <typename ET, int D, int GW>
 struct StreamLds {
   static constexpr int QCH = SGeo<ET, D, GW>::NC * SGeo<ET, D, GW>::KW;   // distinct 16-byte query chunks per head
   static constexpr int QWAVE = kStage * GW * QCH * 16;                   // staged query bytes per wave
-  static constexpr int QBYTES = stream_wpg<GROUPS>() * QWAVE;
-  static constexpr bool G_OK = GROUPS && std::is_same<ET, Bf16>::value && (D == 64 || D == 128);
-  static constexpr int GBYTES = G_OK ? grp::Stage<D>::BYTES : 0;
-  static constexpr int BYTES = QBYTES > GBYTES ? QBYTES : GBYTES;
 };
-
-// With groups, three waves per SIMD (<= 168 VGPRs): two decode workgroups
-// and one group workgroup per CU.  The widest geometry (one head per KV head,
-// 16 loads per block) keeps two waves per SIMD rather than spill.
-template <typename ET, int D, int GW, bool GROUPS>
-constexpr int stream_waves_per_eu() { return GROUPS && SGeo<ET, D, GW>::LOADS < 16 ? 3 : 2; }
 
 // INL: the plan is computed by the kernel itself (inline_plan) and the unit
 // descriptors are read from LDS; otherwise the planning kernel wrote them to
 // the workspace.  LDS: staged queries (QWAVE bytes per wave), then, with INL,
-// the unit descriptors; dynamic, sized by the launch.  The group-capable
-// instantiation uses a static buffer shared with the group stage.
-template <typename ET, int D, int GW, int PD, bool GROUPS, bool INL>
-__global__ __launch_bounds__(64 * stream_wpg<GROUPS>())
-__attribute__((amdgpu_waves_per_eu(stream_waves_per_eu<ET, D, GW, GROUPS>())))
+// the unit descriptors; dynamic, sized by the launch.
+template <typename ET, int D, int GW, int PD, bool INL>
+__global__ __launch_bounds__(64 * kMaxU) __attribute__((amdgpu_waves_per_eu(2)))
 void stream_decode_kernel(StreamArgs sa, const int4* __restrict__ udesc, float scale_log2e) {
-  static_assert(!(GROUPS && INL), "groups need the planning kernel");
   using G = SGeo<ET, D, GW>;
   using ST = typename Storage<ET>::T;
-  using LD = StreamLds<ET, D, GW, GROUPS>;
-  // one LDS buffer: staged queries on decode workgroups, staged K/V on group ones
-  __shared__ __attribute__((aligned(16))) unsigned char slds[GROUPS ? LD::BYTES : 16];
-  extern __shared__ __attribute__((aligned(16))) unsigned char dlds[];
-  unsigned char* lds = GROUPS ? slds : dlds;
-  if constexpr (LD::G_OK) {
-    if ((int)blockIdx.x >= sa.stream_wgs) {
-      grp::group_items<D>(sa.a, sa.gp, sa.hdr[3] * sa.a.Hkv, blockIdx.x - sa.stream_wgs, gridDim.x - sa.stream_wgs, lds,
-                          scale_log2e);
-      return;
-    }
-  }
+  using LD = StreamLds<ET, D, GW>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const DecodeArgs& a = sa.a;
   const int lane = threadIdx.x & 63;
   const int U = a.Hq / kHPW;
@@ -714,8 +640,8 @@ void stream_decode_kernel(StreamArgs sa, const int4* __restrict__ udesc, float s
     for (int g = 0; g < GW; ++g) qreg[g] = qlds[wave][s][g][kl * G::NC + c];
     const int b = tb % a.B;
     kb_off = (tofs - b * a.max_blocks) - ustart;   // logical block = flat index + kb_off
-    hi = hv < 0 ? -hv : hv;
-    direct = hv >= 0 && ustart >= F0 && uend <= F1;
+    hi = hv;
+    direct = ustart >= F0 && uend <= F1;
     m_lane = kNegInf;
     l_part = 0.f;
 #pragma unroll
@@ -870,36 +796,7 @@ void stream_decode_kernel(StreamArgs sa, const int4* __restrict__ udesc, float s
 // ---------------------------------------------------------------------------
 // Merge the pieces of units cut by wave ranges.
 // ---------------------------------------------------------------------------
-template <typename ET, int D>
-__global__ __launch_bounds__(256) void stream_merge_kernel(StreamArgs sa) {
-  // One wave per (unit, head group): units cut by ranges and, with groups,
-  // every grouped sequence (its group partials plus its own pieces).
-  using OT = typename Storage<ET>::T;
-  const DecodeArgs& a = sa.a;
-  const int lane = threadIdx.x & 63;
-  const int gidx = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int U = a.Hq / kHPW;
-  if (gidx >= U * sa.TB) return;
-  const int per = sa.hdr[1];
-  const int tb = gidx / U, u = gidx - tb * U;
-  const int t = tb / a.B, b = tb - t * a.B;
-  const int pstart = sa.prefix[tb], plen = sa.prefix[tb + 1] - pstart;
-  const int gch = sa.groups ? sa.gp.nch[b] : 0;   // group partials of this sequence (T = 1)
-  if (plen == 0 && gch == 0) {   // nothing visible: out = 0, lse = -inf
-    constexpr int EPL = D / 16;
-    const int h = lane >> 4, d0 = (lane & 15) * EPL;
-    OT* out = static_cast<OT*>(a.out) + (((size_t)b * a.T + t) * a.Hq + u * kHPW + h) * D + d0;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) store_out<ET>(out + e, 0.f);
-    if (a.lse_out && (lane & 15) == 0) a.lse_out[((size_t)b * a.T + t) * a.Hq + u * kHPW + h] = kNegInf;
-    return;
-  }
-  const int w0 = plen ? pstart / per : 0, w1 = plen ? (pstart + plen - 1) / per : -1;
-  if (w0 == w1 && gch == 0) return;   // finished by one range
-  merge_pieces<ET, D, 8>(a, sa.part, tb, u, w0, w1, lane, sa.gp.part, gch);
-}
-
-// Without groups only units cut by range boundaries need a merge, and each
+// Only units cut by range boundaries need a merge, and each
 // boundary cuts at most one unit: the one containing the boundary's first
 // block.  Workgroup (r, j) merges that unit for head groups 4j .. 4j+3 when
 // the unit begins in range r - 1 (its first cut), one wave per head group;
@@ -922,43 +819,26 @@ __global__ __launch_bounds__(256) void boundary_merge_kernel(StreamArgs sa) {
 template <typename ET, int D, int GW>
 hipError_t launch_s(StreamArgs sa, hipStream_t stream) {
   constexpr int LOADS = SGeo<ET, D, GW>::LOADS;
-#ifdef PKV_STREAM_PD
-  constexpr int PD = PKV_STREAM_PD;
-#else
   // One block ahead per wave: with the block stream running across unit
   // boundaries this measured faster than two (8B- and 1B-shaped batches) and
   // needs 60 fewer VGPRs.
   constexpr int PD = 1;
   (void)LOADS;
-#endif
   const float sl2 = sa.a.scale * kLog2e;
   const int U = sa.a.Hq / kHPW;
-  const int wmax = sa.groups ? stream_wpg<true>() : stream_wpg<false>();
-  const int wpg = U < wmax ? U : wmax;
+  const int wpg = U < kMaxU ? U : kMaxU;
   sa.stream_wgs = sa.ranges * (U / wpg);
-  int group_wgs = 0;
-  if (sa.groups) {
-    // persistent group workgroups, one per CU at most (they sit beside the decode ones)
-    const long long items = (long long)(sa.a.B / 2) * kGroupChunks * sa.a.Hkv;
-    group_wgs = (int)(items < device_cus() ? items : device_cus());
-  }
-  using LD = StreamLds<ET, D, GW, false>;
+  using LD = StreamLds<ET, D, GW>;
   const size_t qbytes = (size_t)wpg * LD::QWAVE;
-  if (sa.groups)
-    hipLaunchKernelGGL((stream_decode_kernel<ET, D, GW, PD, true, false>), dim3(sa.stream_wgs + group_wgs),
-                       dim3(64 * wpg), 0, stream, sa, sa.udesc, sl2);
-  else if (sa.inl)
-    hipLaunchKernelGGL((stream_decode_kernel<ET, D, GW, PD, false, true>), dim3(sa.stream_wgs), dim3(64 * wpg),
+  if (sa.inl)
+    hipLaunchKernelGGL((stream_decode_kernel<ET, D, GW, PD, true>), dim3(sa.stream_wgs), dim3(64 * wpg),
                        qbytes + (size_t)kInlineUnitsPerWave * wpg * sizeof(int4), stream, sa, sa.udesc, sl2);
   else
-    hipLaunchKernelGGL((stream_decode_kernel<ET, D, GW, PD, false, false>), dim3(sa.stream_wgs), dim3(64 * wpg), qbytes,
+    hipLaunchKernelGGL((stream_decode_kernel<ET, D, GW, PD, false>), dim3(sa.stream_wgs), dim3(64 * wpg), qbytes,
                        stream, sa, sa.udesc, sl2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (sa.groups) {
-    const int G = U * sa.TB;
-    hipLaunchKernelGGL((stream_merge_kernel<ET, D>), dim3((G + 3) / 4), dim3(256), 0, stream, sa);
-  } else if (sa.ranges > 1) {
+  if (sa.ranges > 1) {
     hipLaunchKernelGGL((boundary_merge_kernel<ET, D>), dim3((sa.ranges - 1) * ((U + 3) / 4)), dim3(256), 0, stream, sa);
   }
   return hipGetLastError();
@@ -980,11 +860,9 @@ hipError_t launch_main(const StreamArgs& sa, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_plan(const int32_t* lens, int B, int T, int ranges, int max_blocks, int* hdr, int* prefix, int* first,
-                       int4* udesc, hipStream_t stream, const GroupPlan* gp, const int32_t* tables, int G,
-                       const PlanFinish* fin, int4* mdesc) {
+                       int4* udesc, hipStream_t stream, const PlanFinish* fin, int4* mdesc) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, lens, B, T, ranges, max_blocks, B * T, hdr,
-                     prefix, first, udesc, mdesc, gp ? *gp : GroupPlan{}, gp != nullptr, tables, group_members(G),
-                     fin ? *fin : PlanFinish{}, fin != nullptr);
+                     prefix, first, udesc, mdesc, fin ? *fin : PlanFinish{}, fin != nullptr);
   return hipGetLastError();
 }
 
@@ -1008,9 +886,7 @@ size_t stream_workspace_bytes(int B, int T, int Hq, int D) {
   off += R * 16;                                          // merge descriptor per boundary
   off += ((TB + 1) * 16 + 255) / 256 * 256;               // unit descriptors
   off += (R + TB) * Hq * (D + 1) * 4;                     // partial slots
-  off = (off + 255) / 256 * 256;
-  if (T == 1) off += group_workspace_bytes(B, Hq, D);     // shared-prefix groups
-  return off;
+  return (off + 255) / 256 * 256;
 }
 
 bool stream_supported(const DecodeArgs& a) {
@@ -1036,26 +912,15 @@ hipError_t launch_decode_stream(const DecodeArgs& a, void* workspace, hipStream_
   float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(udesc) +
                                          ((size_t)(sa.TB + 1) * 16 + 255) / 256 * 256);
   sa.hdr = hdr; sa.prefix = prefix; sa.first = first; sa.mdesc = mdesc; sa.udesc = udesc; sa.part = part;
-  hipError_t e;
   const int U = a.Hq / kHPW;
-#ifndef PKV_NO_GROUPS
-  sa.groups = groups_enabled() && groups_supported(a) && U % grp::kTiles == 0;
-#endif
-  const size_t part_bytes = ((size_t)stream_ranges(a.Hq) + sa.TB) * a.Hq * (a.D + 1) * 4;
-  unsigned char* after_part = reinterpret_cast<unsigned char*>(part) + (part_bytes + 255) / 256 * 256;
-  if (sa.groups) {
-    sa.gp = group_plan_layout(after_part, a.B, a.Hq, a.D);
-    e = launch_plan(a.context_lens, a.B, a.T, sa.ranges, a.max_blocks, hdr, prefix, first, udesc, stream, &sa.gp,
-                    a.block_tables, a.Hq / a.Hkv);
-  } else {
-    const int wpg = U < kMaxU ? U : kMaxU;
-    sa.inl = inline_plan_enabled() && sa.TB + 1 <= kInlineUnitsPerWave * wpg &&
-             inline_lds_bytes(a, wpg) <= (size_t)device_lds_per_block();
-    const PlanFinish fin{a.out, a.lse_out, a.Hq, a.D, a.bf16};
-    e = sa.inl ? hipSuccess
-               : launch_plan(a.context_lens, a.B, a.T, sa.ranges, a.max_blocks, hdr, prefix, first, udesc, stream,
-                             nullptr, nullptr, 1, &fin, mdesc);
-  }
+  const int wpg = U < kMaxU ? U : kMaxU;
+  // the plan is computed inside the decode kernel when the unit list fits in
+  // its LDS, else by a planning launch first
+  sa.inl = sa.TB + 1 <= kInlineUnitsPerWave * wpg && inline_lds_bytes(a, wpg) <= (size_t)device_lds_per_block();
+  const PlanFinish fin{a.out, a.lse_out, a.Hq, a.D, a.bf16};
+  const hipError_t e = sa.inl ? hipSuccess
+                              : launch_plan(a.context_lens, a.B, a.T, sa.ranges, a.max_blocks, hdr, prefix, first,
+                                            udesc, stream, &fin, mdesc);
   if (e != hipSuccess) return e;
   return launch_main(sa, stream);
 }

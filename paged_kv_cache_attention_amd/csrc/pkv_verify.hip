@@ -283,23 +283,16 @@ bool verify_mfma_supported(const DecodeArgs& a) {
          (a.Hkv <= kMaxWpg || a.Hkv % kMaxWpg == 0) && (long long)a.B * a.max_blocks < (1ll << 30);
 }
 
-// Multi-token steps always take the tile.  Single-token decode takes it too
-// (its T = 1 rows are the G query heads of a KV head, 1 to 8 of the 16 tile
-// rows) unless the shared-prefix groups are switched on, which live in the
-// stream kernel, or the batch's table holds fewer blocks than the grid has
-// waves.  Measured against the VALU stream kernel at T = 1: faster for every
-// head group size at D = 64 (Llama-3.2-1B shape 57.0 -> 55.1 us; 64 query
-// heads over 8 KV heads 97.0 -> 66.5 us) and for the 8B shared-prefix batch
-// (222.7 -> 217.9 us); about 3 % slower on a 64-sequence D = 128, G = 4 batch
-// without shared blocks, and slower on an 8-sequence batch of 1,681 tokens
-// (hence the size floor).
-bool verify_tile_for(const DecodeArgs& a) {
-  if (!verify_mfma_supported(a)) return false;
-  if (a.T >= 2) return true;
-  const int mode = decode_tile_mode();
-  if (mode >= 0) return mode == 1;
-  return !groups_enabled() && (long long)a.B * a.max_blocks >= kStreamWaves;
-}
+// Every shape the tile supports takes it, single-token decode included (its
+// T = 1 rows are the G query heads of a KV head, 1 to 8 of the 16 tile rows).
+// Measured against the VALU stream kernel at T = 1: faster for every head
+// group size at D = 64 (Llama-3.2-1B shape 57.0 -> 55.1 us; 64 query heads
+// over 8 KV heads 97.0 -> 66.5 us) and for the 8B shared-prefix batch
+// (222.7 -> 217.9 us); about 3 % slower on a 64-sequence D = 128, G = 4
+// batch without shared blocks, and 1.2 us slower on an 8-sequence batch of
+// 1,681 tokens.  The stream kernel serves fp32 and the shapes with more than
+// 16 query rows per KV head.
+bool verify_tile_for(const DecodeArgs& a) { return verify_mfma_supported(a); }
 
 size_t verify_workspace_bytes(int B, int T, int Hq, int D) {
   const size_t R = kStreamWaves;   // upper bound on ranges (Hkv = 1)
@@ -337,8 +330,7 @@ hipError_t launch_verify_mfma(const DecodeArgs& a, void* workspace, hipStream_t 
   while (wpg % 2 == 0 && (size_t)wpg * tile_bytes + 64 > (size_t)device_lds_per_block()) wpg /= 2;
   const size_t tiles = (size_t)wpg * tile_bytes;
   const size_t lds_inl = tiles + (size_t)kInlinePerWave * wpg * 4;
-  const bool inl = inline_plan_enabled() && a.B + 1 <= kInlinePerWave * wpg &&
-                   lds_inl + 64 <= (size_t)device_lds_per_block();
+  const bool inl = a.B + 1 <= kInlinePerWave * wpg && lds_inl + 64 <= (size_t)device_lds_per_block();
   hipError_t e = hipSuccess;
   // one unit per sequence: blocks = ceil(L / 16)
   if (!inl) e = launch_plan(a.context_lens, a.B, 1, va.ranges, a.max_blocks, hdr, prefix, first, udesc, stream);

@@ -62,11 +62,20 @@ def appended_oracle_pools(w):
     return kp, vp
 
 
+def max_abs_finite(w, arr):
+    """Largest finite |value| of a storage array (NaN poison ignored)."""
+    if w.dtype == "bf16":   # on the bit patterns: |x| orders like its low 15 bits
+        mag = np.asarray(arr, dtype=np.uint16).ravel() & np.uint16(0x7FFF)
+        mag = mag[mag < 0x7F80]
+        return float(w.values(mag.max(initial=0).astype(np.uint16)))
+    return float(np.nanmax(np.abs(np.asarray(arr, dtype=np.float32))))
+
+
 def mfma_floor(w):
     """Near-zero floor of the MFMA tiles for workload w: 2^-16 max |V| (+ ULP_FLOOR)."""
-    vmax = float(np.nanmax(np.abs(w.values(w.v_pool))))
+    vmax = max_abs_finite(w, w.v_pool)
     if w.v_new is not None:
-        vmax = max(vmax, float(np.nanmax(np.abs(w.values(w.v_new)))))
+        vmax = max(vmax, max_abs_finite(w, w.v_new))
     return MFMA_P_REL * vmax + ULP_FLOOR
 
 
@@ -106,7 +115,59 @@ def assert_within_bf16_ulp(got, base, where=""):
 def check_lse(got, ref, where=""):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape
     both_inf = np.isneginf(got) & np.isneginf(ref)
-    d = np.abs(np.where(both_inf, 0.0, got - ref))
-    assert np.isfinite(d).all() and d.max() <= LSE_ATOL + 1e-6 * np.abs(np.where(both_inf, 0, ref)).max(), \
-        f"{where}: lse max abs {d.max():.3e}"
+    # empty rows must be -inf on both sides; they are taken out before subtracting
+    g = np.where(both_inf, 0.0, got)
+    r = np.where(both_inf, 0.0, ref)
+    assert np.isfinite(g).all() and np.isfinite(r).all(), f"{where}: lse -inf/NaN where the other side is finite"
+    d = np.abs(g - r)
+    assert d.max(initial=0.0) <= LSE_ATOL + 1e-6 * np.abs(r).max(initial=0.0), f"{where}: lse max abs {d.max():.3e}"
+
+
+def _compact(w, b, k_vals=None, v_vals=None):
+    """Sequence b's own blocks as a small pool with table 0 .. nb-1 (a
+    relabelling of physical ids, which leaves attention unchanged), widened
+    from storage only for those blocks unless float pools are given."""
+    nb = -(-int(w.context_lens[b]) // w.block_size)
+    ids = np.asarray(w.block_tables[b, :nb], dtype=np.int64)
+    kp = k_vals[ids] if k_vals is not None else w.values(w.k_pool[ids])
+    vp = v_vals[ids] if v_vals is not None else w.values(w.v_pool[ids])
+    return kp, vp, np.arange(nb, dtype=np.int64)[None, :]
+
+
+def oracle_by_sequence(w, seqs=None, k_vals=None, v_vals=None, partition_size=0, threads=8):
+    """The oracle on each listed sequence (all by default), one compact pool
+    per sequence, in a thread pool.  Returns (out, lse) stacked over seqs, or
+    with partition_size > 0 the oracle's partition partials (o, lse) with
+    P_max = ceil(max_blocks * block_size / partition_size)."""
+    from concurrent.futures import ThreadPoolExecutor
+    seqs = list(range(w.B)) if seqs is None else list(seqs)
+    qv = w.values(w.q)
+    P_max = -(-w.max_blocks * w.block_size // partition_size) if partition_size else 0
+
+    def one(b):
+        kp, vp, tab = _compact(w, b, k_vals, v_vals)
+        args = (qv[b:b + 1], kp, vp, tab, w.context_lens[b:b + 1], w.scale, w.block_size)
+        if partition_size:
+            return oracle.partition_attention(*args, partition_size, num_parts=P_max)
+        return oracle.paged_attention(*args)
+
+    with ThreadPoolExecutor(max(1, min(threads, len(seqs)))) as ex:
+        res = list(ex.map(one, seqs))
+    return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res])
+
+
+def check_partials(got_o, got_l, ref_o, ref_l, vmax, where):
+    """fp32 split-KV partials (normalised o_p and lse_p) against the oracle's.
+    Gate for o_p: 2^-16 max|V| (the MFMA tiles' hi + lo split of P) + 2e-6
+    (fp32 accumulation); empty partitions must be exactly (0, -inf)."""
+    got_o = np.asarray(got_o, dtype=np.float64)
+    ref_o = np.asarray(ref_o, dtype=np.float64)
+    check_lse(got_l, ref_l, where)
+    empty = np.isneginf(np.asarray(ref_l))
+    assert not got_o[empty].any(), f"{where}: empty partition with nonzero o"
+    err = np.abs(got_o - ref_o)
+    gate = MFMA_P_REL * vmax + 2e-6
+    assert np.isfinite(got_o).all() and err.max(initial=0.0) <= gate, \
+        f"{where}: partial max abs {err.max():.3e} > {gate:.3e}"

@@ -418,11 +418,31 @@ def pin_bf16_rounding():
     assert oracle.round_to_bf16(np.array([1.0 + 3 * 2 ** -8]))[0] == 1.0 + 2 ** -6
 
 
+def pin_bf16_ulp():
+    """The spacing of bf16 values, which sets every bf16 gate of the GPU tests.
+
+    Hand values: bf16 keeps 8 significant bits, so the spacing in the binade
+    [2^k, 2^(k+1)) is 2^(k-7): 1.0 -> 2^-7, 0.75 -> 2^-8, 3.0 -> 2^-6,
+    1e-3 (in [2^-10, 2^-9)) -> 2^-17, and the sign does not matter.  Then, for
+    every positive normal bf16 value below the largest, the spacing equals the
+    gap to the next bf16 value, taken from the generator's bit arithmetic
+    (the value of bit pattern u + 1 minus that of u)."""
+    hand = {1.0: 2.0 ** -7, 0.75: 2.0 ** -8, 3.0: 2.0 ** -6, 1e-3: 2.0 ** -17, -1.5: 2.0 ** -7,
+            2.0 ** -126: 2.0 ** -133, 255.0: 1.0, 256.0: 2.0}
+    for x, want in hand.items():
+        assert oracle.bf16_ulp(np.array([x]))[0] == want, (x, want)
+    bits = np.arange(0x0080, 0x7F7F, dtype=np.uint32)           # positive normal, below the largest finite
+    vals = workload.bf16_bits_to_f32(bits.astype(np.uint16)).astype(np.float64)
+    nxt = workload.bf16_bits_to_f32((bits + 1).astype(np.uint16)).astype(np.float64)
+    np.testing.assert_array_equal(oracle.bf16_ulp(vals), nxt - vals)
+    np.testing.assert_array_equal(oracle.bf16_ulp(-vals), nxt - vals)
+
+
 ALL_PINS = [
     pin_golden_two_token, pin_golden_gqa_causal_verify, pin_golden_gqa_head_mapping, pin_golden_lse_merge,
     pin_gather_inverse_scatter, pin_append_then_gather, pin_torch_sdpa_decode, pin_torch_sdpa_causal_verify,
     pin_torch_sdpa_chunked_prefill, pin_rope_hand_values, pin_rope_relative_position, pin_rope_append_positions,
     pin_brute_force_fsum, pin_closed_forms, pin_dominant_score, pin_key_shift_invariance,
     pin_physical_permutation, pin_gqa_equals_repeated_mha, pin_verify_equals_decode_chain,
-    pin_split_equals_full, pin_lse_merge_algebra, pin_bf16_rounding,
+    pin_split_equals_full, pin_lse_merge_algebra, pin_bf16_rounding, pin_bf16_ulp,
 ]

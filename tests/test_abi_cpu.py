@@ -192,3 +192,39 @@ def test_misaligned_tensors_rejected():
     assert lib.paged_kv_copy_blocks(P, odd, P, P, 1, 8, 64, 16, 8, pkv.PKV_BF16, None) == pkv.PKV_EINVAL
     assert lib.paged_kv_gather(P, P, P, P, odd, P, 2, 64, 8, 64, 16, 4, 8, pkv.PKV_BF16, None) == pkv.PKV_EINVAL
     assert "16-byte" in lib.pkv_last_error().decode()
+
+
+def test_binding_checks_attention_arguments():
+    """The binding rejects tensors whose dtype, shape or device disagree before
+    any pointer reaches the library (metadata only, CPU tensors)."""
+    import torch
+    B, T, Hq, Hkv, D, N = 3, 2, 8, 2, 64, 10
+    bf = torch.bfloat16
+    q = torch.zeros(B, T, Hq, D, dtype=bf)
+    kp = torch.zeros(N, 16, Hkv, D, dtype=bf)
+    tab = torch.zeros(B, 4, dtype=torch.int32)
+    lens = torch.ones(B, dtype=torch.int32)
+    ok = dict(q=q, k_pool=kp, v_pool=kp.clone(), block_tables=tab, context_lens=lens,
+              out=torch.zeros_like(q), lse_out=torch.zeros(B, T, Hq))
+    pkv.check_attention_args(**ok)
+    bad = [
+        (dict(q=q.float()), TypeError),                                       # fp32 q, bf16 pools
+        (dict(out=torch.zeros(B, T, Hq, D)), TypeError),                       # fp32 out, bf16 q
+        (dict(v_pool=torch.zeros(N, 16, Hkv, 2 * D, dtype=bf)), ValueError),   # pools differ
+        (dict(k_pool=torch.zeros(N, 16, Hkv, 2 * D, dtype=bf),
+              v_pool=torch.zeros(N, 16, Hkv, 2 * D, dtype=bf)), ValueError),   # head size differs from q
+        (dict(k_pool=torch.zeros(N, 16, 3, D, dtype=bf), v_pool=torch.zeros(N, 16, 3, D, dtype=bf)), ValueError),
+        (dict(out=torch.zeros(B, T, Hq, D // 2, dtype=bf)), ValueError),
+        (dict(lse_out=torch.zeros(B, T, Hq, dtype=torch.float64)), ValueError),
+        (dict(lse_out=torch.zeros(B, Hq)), ValueError),
+        (dict(block_tables=torch.zeros(B * 4, dtype=torch.int32)), ValueError),
+        (dict(block_tables=torch.zeros(B + 1, 4, dtype=torch.int32)), ValueError),
+        (dict(block_tables=tab.long()), TypeError),
+        (dict(context_lens=torch.ones(B + 1, dtype=torch.int32)), ValueError),
+        (dict(context_lens=lens.long()), TypeError),
+        (dict(q=q[0]), ValueError),
+        (dict(lse_out=torch.zeros(B, T, Hq, device="meta")), ValueError),    # two devices
+    ]
+    for change, exc in bad:
+        with pytest.raises(exc):
+            pkv.check_attention_args(**dict(ok, **change))

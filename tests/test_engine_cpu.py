@@ -201,3 +201,39 @@ def test_randomised_workloads_keep_every_invariant(seed):
         assert np.array_equal(streams[rid], expected_stream(rid, p, m))
     assert all(r == 0 for r in refs)
     assert st["free_blocks"] + st["cached_blocks"] == pool
+
+
+def test_copy_sources_never_reused_as_destinations_in_one_plan():
+    """A partly filled cached block that an admission copies from must not be
+    handed out again in the same plan.  Pool of 4 blocks of 4 tokens: A
+    [1..6] and B [21..23] finish and stay cached; then C [1..7] reuses A's
+    blocks (copying A's partly filled second block) and D [21..24] reuses B's
+    partly filled block.  Had C's copy source gone back to the evictable list
+    at once, D's copy would have taken it as its destination in the same plan
+    (sources {a1, b0}, destinations {free, a1})."""
+    eng = pkv.Engine(4, 4, max_blocks_per_seq=4, max_running=4, max_prefill_tokens=64, prefix_cache=True)
+    dev = FakeDevice(4, 4)
+    plans = []
+
+    def drain():
+        for _ in range(100):
+            plan = eng.schedule()
+            if plan.n == 0:
+                return
+            plans.append(plan)
+            src, dst = set(plan.copy_src.tolist()), set(plan.copy_dst.tolist())
+            assert not src & dst, f"plan copies {plan.copy_src} -> {plan.copy_dst}"
+            eng.commit(dev.execute(eng, plan))
+
+    eng.add_request(1, [1, 2, 3, 4, 5, 6], 1)
+    eng.add_request(2, [21, 22, 23], 1)
+    drain()
+    eng.add_request(3, [1, 2, 3, 4, 5, 6, 7], 1)
+    eng.add_request(4, [21, 22, 23, 24], 1)
+    drain()
+    st = eng.stats()
+    assert st["finished"] == 4 and st["cow_copies"] >= 2 and st["prefix_hit_tokens"] >= 9
+    for rid, p in ((3, [1, 2, 3, 4, 5, 6, 7]), (4, [21, 22, 23, 24])):
+        assert np.array_equal(eng.request_tokens(rid), expected_stream(rid, p, 1))
+    assert all(eng.block_ref(b) == 0 for b in range(4))
+    eng.close()

@@ -41,14 +41,6 @@ SHAPES = [  # (dtype, D, Hq, Hkv, T)
 ]
 
 
-
-@pytest.fixture(autouse=True, params=["tile", "stream"])
-def decode_kernel(request, monkeypatch):
-    """Single-token decode through the MFMA tile and through the VALU stream
-    kernel (PKV_DECODE_TILE, read by the library on each call)."""
-    monkeypatch.setenv("PKV_DECODE_TILE", "1" if request.param == "tile" else "0")
-    return request.param
-
 @pytest.mark.parametrize("dtype,D,Hq,Hkv,T", SHAPES)
 @pytest.mark.parametrize("part", [0, 32])
 def test_shapes_and_edge_lengths(dtype, D, Hq, Hkv, T, part):

@@ -12,7 +12,8 @@ import torch
 import oracle
 import workload
 import paged_kv_cache_attention_amd as pkv
-from gpu_util import (appended_oracle_pools, check_attention, check_lse, dev, host, oracle_inputs, upload)
+from gpu_util import (appended_oracle_pools, check_attention, check_lse, check_partials, dev, host, mfma_floor,
+                      oracle_by_sequence, oracle_inputs, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -20,14 +21,6 @@ pytestmark = pytest.mark.gpu
 def say(*a):
     print(*a, flush=True)
 
-
-
-@pytest.fixture(autouse=True, params=["tile", "stream"])
-def decode_kernel(request, monkeypatch):
-    """Single-token decode through the MFMA tile and through the VALU stream
-    kernel (PKV_DECODE_TILE, read by the library on each call)."""
-    monkeypatch.setenv("PKV_DECODE_TILE", "1" if request.param == "tile" else "0")
-    return request.param
 
 @pytest.fixture(scope="module")
 def c1():
@@ -139,24 +132,66 @@ def test_llama1b_append_then_decode(c3, part):
 
 
 def test_llama8b_prefix_share_full():
+    """The 8B-shaped prefix-sharing batch at full size, in the launch
+    configuration the benchmark times: every one of the 256 sequences against
+    the oracle."""
     w = workload.llama8b_prefix_share()
-    say("decode llama8b_prefix_share partition", w.partition_size)
+    say("decode llama8b_prefix_share, all sequences")
     d = upload(w)
     out, lse = run_decode(w, d)
-    seqs = list(range(0, w.B, 5)) + [int(np.argmax(w.context_lens))]
-    ref, ref_lse = oracle.paged_attention(*oracle_inputs(w, seqs), w.scale, w.block_size)
-    check_attention(host(out)[seqs], ref, "bf16", "llama8b")
-    check_lse(host(lse)[seqs], ref_lse, "llama8b")
+    ref, ref_lse = oracle_by_sequence(w)
+    check_attention(host(out), ref, "bf16", "llama8b", floor=mfma_floor(w))
+    check_lse(host(lse), ref_lse, "llama8b")
 
 
-def test_longctx_verify_full():
+@pytest.fixture(scope="module")
+def c5():
+    """The long-context verify batch (16 sequences of 16K-64K tokens, T = 4),
+    uploaded once, with the oracle's result for every sequence."""
     w = workload.longctx_verify()
-    say("verify longctx partition", w.partition_size, "lens", list(w.context_lens))
-    d = upload(w)
-    out, lse = run_decode(w, d)
-    got, got_lse = host(out), host(lse)
-    for b in [0, int(np.argmax(w.context_lens)), 7]:
-        ref, ref_lse = oracle.paged_attention(*oracle_inputs(w, [b]), w.scale, w.block_size)
-        check_attention(got[[b]], ref, "bf16", f"longctx b={b}")
-        check_lse(got_lse[[b]], ref_lse, f"longctx b={b}")
-        say("  sequence", b, "ok")
+    say("longctx lens", list(w.context_lens))
+    ref = oracle_by_sequence(w)
+    return w, upload(w), ref
+
+
+def test_longctx_verify_full(c5):
+    """Single pass (balanced split): all 16 sequences against the oracle."""
+    w, d, (ref, ref_lse) = c5
+    say("verify longctx, partition 0")
+    out, lse = run_decode(w, d, partition_size=0)
+    check_attention(host(out), ref, "bf16", "longctx part=0", floor=mfma_floor(w))
+    check_lse(host(lse), ref_lse, "longctx part=0")
+
+
+def test_longctx_verify_512_token_partitions(c5):
+    """As configured: the KV split into 512-token partitions from position 0,
+    each emitting a normalised partial and its log-sum-exp, merged by
+    log-sum-exp.  Output and lse of all 16 sequences against the oracle, and
+    the partials left in the workspace against the oracle's partitions for
+    the two sequences with the most partitions (P_b > 64, so the merge runs
+    its chunked loop over more than 64 partials)."""
+    w, d, (ref, ref_lse) = c5
+    part = 512
+    ws_bytes = pkv.pkv_decode_workspace_bytes(w.B, w.T, w.Hq, w.D, w.max_blocks, w.block_size, part)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    lse = torch.full((w.B, w.T, w.Hq), float("nan"), dtype=torch.float32, device="cuda")
+    say("verify longctx, partition 512")
+    out = pkv.paged_attention_decode(d["q"], d["k"], d["v"], d["tables"], d["lens"], lse_out=lse,
+                                     scale=float(w.scale), partition_size=part, workspace=ws)
+    torch.cuda.synchronize()
+    check_attention(host(out), ref, "bf16", "longctx part=512", floor=mfma_floor(w))
+    check_lse(host(lse), ref_lse, "longctx part=512")
+    P_max = -(-w.max_blocks * w.block_size // part)
+    rows = w.B * w.T * w.Hq
+    po = ws[: rows * P_max * w.D * 4].view(torch.float32).view(w.B, w.T, w.Hq, P_max, w.D)
+    pl = ws[rows * P_max * w.D * 4: rows * P_max * (w.D + 1) * 4].view(torch.float32).view(w.B, w.T, w.Hq, P_max)
+    Pb = -(-w.context_lens.astype(np.int64) // part)
+    seqs = [int(b) for b in np.argsort(-Pb, kind="stable")[:2]]
+    assert all(Pb[b] > 64 for b in seqs)
+    ref_o, ref_l = oracle_by_sequence(w, seqs, partition_size=part)
+    vmax = float(np.abs(w.values(w.v_pool[w.block_tables[seqs].ravel()])).max())
+    for i, b in enumerate(seqs):
+        n = int(Pb[b])
+        say("  partials of sequence", b, "P_b", n)
+        check_partials(host(po[b, :, :, :n]), host(pl[b, :, :, :n]), ref_o[i, :, :, :n], ref_l[i, :, :, :n], vmax,
+                       f"longctx partials b={b}")

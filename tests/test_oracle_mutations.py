@@ -45,6 +45,18 @@ def _round_truncate(x):
     return np.where(np.isfinite(x), np.ldexp(np.trunc(m * 256.0), e - 8), x)
 
 
+def _ulp_one_bit_short(x):
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    _, e = np.frexp(np.where(x > 0, x, 1.0))
+    return np.ldexp(1.0, e - 7)
+
+
+def _ulp_of_next_binade(x):
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    _, e = np.frexp(np.where(x > 0, x, 1.0))
+    return np.ldexp(1.0, e - 7 - (x < 1.0))
+
+
 _orig_row = oa.softmax_attention_row
 _orig_combine = oa.lse_combine
 
@@ -59,6 +71,8 @@ MUTATIONS = {
     "missing_normalisation": ("softmax_attention_row", _row_no_normalise),
     "lse_merge_wrong_sign": ("lse_combine", _combine_wrong_sign),
     "bf16_truncates": ("round_to_bf16", _round_truncate),
+    "bf16_ulp_doubled": ("bf16_ulp", _ulp_one_bit_short),
+    "bf16_ulp_wrong_above_one": ("bf16_ulp", _ulp_of_next_binade),
 }
 
 

@@ -357,6 +357,10 @@ def llama8b_long_prompt_chunk(poison=True, partition_size=0, structure_only=Fals
                    structure_only=structure_only)
 
 
+# Seed of each named workload (its PCG64 stream; also the workload number).
+WORKLOAD_SEEDS = {"tiny_fp32": 1, "tinylm_mha_bf16": 2, "llama1b_gqa_append": 3, "llama8b_prefix_share": 4,
+                  "longctx_verify": 5, "llama8b_chunked_prefill": 6, "llama8b_long_prompt_chunk": 7}
+
 WORKLOADS = {
     "tiny_fp32": tiny_fp32,
     "tinylm_mha_bf16": tinylm_mha_bf16,
