@@ -182,7 +182,9 @@ def hipcc_version():
 def provenance(torch, w, hipcc):
     """What produced the numbers: device, ROCm and hipcc versions, commit, seed, host CPU."""
     from paged_kv_cache_attention_amd import build as pkv_build
-    info = {"gpu": torch.cuda.get_device_name(0), "torch": torch.__version__, "torch_hip": torch.version.hip,
+    props = torch.cuda.get_device_properties(0)
+    info = {"gpu": torch.cuda.get_device_name(0), "gpu_arch": getattr(props, "gcnArchName", None),
+            "gpu_cus": props.multi_processor_count, "torch": torch.__version__, "torch_hip": torch.version.hip,
             "hipcc": hipcc, "seed": workload.WORKLOAD_SEEDS.get(w.name), "host_cpu": cpu_model(),
             "host_cores": host_cores()}
     try:

@@ -71,7 +71,11 @@ typedef enum {
 
 typedef enum {
   PKV_FP32 = 0, /* float32 storage; accumulation in float32 */
-  PKV_BF16 = 1  /* bfloat16 storage; accumulation in float32, output rounded to nearest even */
+  PKV_BF16 = 1, /* bfloat16 storage; accumulation in float32, output rounded to nearest even */
+  /* Not a dtype: makes every int value representable in a pkv_dtype, so that
+   * the library can reject an unknown value (PKV_EINVAL) instead of receiving
+   * a value outside the enumeration's range. */
+  PKV_DTYPE_INT_RANGE_ = 0x7fffffff
 } pkv_dtype;
 
 /*
@@ -147,13 +151,15 @@ pkv_status paged_kv_copy_blocks(void* k_pool, void* v_pool, const int32_t* src, 
 /*
  * pkv_decode_workspace_bytes -- bytes of device workspace paged_attention_decode
  * needs for these sizes and this partition size.  With partition_size > 0 the
- * split-KV partials use B*T*Hq*P_max*(D+1) float32 values, where
- * P_max = ceil(max_blocks * block_size / partition_size).  With
- * partition_size = 0 the workspace holds the plan of the balanced split
- * (a header, per-unit prefix sums and descriptors) and one normalised partial
- * per (range, unit) piece: (ranges + B*T) * Hq * (D+1) float32 values, where
- * ranges = 2048 / (Hq/4) (256 at Hq = 32), plus the shared-prefix group area
- * when T = 1.  Returns 0 for invalid sizes.
+ * workspace starts with the split-KV partials, B*T*Hq*P_max*(D+1) float32
+ * values where P_max = ceil(max_blocks * block_size / partition_size); the
+ * MFMA tile adds its plan (a header and per-sequence prefix sums) and two
+ * normalised piece slots per range, at most 2*2048*min(16, T*Hq)*(D+1)
+ * float32 values.  With partition_size = 0 the workspace holds the plan of the
+ * balanced split (a header, per-unit prefix sums and descriptors) and one
+ * normalised partial per (range, unit) piece: (ranges + B*T) * Hq * (D+1)
+ * float32 values, where ranges = 2048 / (Hq/4) (256 at Hq = 32).  Returns 0
+ * for invalid sizes.
  */
 size_t pkv_decode_workspace_bytes(int B, int T, int Hq, int D, int max_blocks, int block_size,
                                   int partition_size);
@@ -185,13 +191,18 @@ size_t pkv_decode_workspace_bytes(int B, int T, int Hq, int D, int max_blocks, i
  * partition_size > 0 (a multiple of block_size) splits every sequence into
  * partitions of that many tokens starting at position 0; each partition
  * emits a normalised partial output and its log-sum-exp into `workspace`,
- * and a second kernel merges them as lse_reduce does.  Sequences that fit in
- * one partition are written straight to `out`.  After a split call, the
- * workspace holds, for every (b, t, h) whose sequence has P_b =
- * ceil(L / partition_size) > 1 partitions, part_out [B, T, Hq, P_max, D]
- * float32 at offset 0 followed by part_lse [B, T, Hq, P_max] float32, valid
- * for p < P_b; everything else in it is unspecified.  A partition with no
- * visible token for a query row has part_lse = -inf and part_out = 0.
+ * and a second kernel merges them as lse_reduce does ("Inference From
+ * Scratch", Chapters table, ch. 8: softmax over pieces combines through the
+ * running max and sum).  On the MFMA tile shapes the partitions are spread
+ * over the balanced ranges above (a partition cut by a range boundary is
+ * rebuilt from its pieces by the merge kernel); other shapes run one
+ * workgroup per partition.  Sequences with one partition are written
+ * straight to `out`.  After a split call, the workspace holds, for every
+ * (b, t, h) whose sequence has P_b = ceil(L / partition_size) > 1
+ * partitions, part_out [B, T, Hq, P_max, D] float32 at offset 0 followed by
+ * part_lse [B, T, Hq, P_max] float32, valid for p < P_b; everything else in it
+ * is unspecified.  A partition with no visible token for a query row has
+ * part_lse = -inf and part_out = 0.
  *
  * out must not alias any input.  The workspace must be at least
  * pkv_decode_workspace_bytes(...) bytes of device memory (else PKV_EWORKSPACE);

@@ -110,5 +110,40 @@ def build(verbose: bool = False) -> pathlib.Path:
     return LIB
 
 
+SANITIZED_LIB = OBJ_DIR / "libpkv_host_sanitized.so"
+# Host code only: device code is built as usual; each -fsanitize= applies to
+# the host pass through -Xarch_host.
+SANITIZE_FLAGS = ["-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def sanitizer_runtime() -> pathlib.Path:
+    """The ASan runtime of ROCm's clang (it carries the UBSan handlers too);
+    a process loading the sanitized library preloads it."""
+    rts = sorted(pathlib.Path("/opt/rocm/llvm/lib/clang").glob("*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not rts:
+        raise RuntimeError("no libclang_rt.asan-x86_64.so under /opt/rocm/llvm/lib/clang")
+    return rts[-1]
+
+
+def build_sanitized(verbose: bool = False) -> pathlib.Path:
+    """libpkv with the host code (engine, argument checks, launchers) built
+    with AddressSanitizer and UndefinedBehaviorSanitizer, for the CPU tests."""
+    OBJ_DIR.mkdir(exist_ok=True)
+    from concurrent.futures import ThreadPoolExecutor
+
+    def obj(src):
+        return OBJ_DIR / (src + ".san.o")
+    jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(jobs) as ex:
+        list(ex.map(lambda src: _compile([hipcc(), *FLAGS, *SANITIZE_FLAGS, "-c", f"-I{INCLUDE}", f"-I{CSRC}", "-o",
+                                          str(obj(src)), str(CSRC / src)], verbose), SOURCES))
+    tmp = SANITIZED_LIB.with_suffix(".so.tmp")
+    _compile([hipcc(), *FLAGS, *SANITIZE_FLAGS, "-shared", "-o", str(tmp), *[str(obj(src)) for src in SOURCES]],
+             verbose)
+    os.replace(tmp, SANITIZED_LIB)
+    return SANITIZED_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

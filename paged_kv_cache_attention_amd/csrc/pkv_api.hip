@@ -70,8 +70,8 @@ int* debug_flag() {
 }
 
 pkv_status debug_validate(const int32_t* tables, const int32_t* lens, int B, int T, int len_add, int block_size,
-                          int max_blocks, int N_blocks, hipStream_t s) {
-  int* flag = debug_flag();
+                          int max_blocks, int N_blocks, hipStream_t s, int* flag = nullptr) {
+  if (!flag) flag = debug_flag();
   if (!flag) return fail(PKV_EHIP, "PKV_DEBUG: cannot allocate the check flag");
   pkv_status st = from_hip(hipMemsetAsync(flag, 0, sizeof(int), s), "PKV_DEBUG memset");
   if (st != PKV_OK) return st;
@@ -111,9 +111,11 @@ size_t pkv_decode_workspace_bytes(int B, int T, int Hq, int D, int max_blocks, i
     const size_t a = pkv::stream_workspace_bytes(B, T, Hq, D), b = pkv::verify_workspace_bytes(B, T, Hq, D);
     return a > b ? a : b;
   }
+  // the documented partials, then (for the MFMA tile) its plan and piece slots
   const unsigned long long P = (unsigned long long)partitions_max(max_blocks, block_size, partition_size);
   const unsigned long long rows = (unsigned long long)B * T * Hq;
-  return (size_t)(rows * P * (unsigned long long)(D + 1) * 4ull);
+  const size_t partials = (size_t)(rows * P * (unsigned long long)(D + 1) * 4ull);
+  return (partials + 255) / 256 * 256 + pkv::verify_partition_extra_bytes(B, T, Hq, D);
 }
 
 size_t pkv_prefill_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int block_size, int max_blocks,
@@ -210,10 +212,13 @@ pkv_status paged_kv_gather(const void* k_pool, const void* v_pool, const int32_t
                   "paged_kv_gather launch");
 }
 
-pkv_status paged_attention_decode(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
-                                  const int32_t* context_lens, void* out, float* lse_out, int B, int T, int Hq, int Hkv,
-                                  int D, int block_size, int max_blocks, int N_blocks, float scale, int partition_size,
-                                  void* workspace, size_t workspace_bytes, pkv_dtype dtype, void* stream) {
+}  // extern "C"
+
+// The decode entry point's body.
+static pkv_status decode_impl(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                              const int32_t* context_lens, void* out, float* lse_out, int B, int T, int Hq, int Hkv,
+                              int D, int block_size, int max_blocks, int N_blocks, float scale, int partition_size,
+                              void* workspace, size_t workspace_bytes, pkv_dtype dtype, void* stream) {
   pkv_status st = check_dtype(dtype);
   if (st != PKV_OK) return st;
   if (B < 0 || T < 1 || Hq < 1) return fail(PKV_EINVAL, "B must be >= 0, T and Hq >= 1");
@@ -248,6 +253,11 @@ pkv_status paged_attention_decode(const void* q, const void* k_pool, const void*
   const bool fixed_split = partition_size > 0 && partition_size < max_blocks * block_size;
   if (partition_size == 0 && pkv::verify_tile_for(a))
     return from_hip(pkv::launch_verify_mfma(a, workspace, s), "paged_attention_decode verify launch");
+  if (partition_size > 0 && pkv::verify_tile_for(a)) {   // split-KV partitions on the MFMA tile
+    a.part_tokens = partition_size;
+    a.P_max = partitions_max(max_blocks, block_size, partition_size);
+    return from_hip(pkv::launch_verify_mfma(a, workspace, s), "paged_attention_decode partition launch");
+  }
   if (partition_size == 0 && pkv::stream_supported(a))
     return from_hip(pkv::launch_decode_stream(a, workspace, s), "paged_attention_decode launch");
   if (fixed_split) {
@@ -266,6 +276,17 @@ pkv_status paged_attention_decode(const void* q, const void* k_pool, const void*
   return from_hip(pkv::launch_lse_reduce(a.part_out, a.part_lse, out, lse_out, B, T, Hq, D, a.P_max, a.bf16,
                                          context_lens, partition_size, s),
                   "lse_reduce launch");
+}
+
+
+extern "C" {
+
+pkv_status paged_attention_decode(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                                  const int32_t* context_lens, void* out, float* lse_out, int B, int T, int Hq, int Hkv,
+                                  int D, int block_size, int max_blocks, int N_blocks, float scale, int partition_size,
+                                  void* workspace, size_t workspace_bytes, pkv_dtype dtype, void* stream) {
+  return decode_impl(q, k_pool, v_pool, block_tables, context_lens, out, lse_out, B, T, Hq, Hkv, D, block_size,
+                     max_blocks, N_blocks, scale, partition_size, workspace, workspace_bytes, dtype, stream);
 }
 
 pkv_status paged_attention_prefill(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,

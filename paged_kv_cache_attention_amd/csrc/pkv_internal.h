@@ -83,6 +83,12 @@ bool verify_mfma_supported(const DecodeArgs& a);
 // Whether paged_attention_decode (single pass) runs the MFMA tile for a.
 bool verify_tile_for(const DecodeArgs& a);
 size_t verify_workspace_bytes(int B, int T, int Hq, int D);
+// Split-KV partitions on the tile (a.part_tokens > 0): bytes the workspace
+// needs beyond the documented partials (plan and piece slots).
+size_t verify_partition_extra_bytes(int B, int T, int Hq, int D);
+// Single pass (a.part_tokens == 0) or split-KV partitions of a.part_tokens
+// tokens (a.P_max per sequence): the workspace then starts with the partials
+// [B, T, Hq, P_max, D] and [B, T, Hq, P_max].
 hipError_t launch_verify_mfma(const DecodeArgs& a, void* workspace, hipStream_t stream);
 
 // Log-sum-exp merge of split partials.  When `lens` is given, rows whose

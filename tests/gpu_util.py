@@ -67,7 +67,7 @@ def max_abs_finite(w, arr):
     if w.dtype == "bf16":   # on the bit patterns: |x| orders like its low 15 bits
         mag = np.asarray(arr, dtype=np.uint16).ravel() & np.uint16(0x7FFF)
         mag = mag[mag < 0x7F80]
-        return float(w.values(mag.max(initial=0).astype(np.uint16)))
+        return float(w.values(np.array([mag.max(initial=0)], dtype=np.uint16))[0])
     return float(np.nanmax(np.abs(np.asarray(arr, dtype=np.float32))))
 
 
@@ -102,13 +102,13 @@ def check_attention(got, ref, dtype, where="", floor=ULP_FLOOR):
     return float(err.max()), float(rel)
 
 
-def assert_within_bf16_ulp(got, base, where=""):
-    """Two bf16 results agree to one ulp (or ULP_FLOOR for near-zero values)."""
+def assert_within_bf16_ulp(got, base, where="", floor=ULP_FLOOR):
+    """Two bf16 results agree to one ulp (or `floor` for near-zero values)."""
     got = np.asarray(got, dtype=np.float64)
     base = np.asarray(base, dtype=np.float64)
     assert np.isfinite(got).all() and np.isfinite(base).all(), where
     d = np.abs(got - base)
-    bad = (d > oracle.bf16_ulp(base)) & (d > ULP_FLOOR)
+    bad = (d > oracle.bf16_ulp(base)) & (d > floor)
     assert not bad.any(), f"{where}: {int(bad.sum())} elements differ by more than 1 ulp; max diff {d.max():.3e}"
 
 

@@ -33,10 +33,22 @@ def test_library_exports_every_declared_symbol():
 def test_workspace_sizing():
     f = pkv.pkv_decode_workspace_bytes
     assert f(4, 1, 32, 128, 64, 16, 0) > 0          # balanced split needs its own workspace
+
+    def partitioned(B, T, Hq, D, P):
+        """The documented partials (offset 0), rounded up to 256 bytes, then
+        the tile's plan (a header, 2 B + 18 unit prefix sums, B + 1 window
+        shares, 2048 range starts, B + 1 descriptors, each area rounded to 256
+        bytes) and two piece slots of min(16, T * Hq) rows per range for the
+        2048 ranges of Hkv = 1."""
+        r = lambda n: -(-n // 256) * 256
+        partials = r(B * T * Hq * P * (D + 1) * 4)
+        plan = 256 + r((2 * B + 18) * 4) + r((B + 1) * 4) + r(2048 * 4) + r((B + 1) * 16)
+        return partials + plan + 2 * 2048 * min(16, T * Hq) * (D + 1) * 4
     # P_max = ceil(64*16/256) = 4 partitions
-    assert f(4, 1, 32, 128, 64, 16, 256) == 4 * 1 * 32 * 4 * 129 * 4
-    assert f(16, 4, 32, 128, 4096, 16, 512) == 16 * 4 * 32 * 128 * 129 * 4
-    assert f(1, 1, 1, 64, 3, 16, 32) == 1 * 2 * 65 * 4
+    assert f(4, 1, 32, 128, 64, 16, 256) == partitioned(4, 1, 32, 128, 4)
+    assert f(16, 4, 32, 128, 4096, 16, 512) == partitioned(16, 4, 32, 128, 128)
+    assert f(1, 1, 1, 64, 3, 16, 32) == partitioned(1, 1, 1, 64, 2)
+    assert f(16, 4, 32, 128, 4096, 16, 512) >= 16 * 4 * 32 * 128 * 129 * 4
 
 
 def _decode(**kw):
@@ -228,3 +240,4 @@ def test_binding_checks_attention_arguments():
     for change, exc in bad:
         with pytest.raises(exc):
             pkv.check_attention_args(**dict(ok, **change))
+

@@ -8,8 +8,8 @@ import torch
 import oracle
 import workload
 import paged_kv_cache_attention_amd as pkv
-from gpu_util import (assert_within_bf16_ulp, check_attention, check_lse, dev, host, mfma_floor, oracle_inputs,
-                      upload)
+from gpu_util import (assert_within_bf16_ulp, check_attention, check_lse, check_partials, dev, host, max_abs_finite,
+                      mfma_floor, oracle_inputs, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -102,7 +102,7 @@ def test_split_sizes_agree_and_runs_are_deterministic():
         outs[part] = (host(o1), host(l1))
     base_o, base_l = outs[0]
     for part, (o, l) in outs.items():
-        assert_within_bf16_ulp(o, base_o, f"part={part} vs unsplit")
+        assert_within_bf16_ulp(o, base_o, f"part={part} vs unsplit", floor=2 * mfma_floor(w))
         np.testing.assert_allclose(l, base_l, rtol=0, atol=1e-4)
 
 
@@ -132,7 +132,8 @@ def test_verify_rows_equal_decode_chain():
             o1 = pkv.paged_attention_decode(qt, d["k"], d["v"], d["tables"], lens_t, lse_out=lse1,
                                             scale=float(w.scale), partition_size=part)
             torch.cuda.synchronize()
-            assert_within_bf16_ulp(host(o1)[:, 0], host(o4)[:, t], f"verify row {t} vs decode")
+            assert_within_bf16_ulp(host(o1)[:, 0], host(o4)[:, t], f"verify row {t} vs decode",
+                                   floor=2 * mfma_floor(w))
             np.testing.assert_allclose(host(lse1)[:, 0], host(l4)[:, t], rtol=0, atol=1e-4)
         oracle_check(w, o4, l4, f"verify part={part}")
 
@@ -171,12 +172,46 @@ def test_fully_masked_partition_rows():
     pl = ws[rows * P_max * w.D * 4: rows * P_max * (w.D + 1) * 4].view(torch.float32).view(w.B, T, w.Hq, P_max)
     ref_o, ref_l = oracle.partition_attention(*oracle_inputs(w), w.scale, w.block_size, part, num_parts=P_max)
     got_o, got_l = host(po), host(pl)
+    vmax = max_abs_finite(w, w.v_pool)
     for b, L in enumerate(lens):
         Pb = math.ceil(L / part)
-        for p in range(Pb):
-            check_lse(got_l[b, :, :, p], ref_l[b, :, :, p], f"partial lse b={b} p={p}")
-            np.testing.assert_allclose(got_o[b, :, :, p], ref_o[b, :, :, p], rtol=0, atol=2e-6)
+        check_partials(got_o[b, :, :, :Pb], got_l[b, :, :, :Pb], ref_o[b, :, :, :Pb], ref_l[b, :, :, :Pb], vmax,
+                       f"partials b={b}")
     assert np.isneginf(got_l[0, 0, :, 1]).all() and not got_o[0, 0, :, 1].any()
+
+
+@pytest.mark.parametrize("T,Hq,Hkv,D,part", [(1, 32, 8, 128, 512), (4, 32, 8, 128, 512), (2, 16, 4, 64, 1024),
+                                             (1, 8, 8, 64, 256)])
+def test_tile_partitions_span_several_ranges(T, Hq, Hkv, D, part):
+    """A batch small enough that the balanced ranges (16 blocks at least) are
+    shorter than a partition, so most partitions are cut by one or more range
+    boundaries and rebuilt from pieces by the merge.  Output, lse and every
+    partition's partial against the oracle."""
+    lens = [max(T, L) for L in (1500, 2049, 700, 3333, 15, 512 + 2, 4096)]
+    w = workload.uniform_batch("span", seed=60 + T, B=len(lens), T=T, Hq=Hq, Hkv=Hkv, D=D, dtype="bf16", lens=lens)
+    say("tile partitions across ranges", T, Hq, Hkv, D, part)
+    d = upload(w)
+    ws = torch.empty(pkv.pkv_decode_workspace_bytes(w.B, T, Hq, D, w.max_blocks, 16, part), dtype=torch.uint8,
+                     device="cuda")
+    lse = torch.full((w.B, T, Hq), float("nan"), device="cuda")
+    out = pkv.paged_attention_decode(d["q"], d["k"], d["v"], d["tables"], d["lens"], lse_out=lse,
+                                     scale=float(w.scale), partition_size=part, workspace=ws)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.paged_attention(*oracle_inputs(w), w.scale, w.block_size)
+    check_attention(host(out), ref, "bf16", f"span T={T} part={part}", floor=mfma_floor(w))
+    check_lse(host(lse), ref_lse, f"span T={T} part={part}")
+    P_max = math.ceil(w.max_blocks * 16 / part)
+    rows = w.B * T * Hq
+    po = ws[: rows * P_max * D * 4].view(torch.float32).view(w.B, T, Hq, P_max, D)
+    pl = ws[rows * P_max * D * 4: rows * P_max * (D + 1) * 4].view(torch.float32).view(w.B, T, Hq, P_max)
+    ref_o, ref_l = oracle.partition_attention(*oracle_inputs(w), w.scale, w.block_size, part, num_parts=P_max)
+    got_o, got_l = host(po), host(pl)
+    vmax = max_abs_finite(w, w.v_pool)
+    for b, L in enumerate(lens):
+        Pb = math.ceil(L / part)
+        if Pb > 1:   # single-partition sequences go straight to out
+            check_partials(got_o[b, :, :, :Pb], got_l[b, :, :, :Pb], ref_o[b, :, :, :Pb], ref_l[b, :, :, :Pb],
+                           vmax, f"span partials b={b}")
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])

@@ -12,8 +12,8 @@ import torch
 import oracle
 import workload
 import paged_kv_cache_attention_amd as pkv
-from gpu_util import (appended_oracle_pools, check_attention, check_lse, check_partials, dev, host, mfma_floor,
-                      oracle_by_sequence, oracle_inputs, upload)
+from gpu_util import (appended_oracle_pools, check_attention, check_lse, check_partials, dev, host, max_abs_finite,
+                      mfma_floor, oracle_by_sequence, oracle_inputs, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -131,17 +131,24 @@ def test_llama1b_append_then_decode(c3, part):
     check_lse(host(lse), ref_lse, f"llama1b part={part}")
 
 
-def test_llama8b_prefix_share_full():
-    """The 8B-shaped prefix-sharing batch at full size, in the launch
-    configuration the benchmark times: every one of the 256 sequences against
-    the oracle."""
+@pytest.fixture(scope="module")
+def c4():
+    """The 8B-shaped prefix-sharing batch (256 sequences), uploaded once, with
+    the oracle's result for every sequence."""
     w = workload.llama8b_prefix_share()
-    say("decode llama8b_prefix_share, all sequences")
-    d = upload(w)
-    out, lse = run_decode(w, d)
-    ref, ref_lse = oracle_by_sequence(w)
-    check_attention(host(out), ref, "bf16", "llama8b", floor=mfma_floor(w))
-    check_lse(host(lse), ref_lse, "llama8b")
+    return w, upload(w), oracle_by_sequence(w)
+
+
+@pytest.mark.parametrize("part", [0, 512])
+def test_llama8b_prefix_share_full(c4, part):
+    """The 8B-shaped prefix-sharing batch at full size, single pass (the
+    launch configuration the benchmark times) and split into 512-token
+    partitions: every one of the 256 sequences against the oracle."""
+    w, d, (ref, ref_lse) = c4
+    say("decode llama8b_prefix_share, all sequences, partition", part)
+    out, lse = run_decode(w, d, partition_size=part)
+    check_attention(host(out), ref, "bf16", f"llama8b part={part}", floor=mfma_floor(w))
+    check_lse(host(lse), ref_lse, f"llama8b part={part}")
 
 
 @pytest.fixture(scope="module")
@@ -189,7 +196,7 @@ def test_longctx_verify_512_token_partitions(c5):
     seqs = [int(b) for b in np.argsort(-Pb, kind="stable")[:2]]
     assert all(Pb[b] > 64 for b in seqs)
     ref_o, ref_l = oracle_by_sequence(w, seqs, partition_size=part)
-    vmax = float(np.abs(w.values(w.v_pool[w.block_tables[seqs].ravel()])).max())
+    vmax = max_abs_finite(w, w.v_pool)
     for i, b in enumerate(seqs):
         n = int(Pb[b])
         say("  partials of sequence", b, "P_b", n)
