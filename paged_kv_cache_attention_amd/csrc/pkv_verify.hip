@@ -50,35 +50,20 @@ constexpr int kTilePD = 1;
 constexpr int kInlinePerWave = 512;            // LDS prefix entries per wave
 constexpr int kInlinePT = kInlinePerWave / 64;  // sequences per thread
 constexpr int kMinBlocksPerRange = 16;
-
-// Shared prefixes (single pass, in-kernel plan): the sequences are taken in
-// windows of M = 16 / (T G) adjacent ones (M >= 2), as many as one tile has
-// rows for.  The leading blocks a window's sequences have in common (the same
-// physical ids as its longest member, up to kShareMaxBlocks) form the window's
-// prefix unit, attended once for all of them with every member's query rows in
-// the one tile; each sequence's own unit is the rest of its blocks.  The flat
-// block list is then, window by window: the prefix unit, then each member's
-// own unit, so unit u = w (M + 1) + k is window w's prefix unit for k = 0 and
-// the own unit of sequence w M + k - 1 otherwise.  Without sharing (M = 1
-// here) unit u is sequence u.
-constexpr int kShareMaxBlocks = 64;   // prefix blocks a window may share (1024 tokens)
-constexpr int kShareSeg = 16;         // table entries one thread compares
+// Partition staging area per wave: 16 rows of D + 4 floats.
+template <int D>
+constexpr int kStageFloats = 16 * (D + 4);
 
 struct VerifyArgs {
   DecodeArgs a;       // with partitions: a.part_out [B, T, Hq, P_max, D], a.part_lse [B, T, Hq, P_max]
   int* hdr;           // [total, per, tbtot]
-  int* prefix;        // [units + 1] blocks per unit, prefix sums
-  int* wshare;        // [windows] prefix blocks of each window (shared prefixes only)
+  int* prefix;        // [B + 1] blocks per sequence, prefix sums
   const int* first;   // [ranges] first non-empty sequence of each range (index into udesc)
   const int4* udesc;  // [B + 1] non-empty sequences, x = sequence
   float* part;        // single pass: [(ranges + B)][T][Hq][D + 1]; partitions: [2 * ranges][T][Hq][D + 1]
-  float* gpart;       // shared prefixes: [(ranges + windows)][M * T][Hq][D + 1]
   int ranges;
   int PB;             // blocks per partition (partitions only)
-  int M;              // sequences per window (1: no sharing)
 };
-
-__host__ __device__ inline int units_of(int B, int M) { return M > 1 ? (B + M - 1) / M * (M + 1) : B; }
 
 // Prefix sums over n counts (count(i) for i < n) into sp[0..n] by the whole
 // workgroup, kInlinePT consecutive entries per thread; returns the total.
@@ -118,115 +103,18 @@ __device__ __forceinline__ int inline_scan(int n, CountFn count, int* sp, int* w
   return total;
 }
 
-// Shared prefix blocks of every window into sS[w] (M >= 2).  snb[b] holds
-// each sequence's block count and sfirst[b] its first physical block.  A
-// window's lead is its longest member (the first of equals); member m agrees
-// with it up to d_m, the first block i < nb_m whose id differs (nb_m if none).
-// The window shares S = min(nb_lead, kShareMaxBlocks, min over members with
-// d_m < nb_m of d_m) blocks: every member that has block i < S holds the
-// lead's block there.  Windows whose members do not all start with the lead's
-// first block share nothing and load no table entries.  Threads take
-// (sequence, 16-entry segment) pairs and issue all their loads at once.
-__device__ __forceinline__ void detect_shared_prefixes(const DecodeArgs& a, int M, const int* snb, const int* sfirst,
-                                                       int* sd, int* sS) {
-  const int nwin = (a.B + M - 1) / M;
-  constexpr int NSEG = kShareMaxBlocks / kShareSeg;
-  const int pairs = a.B * NSEG;
-  auto lead_of = [&](int w) {
-    const int m0 = w * M, m1 = min(a.B, m0 + M);
-    int ld = m0;
-    for (int m = m0 + 1; m < m1; ++m)
-      if (snb[m] > snb[ld]) ld = m;
-    return ld;
-  };
-  for (int pr = threadIdx.x; pr < pairs; pr += blockDim.x) {
-    const int m = pr / NSEG, sg = pr - m * NSEG;
-    const int ld = lead_of(m / M);
-    const int lim = min(min(snb[m], snb[ld]), kShareMaxBlocks);
-    const int i0 = sg * kShareSeg;
-    int d = kShareSeg;   // first differing entry of this segment, kShareSeg if none
-    if (m != ld && sfirst[m] == sfirst[ld] && i0 < lim) {
-      const int32_t* tm = a.block_tables + (size_t)m * a.max_blocks + i0;
-      const int32_t* tl = a.block_tables + (size_t)ld * a.max_blocks + i0;
-      int xm[kShareSeg], xl[kShareSeg];
-#pragma unroll
-      for (int k = 0; k < kShareSeg; ++k) {
-        const bool ok = i0 + k < lim;
-        xm[k] = ok ? tm[k] : 0;
-        xl[k] = ok ? tl[k] : 0;
-      }
-#pragma unroll
-      for (int k = kShareSeg - 1; k >= 0; --k)
-        if (i0 + k < lim && xm[k] != xl[k]) d = k;
-    }
-    // a segment at or past lim holds no comparison; the lead agrees with itself
-    sd[pr] = (m == ld || i0 >= lim) ? kShareSeg : (sfirst[m] == sfirst[ld] ? d : 0);
-  }
-  __syncthreads();
-  for (int w = threadIdx.x; w < nwin; w += blockDim.x) {
-    const int m0 = w * M, m1 = min(a.B, m0 + M);
-    const int ld = lead_of(w);
-    int S = min(snb[ld], kShareMaxBlocks);
-    int members = 0;
-    for (int m = m0; m < m1; ++m) {
-      if (snb[m] == 0) continue;
-      ++members;
-      if (m == ld) continue;
-      int dm = min(snb[m], kShareMaxBlocks);   // agreement over every block of m compared
-      for (int sg = 0; sg < NSEG; ++sg) {
-        const int v = sd[m * NSEG + sg];
-        if (v < kShareSeg) {
-          dm = min(dm, sg * kShareSeg + v);
-          break;
-        }
-      }
-      if (dm < min(snb[m], kShareMaxBlocks)) S = min(S, dm);   // m diverges inside its own blocks
-    }
-    sS[w] = members >= 2 ? S : 0;
-  }
-  __syncthreads();
-}
-
-// The plan inside the kernel, by the whole workgroup: unit block counts and
-// their prefix sums into sp[0 .. units] (LDS), and with shared prefixes
-// (va.M >= 2) each window's prefix blocks into sS (LDS; snb, sfirst and sd are
-// LDS scratch of B, B and 4 B entries).  Workgroup g publishes entries
-// g * threads + tid (+ multiples of all threads) of the prefix sums and the
-// windows' prefix blocks, and workgroup 0 the header, for the merge kernel.
-// Returns the total.
-__device__ __forceinline__ int verify_inline_plan(const VerifyArgs& va, int* sp, int* wsc, int* snb, int* sfirst,
-                                                  int* sd, int* sS) {
+// The plan inside the kernel, by the whole workgroup: each sequence's block
+// count (ceil(L / 16)) and their prefix sums into sp[0 .. B] (LDS).
+// Workgroup g publishes entries g * threads + tid (+ multiples of all
+// threads) and workgroup 0 the header, for the merge kernel.  Returns the
+// total.
+__device__ __forceinline__ int verify_inline_plan(const VerifyArgs& va, int* sp, int* wsc) {
   const DecodeArgs& a = va.a;
   const int tid = threadIdx.x;
   const int max_tokens = a.max_blocks * kBS;
-  const int M = va.M;
-  auto nb_of = [&](int b) { return (clampi(a.context_lens[b], 0, max_tokens) + kBS - 1) / kBS; };
-  int total;
-  if (M > 1) {
-    for (int b = tid; b < a.B; b += blockDim.x) {
-      // both loads issued together (entry 0 of a row exists whatever the length)
-      const int L = a.context_lens[b];
-      const int f = a.block_tables[(size_t)b * a.max_blocks];
-      const int n = (clampi(L, 0, max_tokens) + kBS - 1) / kBS;
-      snb[b] = n;
-      sfirst[b] = n > 0 ? f : -1 - b;
-    }
-    __syncthreads();
-    detect_shared_prefixes(a, M, snb, sfirst, sd, sS);
-    const int US = M + 1;
-    total = inline_scan(units_of(a.B, M), [&](int u) {
-      const int w = u / US, k = u - w * US;
-      if (k == 0) return sS[w];
-      const int b = w * M + k - 1;
-      return b < a.B ? snb[b] - min(sS[w], snb[b]) : 0;
-    }, sp, wsc);
-    const int nwin = (a.B + M - 1) / M;
-    for (int w = blockIdx.x * blockDim.x + tid; w < nwin; w += gridDim.x * blockDim.x) va.wshare[w] = sS[w];
-  } else {
-    total = inline_scan(a.B, nb_of, sp, wsc);
-  }
-  const int nu = units_of(a.B, M);
-  for (int k = blockIdx.x * blockDim.x + tid; k <= nu; k += gridDim.x * blockDim.x) va.prefix[k] = sp[k];
+  const int total = inline_scan(a.B, [&](int b) { return (clampi(a.context_lens[b], 0, max_tokens) + kBS - 1) / kBS; },
+                                sp, wsc);
+  for (int k = blockIdx.x * blockDim.x + tid; k <= a.B; k += gridDim.x * blockDim.x) va.prefix[k] = sp[k];
   if (blockIdx.x == 0 && tid == 0) {
     va.hdr[0] = total;
     va.hdr[1] = max(kMinBlocksPerRange, (total + va.ranges - 1) / va.ranges);
@@ -269,11 +157,44 @@ __device__ __forceinline__ void emit_rows(const tile::State<D>& st, const Decode
   }
 }
 
+// A partition's normalised rows, staged through the wave's LDS area so that
+// they leave as whole rows of 16-byte stores (each row D contiguous floats
+// of part_out) instead of 4-byte stores scattered over the rows: rows r < R
+// of the tile, row r being query token t = r / G, head kv G + r % G; lse to
+// part_lse.  The area holds 16 rows of D + 4 floats (the padding puts the 4
+// rows a store instruction writes on distinct banks).
+template <int D>
+__device__ __forceinline__ void emit_partition_staged(const tile::State<D>& st, const DecodeArgs& a, size_t prow,
+                                                      int p, int kv, int G, int R, float* stage, int lane) {
+  constexpr int DT = D / 16, STR = D + 4, C4 = D / 4;   // 16-byte chunks per row
+  const int row = lane & 15, quad = lane >> 4;
+  const float l_row = tile::row_sum(st);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = 4 * quad + k;
+    const float lr = __shfl(l_row, r);
+    const float inv = lr != 0.f ? 1.f / lr : 0.f;
+#pragma unroll
+    for (int d = 0; d < DT; ++d) stage[r * STR + 16 * d + row] = st.acc[d][k] * inv;
+  }
+  if (quad == 0 && row < R) {   // row lane r holds its own max and sum
+    const float lr = l_row;
+    const int t = row / G, h = kv * G + (row - t * G);
+    a.part_lse[(prow + (size_t)t * a.Hq + h) * a.P_max + p] = lr != 0.f ? (st.m_row + log2f(lr)) * kLn2 : kNegInf;
+  }
+  // (LDS operations of one wave complete in order: the reads see the writes)
+  for (int c = lane; c < R * C4; c += 64) {
+    const int r = c / C4, c4 = c - r * C4;
+    const int t = r / G, h = kv * G + (r - t * G);
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + r * STR + 4 * c4);
+    store16(a.part_out + ((prow + (size_t)t * a.Hq + h) * a.P_max + p) * D + 4 * c4, v);
+  }
+}
+
 // INL: the plan is computed in the kernel (LDS); otherwise read from the
 // workspace written by the planning kernel.  LDS (dynamic): one V tile per
-// wave, then with INL the unit prefix list (kInlinePerWave entries per wave)
-// and, with shared prefixes, the detection scratch.  PART: split-KV partitions
-// of va.PB blocks (no shared prefixes).
+// wave, then with INL the prefix list; with PART a staging area of 16 rows
+// per wave.  PART: split-KV partitions of va.PB blocks.
 template <int D, int PD, bool INL, bool PART>
 __global__ __launch_bounds__(64 * kMaxWpg) void verify_mfma_kernel(VerifyArgs va, float scale_log2e) {
   const DecodeArgs& a = va.a;
@@ -284,17 +205,12 @@ __global__ __launch_bounds__(64 * kMaxWpg) void verify_mfma_kernel(VerifyArgs va
   constexpr int kTileBytes = tile::run_tile_bytes<D, PD>();
   unsigned char* vtiles = vlds + wave * kTileBytes;
   int* sprefix = reinterpret_cast<int*>(vlds + wpg * kTileBytes);
-  int* snb = sprefix + kInlinePerWave * wpg;   // shared prefixes: [B] blocks per sequence
-  int* sfirst = snb + a.B;                      // [B] first physical block
-  int* sd = sfirst + a.B;                       // [B * 4] detection scratch
-  int* sS = sd + a.B * (kShareMaxBlocks / kShareSeg);   // [windows] prefix blocks per window
+  float* stage = reinterpret_cast<float*>(vlds + wpg * kTileBytes + (INL ? kInlinePerWave * wpg * 4 : 0)) +
+                 wave * kStageFloats<D>;
   __shared__ int wsc[16];
-  const int M = PART ? 1 : va.M;
-  const int US = M > 1 ? M + 1 : 1;
-  const int NU = units_of(a.B, M);
   int total, per;
   if constexpr (INL) {
-    total = __builtin_amdgcn_readfirstlane(verify_inline_plan(va, sprefix, wsc, snb, sfirst, sd, sS));
+    total = __builtin_amdgcn_readfirstlane(verify_inline_plan(va, sprefix, wsc));
     per = max(kMinBlocksPerRange, (total + va.ranges - 1) / va.ranges);
   } else {
     total = va.hdr[0];
@@ -315,23 +231,26 @@ __global__ __launch_bounds__(64 * kMaxWpg) void verify_mfma_kernel(VerifyArgs va
   const int F0 = rng * per;
   if (F0 >= total) return;
   const int F1 = min(total, F0 + per);
-  int u;   // the unit holding block F0
+  int b;
   if constexpr (INL) {
-    // largest u < NU with prefix[u] <= F0 (a non-empty unit: F0 < total)
-    int lo = 0, hi = NU;
+    // the sequence holding block F0: largest b < B with prefix[b] <= F0
+    int lo = 0, hi = a.B;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (sprefix[mid] <= F0) lo = mid; else hi = mid;
     }
-    u = __builtin_amdgcn_readfirstlane(lo);
+    b = __builtin_amdgcn_readfirstlane(lo);
   } else {
-    u = va.udesc[va.first[rng]].x;
+    b = va.udesc[va.first[rng]].x;
   }
 
   const int G = a.Hq / a.Hkv;
-  const int R = a.T * G;                 // query rows of one sequence for this KV head (<= 16)
+  const int R = a.T * G;                 // query rows of this KV head (<= 16)
   const int row = lane & 15;             // this lane's row in S^T / P
   const int quad = lane >> 4;            // row quad in O
+  const bool row_ok = row < R;
+  const int rq = row_ok ? row : 0;
+  const int t_row = rq / G;
   const size_t kv_row_bytes = (size_t)a.Hkv * D * 2;
   const size_t block_bytes = (size_t)kBS * kv_row_bytes;
   const uint32_t lane_off = (uint32_t)((size_t)row * kv_row_bytes + (size_t)kv * D * 2 + quad * 16);
@@ -339,63 +258,25 @@ __global__ __launch_bounds__(64 * kMaxWpg) void verify_mfma_kernel(VerifyArgs va
   const unsigned char* vhead = static_cast<const unsigned char*>(a.v_pool) + (size_t)kv * D * 2;
   const int nmax = a.N_blocks - 1;
   const int max_tokens = a.max_blocks * kBS;
-  const uint16_t* qbase = static_cast<const uint16_t*>(a.q);
 
   const size_t slot_floats = (size_t)a.T * a.Hq * (D + 1);
   while (true) {
-    const int ustart = prefix_of(u), ulen = prefix_of(u + 1) - ustart;
-    const int js = max(F0, ustart) - ustart;
-    const int je = min(F1, ustart + ulen) - ustart;
-    const int w = u / US, k = u - w * US;
-    if (je > js && M > 1 && k == 0) {
-      // ---- prefix unit of window w: its blocks [0, S) for every member ----
-      const int m0 = w * M, mc = min(M, a.B - m0);
-      const int S = sS[w];
-      int ld = m0;   // the longest member: the window's blocks are its table entries
-      for (int m = m0 + 1; m < m0 + mc; ++m)
-        if (snb[m] > snb[ld]) ld = m;
-      ld = __builtin_amdgcn_readfirstlane(ld);
-      // row r of the tile: member r / R, its query token and head
-      const int jm = row / R;
-      const bool rok = jm < mc;
-      const int rr = rok ? row - jm * R : 0;
-      const int tm = rr / G;
-      const int bm = m0 + (rok ? jm : 0);
-      const int Lm = clampi(a.context_lens[bm], 0, max_tokens);
-      const int sm = min(S, (Lm + kBS - 1) / kBS);   // blocks of the prefix this member has
-      const int hi = rok ? min(Lm - a.T + tm + 1, sm * kBS) : 0;
-      // V rows at or past every member's shared length are zeroed
-      int vl = rok ? min(Lm, sm * kBS) : 0;
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) vl = max(vl, __shfl_xor(vl, off));
-      u32x4_t qreg[D / 32];
-      tile::load_q<D>(qreg, qbase + ((size_t)(bm * a.T + tm) * a.Hq + kv * G + (rr - tm * G)) * D, rok, lane);
-      tile::State<D> st;
-      tile::init(st);
-      tile::run<D, PD>(st, qreg, hi, vl, a.block_tables + (size_t)ld * a.max_blocks + js, js, je - js, nmax, kpool,
-                       vhead, kv_row_bytes, block_bytes, vtiles, scale_log2e, lane);
-      // rows (member j, token t) as (j T + t) of the window's slot
-      float* slot = va.gpart + (size_t)(rng + w) * M * slot_floats;
-      emit_rows<D>(st, a, m0, kv, G, mc * R, false,
-                   [&](int t, int h) { return slot + ((size_t)t * a.Hq + h) * (D + 1); },
-                   [&](int t, int h) { return slot + ((size_t)t * a.Hq + h) * (D + 1) + D; }, lane);
-    } else if (je > js) {
-      // ---- own unit of sequence b: its blocks [sb, nb) ----
-      const int b = M > 1 ? w * M + k - 1 : u;
+    const int pstart = prefix_of(b), plen = prefix_of(b + 1) - pstart;
+    const int js = max(F0, pstart) - pstart;
+    const int je = min(F1, pstart + plen) - pstart;
+    const bool direct = pstart >= F0 && pstart + plen <= F1;
+    if (je > js) {
       const int L = clampi(a.context_lens[b], 0, max_tokens);
-      const int sb = M > 1 ? min(sS[w], (L + kBS - 1) / kBS) : 0;   // blocks its window's prefix unit took
-      const bool row_ok = row < R;
-      const int rq = row_ok ? row : 0;
-      const int t_row = rq / G;
       const int hi_row = row_ok ? L - a.T + t_row + 1 : 0;   // causal limit of this row's query token
       u32x4_t qreg[D / 32];
-      tile::load_q<D>(qreg, qbase + ((size_t)(b * a.T + t_row) * a.Hq + kv * G + (rq - t_row * G)) * D, row_ok,
-                      lane);
+      tile::load_q<D>(qreg, static_cast<const uint16_t*>(a.q) +
+                                ((size_t)(b * a.T + t_row) * a.Hq + kv * G + (rq - t_row * G)) * D,
+                      row_ok, lane);
       const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks;
       if constexpr (PART) {
         // the partitions this range holds of sequence b, one at a time
         const int PB = va.PB;
-        const int Pb = (ulen + PB - 1) / PB;
+        const int Pb = (plen + PB - 1) / PB;
         for (int p0 = js; p0 < je;) {
           const int p = p0 / PB;
           const int pe = min(je, (p + 1) * PB);
@@ -403,12 +284,12 @@ __global__ __launch_bounds__(64 * kMaxWpg) void verify_mfma_kernel(VerifyArgs va
           tile::init(st);
           tile::run<D, PD>(st, qreg, hi_row, L, trow + p0, p0, pe - p0, nmax, kpool, vhead, kv_row_bytes,
                            block_bytes, vtiles, scale_log2e, lane);
-          const bool whole = p0 == p * PB && pe == min(ulen, (p + 1) * PB);
-          if (whole) {
-            const size_t prow = (size_t)b * a.T * a.Hq;   // (+ t * Hq + h) * P_max + p
-            emit_rows<D>(st, a, b, kv, G, R, Pb == 1,
-                         [&](int t, int h) { return a.part_out + ((prow + t * a.Hq + h) * a.P_max + p) * D; },
-                         [&](int t, int h) { return a.part_lse + (prow + t * a.Hq + h) * a.P_max + p; }, lane);
+          const bool whole = p0 == p * PB && pe == min(plen, (p + 1) * PB);
+          if (whole && Pb > 1) {
+            emit_partition_staged<D>(st, a, (size_t)b * a.T * a.Hq, p, kv, G, R, stage, lane);
+          } else if (whole) {
+            emit_rows<D>(st, a, b, kv, G, R, true, [&](int, int) { return (float*)nullptr; },
+                         [&](int, int) { return (float*)nullptr; }, lane);
           } else {
             // a piece of a partition cut by this range's start (slot 0) or,
             // starting inside the range, by its end (slot 1)
@@ -422,26 +303,22 @@ __global__ __launch_bounds__(64 * kMaxWpg) void verify_mfma_kernel(VerifyArgs va
       } else {
         tile::State<D> st;
         tile::init(st);
-        tile::run<D, PD>(st, qreg, hi_row, L, trow + sb + js, sb + js, je - js, nmax, kpool, vhead, kv_row_bytes,
-                         block_bytes, vtiles, scale_log2e, lane);
-        // straight to out when the sequence shares nothing and this range holds all of it
-        const bool direct = sb == 0 && ustart >= F0 && ustart + ulen <= F1;
+        tile::run<D, PD>(st, qreg, hi_row, L, trow + js, js, je - js, nmax, kpool, vhead, kv_row_bytes, block_bytes,
+                         vtiles, scale_log2e, lane);
         float* slot = va.part + (size_t)(rng + b) * slot_floats;
         emit_rows<D>(st, a, b, kv, G, R, direct,
                      [&](int t, int h) { return slot + ((size_t)t * a.Hq + h) * (D + 1); },
                      [&](int t, int h) { return slot + ((size_t)t * a.Hq + h) * (D + 1) + D; }, lane);
       }
     }
-    if (ustart + ulen >= F1 || u + 1 >= NU) break;
-    ++u;
+    if (pstart + plen >= F1) break;
+    ++b;
   }
 }
 
-// Merge of the pieces of each sequence: one wave per (sequence, query token,
-// 4 heads); 16 lanes per head.  A sequence's pieces are those of its own unit
-// (one per range it spans) and, with a shared prefix, those of its window's
-// prefix unit.  A sequence that shares nothing and lies inside one range was
-// written directly.
+// Merge of the pieces of sequences cut by range boundaries: one wave per
+// (sequence, query token, 4 heads); 16 lanes per head.  A sequence inside one
+// range was written directly.
 template <int D>
 __global__ __launch_bounds__(256) void verify_merge_kernel(VerifyArgs va) {
   constexpr int EPL = D / 16;
@@ -454,66 +331,44 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(VerifyArgs va) {
   const int per = va.hdr[1];
   const int hq = gidx % HG, bt = gidx / HG;
   const int b = bt / a.T, t = bt - b * a.T;
-  const int M = va.M, US = M > 1 ? M + 1 : 1;
-  const int w = M > 1 ? b / M : 0, j = M > 1 ? b - w * M : 0;
-  const int uo = M > 1 ? w * US + 1 + j : b;
-  const int ostart = va.prefix[uo], olen = va.prefix[uo + 1] - ostart;
-  const int L = clampi(a.context_lens[b], 0, a.max_blocks * kBS);
-  const int sb = M > 1 ? min(va.wshare[w], (L + kBS - 1) / kBS) : 0;
+  const int pstart = va.prefix[b], plen = va.prefix[b + 1] - pstart;
   const int h = hq * 4 + (lane >> 4), d0 = (lane & 15) * EPL;
   uint16_t* out = static_cast<uint16_t*>(a.out) + (((size_t)b * a.T + t) * a.Hq + h) * D + d0;
   float* lse_out = a.lse_out ? a.lse_out + ((size_t)b * a.T + t) * a.Hq + h : nullptr;
-  if (sb == 0) {
-    if (olen == 0) {
+  if (plen == 0) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) out[e] = 0;
-      if (lse_out && (lane & 15) == 0) *lse_out = kNegInf;
-      return;
-    }
-    if (ostart / per == (ostart + olen - 1) / per) return;
+    for (int e = 0; e < EPL; ++e) out[e] = 0;
+    if (lse_out && (lane & 15) == 0) *lse_out = kNegInf;
+    return;
   }
+  const int w0 = pstart / per, w1 = (pstart + plen - 1) / per;
+  if (w0 == w1) return;
   float m = kNegInf, ssum = 0.f, acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  // the pieces of one unit over ranges w0 .. w1, slot(r) its piece in range r
-  auto absorb_unit = [&](int w0, int w1, auto slot) {
-    for (int r = w0; r <= w1; r += BATCH) {
-      float lv[BATCH], ov[BATCH][EPL];
+  for (int w = w0; w <= w1; w += BATCH) {
+    float lv[BATCH], ov[BATCH][EPL];
 #pragma unroll
-      for (int k = 0; k < BATCH; ++k) {
-        lv[k] = kNegInf;
-        if (r + k <= w1) {
-          const float* sl = slot(r + k);
-          lv[k] = sl[D];
+    for (int k = 0; k < BATCH; ++k) {
+      lv[k] = kNegInf;
+      if (w + k <= w1) {
+        const float* slot = va.part + (((size_t)(w + k + b) * a.T + t) * a.Hq + h) * (D + 1);
+        lv[k] = slot[D];
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) ov[k][e] = sl[d0 + e];
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < BATCH; ++k) {
-        if (lv[k] == kNegInf) continue;
-        const float nm = fmaxf(m, lv[k]);
-        const float sa = __builtin_amdgcn_exp2f((m - nm) * kLog2e);
-        const float sbw = __builtin_amdgcn_exp2f((lv[k] - nm) * kLog2e);
-        ssum = ssum * sa + sbw;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] = acc[e] * sa + sbw * ov[k][e];
-        m = nm;
+        for (int e = 0; e < EPL; ++e) ov[k][e] = slot[d0 + e];
       }
     }
-  };
-  const size_t slot_floats = (size_t)a.T * a.Hq * (D + 1);
-  if (sb > 0) {
-    const int up = w * US;
-    const int pstart = va.prefix[up], plen = va.prefix[up + 1] - pstart;
-    const size_t prow = (((size_t)j * a.T + t) * a.Hq + h) * (D + 1);   // member j, token t in the window slot
-    absorb_unit(pstart / per, (pstart + plen - 1) / per,
-                [&](int r) { return va.gpart + (size_t)(r + w) * M * slot_floats + prow; });
-  }
-  if (olen > 0) {
-    const size_t orow = ((size_t)t * a.Hq + h) * (D + 1);
-    absorb_unit(ostart / per, (ostart + olen - 1) / per,
-                [&](int r) { return va.part + (size_t)(r + b) * slot_floats + orow; });
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      if (lv[k] == kNegInf) continue;
+      const float nm = fmaxf(m, lv[k]);
+      const float sa = __builtin_amdgcn_exp2f((m - nm) * kLog2e);
+      const float sb = __builtin_amdgcn_exp2f((lv[k] - nm) * kLog2e);
+      ssum = ssum * sa + sb;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = acc[e] * sa + sb * ov[k][e];
+      m = nm;
+    }
   }
   const float inv = ssum != 0.f ? 1.f / ssum : 0.f;
 #pragma unroll
@@ -662,47 +517,32 @@ bool verify_mfma_supported(const DecodeArgs& a) {
 bool verify_tile_for(const DecodeArgs& a) { return verify_mfma_supported(a); }
 
 namespace {
-// The tile's plan area: header, unit block prefix sums (at most 2 B + 17
-// entries: with shared prefixes M >= 2 windows of M + 1 units), the windows'
-// shared prefix blocks, each range's first sequence and the sequence
-// descriptors (the last two written only by the planning kernel).
+// The tile's plan area: header, per-sequence block prefix sums, each range's
+// first sequence and the sequence descriptors (the last two written only by
+// the planning kernel).
 struct PlanLayout {
-  size_t prefix, wshare, first, udesc, end;
+  size_t prefix, first, udesc, end;
 };
 size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 PlanLayout plan_layout(int B) {
   PlanLayout l{};
   l.prefix = 256;
-  l.wshare = l.prefix + align256(((size_t)2 * B + 18) * 4);
-  l.first = l.wshare + align256(((size_t)B + 1) * 4);
+  l.first = l.prefix + align256(((size_t)B + 1) * 4);
   l.udesc = l.first + align256((size_t)kStreamWaves * 4);
   l.end = l.udesc + align256(((size_t)B + 1) * 16);
   return l;
 }
-
-// Members per shared-prefix window for a shape: one tile's rows, 16 / (T G).
-int window_members(int T, int G) { return 16 / (T * G); }
-
-// Shared-prefix detection runs inside every workgroup (one pass over the
-// windows' table entries): only for batches up to this size.
-constexpr int kShareMaxB = 1024;
 }  // namespace
 
-// Single pass.  Piece slots of sequences: (ranges + B) slots of T * Hq rows,
-// where ranges * T * Hq = kStreamWaves * T * G <= kStreamWaves * min(16,
-// T * Hq) for every shape the tile takes.  Piece slots of shared prefixes:
-// (ranges + windows) slots of M T Hq rows, with ranges M T Hq = kStreamWaves
-// M T G <= kStreamWaves * 16 and windows M T Hq <= (B + M) T Hq <= (B + 16)
-// T Hq.
+// Single pass.  Piece slots: (ranges + B) slots of T * Hq rows, where
+// ranges * T * Hq = kStreamWaves * T * G <= kStreamWaves * min(16, T * Hq)
+// for every shape the tile takes.
 size_t verify_workspace_bytes(int B, int T, int Hq, int D) {
-  const size_t own = (size_t)kStreamWaves * (T * Hq < 16 ? T * Hq : 16) + (size_t)B * T * Hq;
-  const size_t shared = (size_t)kStreamWaves * 16 + ((size_t)B + 16) * T * Hq;
-  return plan_layout(B).end + (own + shared) * (D + 1) * 4;
+  const size_t rows = (size_t)kStreamWaves * (T * Hq < 16 ? T * Hq : 16) + (size_t)B * T * Hq;
+  return plan_layout(B).end + rows * (D + 1) * 4;
 }
 
 // Beyond the documented partials: the plan and two piece slots per range.
-// ranges * T * Hq = kStreamWaves * T * G <= kStreamWaves * 16 for every shape
-// the tile takes.
 size_t verify_partition_extra_bytes(int B, int T, int Hq, int D) {
   const size_t rows = (size_t)kStreamWaves * (T * Hq < 16 ? T * Hq : 16);
   return plan_layout(B).end + 2 * rows * (D + 1) * 4;
@@ -725,12 +565,12 @@ hipError_t launch_verify_mfma(const DecodeArgs& a, void* workspace, hipStream_t 
   int* prefix = reinterpret_cast<int*>(ws + pl.prefix);
   int* first = reinterpret_cast<int*>(ws + pl.first);
   int4* udesc = reinterpret_cast<int4*>(ws + pl.udesc);
-  float* slots = reinterpret_cast<float*>(ws + pl.end);
-  va.hdr = hdr; va.prefix = prefix; va.wshare = reinterpret_cast<int*>(ws + pl.wshare); va.first = first;
-  va.udesc = udesc; va.part = slots;
+  va.hdr = hdr; va.prefix = prefix; va.first = first; va.udesc = udesc;
+  va.part = reinterpret_cast<float*>(ws + pl.end);
   // the V tiles of every wave of a workgroup share its LDS: fewer waves per
   // workgroup where they would not fit (the grid then has more workgroups)
   const size_t tile_bytes = a.D == 64 ? tile::run_tile_bytes<64, kTilePD>() : tile::run_tile_bytes<128, kTilePD>();
+  const size_t stage_bytes = part ? (a.D == 64 ? kStageFloats<64> : kStageFloats<128>) * 4 : 0;
   int wpg = a.Hkv < kMaxWpg ? a.Hkv : kMaxWpg;
   // At D = 64, workgroups of at most 4 waves (twice as many per CU, the same
   // waves per SIMD) measured faster: 1B decode batch 51.4 against 53.0 us.
@@ -738,27 +578,18 @@ hipError_t launch_verify_mfma(const DecodeArgs& a, void* workspace, hipStream_t 
   // verify 433.3 against 429.5).  Halving keeps Hkv a multiple of wpg.
   if (a.D == 64)
     while (wpg > 4 && wpg % 2 == 0) wpg /= 2;
-  while (wpg % 2 == 0 && (size_t)wpg * tile_bytes + 64 > (size_t)device_lds_per_block()) wpg /= 2;
-  const size_t tiles = (size_t)wpg * tile_bytes;
-  const size_t lds_list = tiles + (size_t)kInlinePerWave * wpg * 4;
   const size_t lds_cap = (size_t)device_lds_per_block() - 64;
-  const bool inl = a.B + 1 <= kInlinePerWave * wpg && lds_list <= lds_cap;
-  // shared prefixes: single pass, planned in the kernel, two or more
-  // sequences per tile, and room for the units and the detection scratch
-  int M = window_members(a.T, a.Hq / a.Hkv);
-  const size_t lds_share = lds_list + ((size_t)6 * a.B + a.B / 2 + 8) * 4;
-  if (part || !inl || M < 2 || a.B > kShareMaxB || units_of(a.B, M) + 1 > kInlinePerWave * wpg ||
-      lds_share > lds_cap)
-    M = 1;
-  va.M = M;
-  va.gpart = slots + ((size_t)va.ranges + a.B) * a.T * a.Hq * (a.D + 1);
+  while (wpg % 2 == 0 && (size_t)wpg * (tile_bytes + stage_bytes) > lds_cap) wpg /= 2;
+  const size_t tiles = (size_t)wpg * tile_bytes;
+  const size_t lds_inl = tiles + (size_t)kInlinePerWave * wpg * 4 + (size_t)wpg * stage_bytes;
+  const bool inl = a.B + 1 <= kInlinePerWave * wpg && lds_inl <= lds_cap;
   hipError_t e = hipSuccess;
   // one unit per sequence: blocks = ceil(L / 16)
   if (!inl) e = launch_plan(a.context_lens, a.B, 1, va.ranges, a.max_blocks, hdr, prefix, first, udesc, stream);
   if (e != hipSuccess) return e;
   const float sl2 = a.scale * kLog2e;
   const dim3 grid(va.ranges * (a.Hkv / wpg)), block(64 * wpg);
-  const size_t lds = !inl ? tiles : M > 1 ? lds_share : lds_list;
+  const size_t lds = inl ? lds_inl : tiles + (size_t)wpg * stage_bytes;
 #define PKV_VERIFY_LAUNCH(DD, INLV, PARTV) \
   hipLaunchKernelGGL((verify_mfma_kernel<DD, kTilePD, INLV, PARTV>), grid, block, lds, stream, va, sl2)
   if (a.D == 64) {

@@ -1,10 +1,13 @@
-"""Shared prefixes on the MFMA tile: adjacent sequences whose block tables
-start with the same physical blocks ("Inference From Scratch", What you will
-build and Chapters table, ch. 11: prefix caching reuses KV blocks across
-requests) have those blocks attended once per window of 16 / (T G)
-sequences, every member's query rows in one tile.  Each case is checked
-against the oracle, for determinism, and against the same logical data with
-every block copied to a private physical block (no sharing to find)."""
+"""Block tables that share physical blocks, as prefix caching leaves them
+("Inference From Scratch", What you will build and Chapters table, ch. 11:
+prefix caching reuses KV blocks across requests): groups of sequences whose
+tables start with the same physical blocks for different lengths, trees of
+shared prefixes, groups that straddle each other in the batch, members
+shorter than the shared prefix or ending inside a shared block, every query
+rows per KV head ratio.  Each case is checked against the oracle, for
+determinism, and against the same logical data with every block copied to a
+private physical block: the result may not depend on which blocks are
+shared."""
 import dataclasses
 
 import numpy as np
@@ -74,9 +77,9 @@ def check_case(w, where):
 
 
 def test_groups_with_short_and_ragged_members():
-    """Groups of 8 sequences (windows of 4) sharing 40 blocks: members shorter
-    than the prefix (1, 15, 200 tokens), members ending inside the last shared
-    block, one longer than the lead inside its last block."""
+    """Groups of 8 sequences sharing 40 blocks: members shorter than the
+    prefix (1, 15, 200 tokens), members ending inside the last shared block,
+    one longer than the longest other member inside its last block."""
     lens, share = [], []
     for g in range(3):
         for L in (1, 15, 200, 640, 641, 700, 3000, 40 * 16 - 3):
@@ -88,9 +91,7 @@ def test_groups_with_short_and_ragged_members():
 
 
 def test_windows_across_group_boundaries():
-    """Groups of 3, 5, 2 and 6 sequences: windows of 4 straddle groups, so
-    only the members agreeing with a window's longest member share, and a
-    window whose first blocks differ shares nothing."""
+    """Groups of 3, 5, 2 and 6 adjacent sequences sharing 20 blocks each."""
     sizes = [3, 5, 2, 6]
     rng = np.random.default_rng(71)
     lens, share = [], []
@@ -104,13 +105,10 @@ def test_windows_across_group_boundaries():
 
 
 def test_tree_of_prefixes_and_long_chain():
-    """Windows of 4 (G = 4, D = 64).  Window 0: members sharing 150, 90 and 150
-    blocks of one chain with the longest (188 blocks): beyond the 64-block
-    window limit, so 64 are shared and the rest read per member.  Window 1: a
-    tree (members sharing 10, 5, all 10 of theirs, and 10 of a member that
-    shares 90 with others): 5 blocks shared.  Window 2: two members of
-    another chain and one of a third, whose first blocks differ: nothing
-    shared."""
+    """G = 4, D = 64: members sharing 150, 90 and 150 blocks of one chain
+    whose longest member has 188; a tree of members sharing 10, 5 and 90
+    blocks of the same chain; two members of another chain and one of a
+    third."""
     lens = [2400, 3000, 2400, 2560, 2400, 1000, 160, 2400, 1600, 2000, 77]
     share = [(0, 150), (0, 150), (0, 90), (0, 150), (0, 10), (0, 5), (0, 10), (0, 90), (1, 64), (1, 64), (2, 5)]
     w = shared_batch("tree", 72, 1, 16, 4, 64, lens, share)
@@ -121,8 +119,8 @@ def test_tree_of_prefixes_and_long_chain():
 @pytest.mark.parametrize("T,Hq,Hkv,D", [(2, 32, 8, 128), (1, 8, 8, 64), (1, 64, 8, 128), (4, 8, 8, 128),
                                         (1, 16, 8, 64)])
 def test_window_sizes(T, Hq, Hkv, D):
-    """Windows of 16 / (T G) = 2, 16, 2, 4 and 8 sequences, B not a multiple of
-    the window, shared prefixes of 1 to 33 blocks."""
+    """T G = 8, 1, 8, 4 and 2 query rows per KV head, groups of 7 sequences
+    sharing 1 to 33 blocks."""
     rng = np.random.default_rng(73 + T + Hq)
     lens, share = [], []
     for b in range(21):
