@@ -217,6 +217,30 @@ pkv_status paged_attention_decode(const void* q, const void* k_pool, const void*
                                   void* workspace, size_t workspace_bytes, pkv_dtype dtype, void* stream);
 
 /*
+ * paged_attention_decode_noalloc -- paged_attention_decode for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, layouts, kernels
+ * and results as paged_attention_decode, without the workspace arguments: the
+ * library works in a static device scratch of PKV_NOALLOC_SCRATCH_BYTES (plus
+ * 256 bytes) that each GPU it runs on holds until the process ends.  Calls
+ * whose pkv_decode_workspace_bytes(...) exceeds that return PKV_EWORKSPACE
+ * before anything runs.  Nothing is allocated or freed, by the library or on
+ * its behalf; the scratch's device address is looked up once per device, at
+ * the first call on it.  Every call on one GPU shares that GPU's scratch, and
+ * nothing in it needs clearing between calls (each call writes what it later
+ * reads): two calls in flight at once on one GPU (other streams, other host
+ * threads) race on it and give undefined results.  The partial layout that a
+ * split call leaves at offset 0 of the workspace is not exposed here.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+pkv_status paged_attention_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                          const int32_t* block_tables, const int32_t* context_lens,
+                                          void* out, float* lse_out,
+                                          int B, int T, int Hq, int Hkv, int D, int block_size, int max_blocks,
+                                          int N_blocks, float scale, int partition_size, pkv_dtype dtype,
+                                          void* stream);
+
+/*
  * paged_attention_prefill -- chunked-prefill attention over the paged cache
  * ("Efficient LLM Inference", KV Caching: Verify Reuse, Positions and
  * Windows: attending a prompt chunk by chunk against the cached prefix equals

@@ -18,7 +18,8 @@ PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_EHIP = range(5)
 PKV_FP32, PKV_BF16 = 0, 1
 STATUS_NAMES = {0: "PKV_OK", 1: "PKV_EINVAL", 2: "PKV_EUNSUPPORTED", 3: "PKV_EWORKSPACE", 4: "PKV_EHIP"}
 EXPORTS = ("paged_kv_append", "paged_kv_append_rope", "paged_kv_copy_blocks", "paged_kv_gather",
-           "pkv_decode_workspace_bytes", "paged_attention_decode", "paged_attention_prefill",
+           "pkv_decode_workspace_bytes", "paged_attention_decode", "paged_attention_decode_noalloc",
+           "paged_attention_prefill",
            "pkv_prefill_workspace_bytes", "pkv_prefill_piece_tokens", "lse_reduce",
            "pkv_last_error",
            "pkv_engine_create", "pkv_engine_destroy", "pkv_engine_last_error", "pkv_engine_add_request",
@@ -79,6 +80,8 @@ def load_library(path: pathlib.Path = LIB_PATH) -> ctypes.CDLL:
     lib.pkv_decode_workspace_bytes.restype = S
     lib.paged_attention_decode.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, S, I, P]
     lib.paged_attention_decode.restype = I
+    lib.paged_attention_decode_noalloc.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, I, P]
+    lib.paged_attention_decode_noalloc.restype = I
     lib.paged_attention_prefill.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, S, I, P]
     lib.paged_attention_prefill.restype = I
     lib.pkv_prefill_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
@@ -273,6 +276,28 @@ def paged_attention_decode(q, k_pool, v_pool, block_tables, context_lens, out=No
                                       _i32(context_lens, "context_lens"), _ptr(out), _ptr(lse_out), B, T, Hq, Hkv, D,
                                       bs, max_blocks, N, float(scale), int(partition_size), _ptr(workspace), ws_bytes,
                                       _dtype_code(q), _stream(stream, q.device)))
+    return out
+
+
+PKV_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def paged_attention_decode_noalloc(q, k_pool, v_pool, block_tables, context_lens, out, lse_out=None, scale=None,
+                                   partition_size=0, stream=None):
+    """paged_attention_decode without a workspace: the library works in its
+    static device scratch (PKV_NOALLOC_SCRATCH_BYTES per GPU) and neither it
+    nor this binding allocates.  `out` must be given.  Calls in flight at once
+    on one GPU share that scratch and race."""
+    lib = load_library()
+    check_attention_args(q, k_pool, v_pool, block_tables, context_lens, out, lse_out)
+    B, T, Hq, D = q.shape
+    N, bs, Hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
+    if scale is None:
+        scale = 1.0 / D ** 0.5
+    _check(lib.paged_attention_decode_noalloc(_ptr(q), _ptr(k_pool), _ptr(v_pool), _i32(block_tables, "block_tables"),
+                                              _i32(context_lens, "context_lens"), _ptr(out), _ptr(lse_out), B, T, Hq,
+                                              Hkv, D, bs, block_tables.shape[1], N, float(scale), int(partition_size),
+                                              _dtype_code(q), _stream(stream, q.device)))
     return out
 
 

@@ -93,6 +93,33 @@ int partitions_max(int max_blocks, int block_size, int partition_size) {
 
 }  // namespace
 
+// Scratch of the allocation-free decode entry point: a file-scope device array
+// (each GPU the library runs on holds its own copy until the process ends).
+// Host code never uses the array's name as an address: the device address is
+// looked up once per device with hipGetSymbolAddress and kept.  The first
+// kScratchHead bytes hold the PKV_DEBUG flag; the decode workspace follows.
+constexpr size_t kScratchHead = 256;
+static __device__ __align__(256) unsigned char scratch[kScratchHead + PKV_NOALLOC_SCRATCH_BYTES];
+
+static pkv_status noalloc_scratch(unsigned char** base) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static unsigned char* addr[kMaxDevices] = {nullptr};
+  int dev = 0;
+  pkv_status st = from_hip(hipGetDevice(&dev), "hipGetDevice");
+  if (st != PKV_OK) return st;
+  if (dev < 0 || dev >= kMaxDevices) return fail(PKV_EUNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {   // with this device current: its own copy of the array
+    void* p = nullptr;
+    if ((st = from_hip(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)")) != PKV_OK)
+      return st;
+    addr[dev] = static_cast<unsigned char*>(p);
+  }
+  *base = addr[dev];
+  return PKV_OK;
+}
+
 // K/V rows, queries and outputs move with 16-byte vector loads and stores.
 static bool all_aligned16(std::initializer_list<const void*> ps) {
   for (const void* p : ps)
@@ -214,11 +241,13 @@ pkv_status paged_kv_gather(const void* k_pool, const void* v_pool, const int32_t
 
 }  // extern "C"
 
-// The decode entry point's body.
+// The decode entry points' common body.  noalloc: the workspace and the
+// PKV_DEBUG flag live in the library's static device scratch (its size is
+// checked before anything runs, and nothing is allocated).
 static pkv_status decode_impl(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
                               const int32_t* context_lens, void* out, float* lse_out, int B, int T, int Hq, int Hkv,
                               int D, int block_size, int max_blocks, int N_blocks, float scale, int partition_size,
-                              void* workspace, size_t workspace_bytes, pkv_dtype dtype, void* stream) {
+                              void* workspace, size_t workspace_bytes, pkv_dtype dtype, void* stream, bool noalloc) {
   pkv_status st = check_dtype(dtype);
   if (st != PKV_OK) return st;
   if (B < 0 || T < 1 || Hq < 1) return fail(PKV_EINVAL, "B must be >= 0, T and Hq >= 1");
@@ -244,11 +273,24 @@ static pkv_status decode_impl(const void* q, const void* k_pool, const void* v_p
   a.B = B; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.D = D; a.block_size = block_size; a.max_blocks = max_blocks;
   a.N_blocks = N_blocks; a.scale = scale; a.bf16 = dtype == PKV_BF16;
   const size_t need = pkv_decode_workspace_bytes(B, T, Hq, D, max_blocks, block_size, partition_size);
+  int* dbg_flag = nullptr;
+  if (noalloc) {
+    if (need > (size_t)PKV_NOALLOC_SCRATCH_BYTES)
+      return fail(PKV_EWORKSPACE,
+                  "these sizes need %zu bytes of scratch; the allocation-free entry point has %zu (use "
+                  "paged_attention_decode with a workspace)",
+                  need, (size_t)PKV_NOALLOC_SCRATCH_BYTES);
+    unsigned char* base = nullptr;
+    if ((st = noalloc_scratch(&base)) != PKV_OK) return st;
+    dbg_flag = reinterpret_cast<int*>(base);
+    workspace = base + kScratchHead;
+    workspace_bytes = PKV_NOALLOC_SCRATCH_BYTES;
+  }
   if (need && (!workspace || workspace_bytes < need))
     return fail(PKV_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (debug_enabled() && (st = debug_validate(block_tables, context_lens, B, T, 0, block_size, max_blocks, N_blocks, s)) !=
-                             PKV_OK)
+  if (debug_enabled() && (st = debug_validate(block_tables, context_lens, B, T, 0, block_size, max_blocks, N_blocks, s,
+                                              dbg_flag)) != PKV_OK)
     return st;
   const bool fixed_split = partition_size > 0 && partition_size < max_blocks * block_size;
   if (partition_size == 0 && pkv::verify_tile_for(a))
@@ -286,7 +328,16 @@ pkv_status paged_attention_decode(const void* q, const void* k_pool, const void*
                                   int D, int block_size, int max_blocks, int N_blocks, float scale, int partition_size,
                                   void* workspace, size_t workspace_bytes, pkv_dtype dtype, void* stream) {
   return decode_impl(q, k_pool, v_pool, block_tables, context_lens, out, lse_out, B, T, Hq, Hkv, D, block_size,
-                     max_blocks, N_blocks, scale, partition_size, workspace, workspace_bytes, dtype, stream);
+                     max_blocks, N_blocks, scale, partition_size, workspace, workspace_bytes, dtype, stream, false);
+}
+
+pkv_status paged_attention_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                          const int32_t* block_tables, const int32_t* context_lens, void* out,
+                                          float* lse_out, int B, int T, int Hq, int Hkv, int D, int block_size,
+                                          int max_blocks, int N_blocks, float scale, int partition_size,
+                                          pkv_dtype dtype, void* stream) {
+  return decode_impl(q, k_pool, v_pool, block_tables, context_lens, out, lse_out, B, T, Hq, Hkv, D, block_size,
+                     max_blocks, N_blocks, scale, partition_size, nullptr, 0, dtype, stream, true);
 }
 
 pkv_status paged_attention_prefill(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,

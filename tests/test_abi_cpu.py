@@ -240,3 +240,21 @@ def test_binding_checks_attention_arguments():
         with pytest.raises(exc):
             pkv.check_attention_args(**dict(ok, **change))
 
+
+def test_noalloc_rejects_sizes_beyond_its_scratch():
+    """The allocation-free decode refuses, before touching a device, a call
+    whose workspace would not fit its static scratch (here: the long-context
+    verify shape split into 512-token partitions, about 169 MB)."""
+    lib = pkv.load_library()
+    need = pkv.pkv_decode_workspace_bytes(16, 4, 32, 128, 4096, 16, 512)
+    assert need > pkv.PKV_NOALLOC_SCRATCH_BYTES
+    st = lib.paged_attention_decode_noalloc(Q, K, V, TAB, LENS, OUT, None, 16, 4, 32, 8, 128, 16, 4096, 50000,
+                                            0.088, 512, pkv.PKV_BF16, None)
+    assert st == pkv.PKV_EWORKSPACE
+    msg = lib.pkv_last_error().decode()
+    assert str(need) in msg and str(pkv.PKV_NOALLOC_SCRATCH_BYTES) in msg
+    # argument errors come first, as for paged_attention_decode
+    assert lib.paged_attention_decode_noalloc(None, K, V, TAB, LENS, OUT, None, 2, 1, 8, 2, 128, 16, 4, 8, 0.088, 0,
+                                              pkv.PKV_BF16, None) == pkv.PKV_EINVAL
+    # the 8B-shaped single-token batch fits
+    assert pkv.pkv_decode_workspace_bytes(256, 1, 32, 128, 512, 16, 0) <= pkv.PKV_NOALLOC_SCRATCH_BYTES
