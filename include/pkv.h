@@ -153,9 +153,11 @@ pkv_status paged_kv_copy_blocks(void* k_pool, void* v_pool, const int32_t* src, 
  * needs for these sizes and this partition size.  With partition_size > 0 the
  * workspace starts with the split-KV partials, B*T*Hq*P_max*(D+1) float32
  * values where P_max = ceil(max_blocks * block_size / partition_size); the
- * MFMA tile adds its plan (a header and per-sequence prefix sums) and two
- * normalised piece slots per range, at most 2*2048*min(16, T*Hq)*(D+1)
- * float32 values.  With partition_size = 0 the workspace holds the plan of the
+ * MFMA tile adds its plan (a header and per-sequence prefix sums), one
+ * normalised slot per (range, sequence) piece, at most
+ * (2048*min(16, T*Hq) + B*T*Hq)*(D+1) float32 values, and two slots per range
+ * for the pieces of partitions cut by range boundaries, at most
+ * 2*2048*min(16, T*Hq)*(D+1) float32 values.  With partition_size = 0 the workspace holds the plan of the
  * balanced split (a header, per-unit prefix sums and descriptors) and one
  * normalised partial per (range, unit) piece: (ranges + B*T) * Hq * (D+1)
  * float32 values, where ranges = 2048 / (Hq/4) (256 at Hq = 32).  Returns 0

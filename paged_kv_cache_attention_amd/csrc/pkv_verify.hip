@@ -22,16 +22,17 @@
 // the lengths itself and keeps the per-sequence block prefix sums in LDS;
 // otherwise the planning kernel writes them to the workspace first.
 //
-// Split-KV partitions (partition_size > 0): the same balanced ranges, and a
-// wave cuts its piece of a sequence at the partition boundaries (every PB
-// blocks from position 0).  A partition inside one range leaves its
-// normalised partial and log-sum-exp in the documented [B, T, Hq, P_max]
-// layout (or goes straight to `out` when the sequence has one partition).  A
-// partition cut by range boundaries leaves a piece per range in per-range
-// slots: a range holds at most two such pieces, the one its start cuts and
-// the one its end cuts.  The partition merge kernel combines those pieces into
-// the partition's partial (written back to the documented layout), then
-// merges every sequence's partitions by log-sum-exp.
+// Split-KV partitions (partition_size > 0): the same balanced ranges, walked
+// the same way, and the walk cuts at the partition boundaries (every PB
+// blocks from position 0) without stopping its loads.  A partition inside one
+// range leaves its normalised partial and log-sum-exp in the documented
+// [B, T, Hq, P_max] layout; each partition is also folded by log-sum-exp into
+// a running state of the wave (LDS), which becomes the range's piece of the
+// sequence, exactly as in the single pass.  A partition cut by range
+// boundaries leaves a piece per range in per-range slots: a range holds at
+// most two such pieces, the one its start cuts and the one its end cuts.  The
+// finishing kernel merges each sequence's range pieces into `out` and
+// rebuilds every cut partition's partial from its pieces.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 #include "pkv_tile.h"
@@ -41,18 +42,26 @@ namespace {
 
 constexpr int kBS = 16;
 constexpr int kMaxWpg = 8;
-// Blocks whose K and V are in flight while a wave works on one.  One measured
-// faster than two and three on the 8B shared-prefix decode batch (216.1,
-// 218.2, 222.3 us), the 1B batch (53.8, 54.8, 57.3 us) and the long-context
-// verify batch (432.6, 436.6, 439.8 us).
+// Blocks whose K and V are in flight while a wave works on one.
 constexpr int kTilePD = 1;
+// Running partition state of a wave: 16 rows of D + 4 floats (the padding
+// puts the 4 rows one LDS instruction touches on distinct banks).
+template <int D>
+constexpr int kRunFloats = 16 * (D + 4);
+
+// LDS bytes per wave: the V tile; with partitions as many bytes again (the
+// two together stage a partition's 16 x D float partial, while the V tile is
+// idle) and the running state.
+template <int D, bool PART>
+constexpr int verify_wave_lds() {
+  return tile::run_tile_bytes<D>() * (PART ? 2 : 1) + (PART ? kRunFloats<D> * 4 : 0);
+}
+static_assert(2 * tile::run_tile_bytes<64>() == 16 * 64 * 4 && 2 * tile::run_tile_bytes<128>() == 16 * 128 * 4,
+              "the partition stage is the V tile and as many bytes after it");
 
 constexpr int kInlinePerWave = 512;            // LDS prefix entries per wave
 constexpr int kInlinePT = kInlinePerWave / 64;  // sequences per thread
 constexpr int kMinBlocksPerRange = 16;
-// Partition staging area per wave: 16 rows of D + 4 floats.
-template <int D>
-constexpr int kStageFloats = 16 * (D + 4);
 
 struct VerifyArgs {
   DecodeArgs a;       // with partitions: a.part_out [B, T, Hq, P_max, D], a.part_lse [B, T, Hq, P_max]
@@ -60,7 +69,8 @@ struct VerifyArgs {
   int* prefix;        // [B + 1] blocks per sequence, prefix sums
   const int* first;   // [ranges] first non-empty sequence of each range (index into udesc)
   const int4* udesc;  // [B + 1] non-empty sequences, x = sequence
-  float* part;        // single pass: [(ranges + B)][T][Hq][D + 1]; partitions: [2 * ranges][T][Hq][D + 1]
+  float* part;        // range pieces: [(ranges + B)][T][Hq][D + 1], piece of sequence b in range r at r + b
+  float* cut;         // partitions: pieces of cut partitions, [2 * ranges][T][Hq][D + 1]
   int ranges;
   int PB;             // blocks per partition (partitions only)
 };
@@ -157,16 +167,17 @@ __device__ __forceinline__ void emit_rows(const tile::State<D>& st, const Decode
   }
 }
 
-// A partition's normalised rows, staged through the wave's LDS area so that
-// they leave as whole rows of 16-byte stores (each row D contiguous floats
-// of part_out) instead of 4-byte stores scattered over the rows: rows r < R
-// of the tile, row r being query token t = r / G, head kv G + r % G; lse to
-// part_lse.  The area holds 16 rows of D + 4 floats (the padding puts the 4
-// rows a store instruction writes on distinct banks).
+// A whole partition's normalised rows r < R (query token t = r / G, head
+// kv G + r % G) to the documented partials, through the wave's LDS stage so
+// that they leave as whole rows of 16-byte stores (row D contiguous floats)
+// rather than 64-byte pieces of 16 rows far apart (measured about twice as
+// costly); lse from the row lanes.  Stage row r: D floats, 16-byte chunk c
+// at chunk c ^ 4 ((r / 4) % 4), which puts the 4 rows one write instruction
+// touches on distinct banks.
 template <int D>
 __device__ __forceinline__ void emit_partition_staged(const tile::State<D>& st, const DecodeArgs& a, size_t prow,
                                                       int p, int kv, int G, int R, float* stage, int lane) {
-  constexpr int DT = D / 16, STR = D + 4, C4 = D / 4;   // 16-byte chunks per row
+  constexpr int DT = D / 16, C4 = D / 4;
   const int row = lane & 15, quad = lane >> 4;
   const float l_row = tile::row_sum(st);
 #pragma unroll
@@ -175,38 +186,82 @@ __device__ __forceinline__ void emit_partition_staged(const tile::State<D>& st, 
     const float lr = __shfl(l_row, r);
     const float inv = lr != 0.f ? 1.f / lr : 0.f;
 #pragma unroll
-    for (int d = 0; d < DT; ++d) stage[r * STR + 16 * d + row] = st.acc[d][k] * inv;
+    for (int d = 0; d < DT; ++d)
+      stage[r * D + 4 * ((4 * d + (row >> 2)) ^ (4 * quad)) + (row & 3)] = st.acc[d][k] * inv;
   }
-  if (quad == 0 && row < R) {   // row lane r holds its own max and sum
-    const float lr = l_row;
+  if (quad == 0 && row < R) {   // the row lanes hold their row's max and sum
     const int t = row / G, h = kv * G + (row - t * G);
-    a.part_lse[(prow + (size_t)t * a.Hq + h) * a.P_max + p] = lr != 0.f ? (st.m_row + log2f(lr)) * kLn2 : kNegInf;
+    a.part_lse[(prow + (size_t)t * a.Hq + h) * a.P_max + p] = l_row != 0.f ? (st.m_row + log2f(l_row)) * kLn2
+                                                                           : kNegInf;
   }
-  // (LDS operations of one wave complete in order: the reads see the writes)
+  // (one wave's LDS operations complete in order: the reads see the writes)
   for (int c = lane; c < R * C4; c += 64) {
     const int r = c / C4, c4 = c - r * C4;
     const int t = r / G, h = kv * G + (r - t * G);
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + r * STR + 4 * c4);
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + r * D + 4 * (c4 ^ (4 * ((r >> 2) & 3))));
     store16(a.part_out + ((prow + (size_t)t * a.Hq + h) * a.P_max + p) * D + 4 * c4, v);
   }
 }
 
+// Fold a partition's tile state into the wave's running state: O rows in
+// LDS (row r at run + r * (D + 4), unnormalised, scaled to the running max;
+// each lane keeps to the elements its accumulators hold), the running max
+// (base 2) and denominator of row lane % 16 in registers.  `first`: the
+// running state is empty.
+template <int D>
+__device__ __forceinline__ void fold_partition(const tile::State<D>& st, float* run, float& mrun, float& lrun,
+                                               bool first, int lane) {
+  constexpr int DT = D / 16, STR = D + 4;
+  const int row = lane & 15, quad = lane >> 4;
+  const float l_p = tile::row_sum(st);
+  const float m_new = fmaxf(mrun, st.m_row);
+  // 1 for a side that holds the new max (two empty sides included)
+  const float sa = mrun == m_new ? 1.f : __builtin_amdgcn_exp2f(mrun - m_new);
+  const float sb = st.m_row == m_new ? 1.f : __builtin_amdgcn_exp2f(st.m_row - m_new);
+  lrun = first ? l_p : lrun * sa + l_p * sb;
+  mrun = first ? st.m_row : m_new;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = 4 * quad + k;
+    const float ak = __shfl(sa, r), bk = __shfl(sb, r);
+#pragma unroll
+    for (int d = 0; d < DT; ++d) {
+      float* x = run + r * STR + 16 * d + row;
+      *x = first ? st.acc[d][k] : *x * ak + st.acc[d][k] * bk;
+    }
+  }
+}
+
+// The running state as a tile state (for emit_rows): row sums whole in the
+// quad-0 lanes.
+template <int D>
+__device__ __forceinline__ void load_running(tile::State<D>& st, const float* run, float mrun, float lrun, int lane) {
+  constexpr int DT = D / 16, STR = D + 4;
+  const int row = lane & 15, quad = lane >> 4;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int d = 0; d < DT; ++d) st.acc[d][k] = run[(4 * quad + k) * STR + 16 * d + row];
+  st.m_row = mrun;
+  st.l_part = quad == 0 ? lrun : 0.f;
+}
+
 // INL: the plan is computed in the kernel (LDS); otherwise read from the
-// workspace written by the planning kernel.  LDS (dynamic): one V tile per
-// wave, then with INL the prefix list; with PART a staging area of 16 rows
-// per wave.  PART: split-KV partitions of va.PB blocks.
-template <int D, int PD, bool INL, bool PART>
+// workspace written by the planning kernel.  LDS (dynamic): per wave its V
+// tile and with PART its running state, then with INL the prefix list.
+// PART: split-KV partitions of va.PB blocks.
+template <int D, bool INL, bool PART>
 __global__ __launch_bounds__(64 * kMaxWpg) void verify_mfma_kernel(VerifyArgs va, float scale_log2e) {
   const DecodeArgs& a = va.a;
   const int lane = threadIdx.x & 63;
   const int wpg = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   extern __shared__ __attribute__((aligned(16))) unsigned char vlds[];
-  constexpr int kTileBytes = tile::run_tile_bytes<D, PD>();
-  unsigned char* vtiles = vlds + wave * kTileBytes;
-  int* sprefix = reinterpret_cast<int*>(vlds + wpg * kTileBytes);
-  float* stage = reinterpret_cast<float*>(vlds + wpg * kTileBytes + (INL ? kInlinePerWave * wpg * 4 : 0)) +
-                 wave * kStageFloats<D>;
+  constexpr int kWaveLds = verify_wave_lds<D, PART>();
+  unsigned char* vtile = vlds + wave * kWaveLds;
+  float* stage = reinterpret_cast<float*>(vtile);                                      // PART only
+  float* run = reinterpret_cast<float*>(vtile + 2 * tile::run_tile_bytes<D>());   // PART only
+  int* sprefix = reinterpret_cast<int*>(vlds + wpg * kWaveLds);
   __shared__ int wsc[16];
   int total, per;
   if constexpr (INL) {
@@ -273,43 +328,55 @@ __global__ __launch_bounds__(64 * kMaxWpg) void verify_mfma_kernel(VerifyArgs va
                                 ((size_t)(b * a.T + t_row) * a.Hq + kv * G + (rq - t_row * G)) * D,
                       row_ok, lane);
       const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks;
+      float* piece = va.part + (size_t)(rng + b) * slot_floats;
+      tile::State<D> st;
+      tile::init(st);
       if constexpr (PART) {
-        // the partitions this range holds of sequence b, one at a time
         const int PB = va.PB;
         const int Pb = (plen + PB - 1) / PB;
-        for (int p0 = js; p0 < je;) {
-          const int p = p0 / PB;
-          const int pe = min(je, (p + 1) * PB);
-          tile::State<D> st;
-          tile::init(st);
-          tile::run<D, PD>(st, qreg, hi_row, L, trow + p0, p0, pe - p0, nmax, kpool, vhead, kv_row_bytes,
-                           block_bytes, vtiles, scale_log2e, lane);
-          const bool whole = p0 == p * PB && pe == min(plen, (p + 1) * PB);
-          if (whole && Pb > 1) {
-            emit_partition_staged<D>(st, a, (size_t)b * a.T * a.Hq, p, kv, G, R, stage, lane);
-          } else if (whole) {
-            emit_rows<D>(st, a, b, kv, G, R, true, [&](int, int) { return (float*)nullptr; },
-                         [&](int, int) { return (float*)nullptr; }, lane);
-          } else {
-            // a piece of a partition cut by this range's start (slot 0) or,
-            // starting inside the range, by its end (slot 1)
-            float* slot = va.part + (size_t)(2 * rng + (p0 == p * PB ? 1 : 0)) * slot_floats;
-            emit_rows<D>(st, a, b, kv, G, R, false,
-                         [&](int t, int h) { return slot + ((size_t)t * a.Hq + h) * (D + 1); },
-                         [&](int t, int h) { return slot + ((size_t)t * a.Hq + h) * (D + 1) + D; }, lane);
+        const size_t prow = (size_t)b * a.T * a.Hq;   // + t * Hq + h: the row's partials
+        float mrun = kNegInf, lrun = 0.f;
+        bool first = true;
+        // partition p ends before block kb_end: its partial (whole in this
+        // range) or its piece (cut by a range boundary) when the sequence has
+        // several partitions, and its fold into the running state
+        auto flush = [&](tile::State<D>& s, int kb_end) {
+          // the lane index through an empty asm: what the flush derives from
+          // it (LDS and global addresses) is then computed here, not hoisted
+          // out of the walk's loop, where those registers would crowd the
+          // P.V step (its eight V reads, otherwise issued together, went one
+          // at a time at 247 VGPRs)
+          int ln = lane;
+          __asm__ volatile("" : "+v"(ln));
+          const int p = (kb_end - 1) / PB;
+          const bool starts = js <= p * PB;
+          const bool ends = kb_end == min(plen, (p + 1) * PB);
+          if (Pb > 1) {
+            if (starts && ends) {
+              emit_partition_staged<D>(s, a, prow, p, kv, G, R, stage, ln);
+            } else {
+              // cut by this range's start (slot 0) or, starting in it, by its end (slot 1)
+              float* slot = va.cut + (size_t)(2 * rng + (starts ? 1 : 0)) * slot_floats;
+              emit_rows<D>(s, a, b, kv, G, R, false,
+                           [&](int t, int h) { return slot + ((size_t)t * a.Hq + h) * (D + 1); },
+                           [&](int t, int h) { return slot + ((size_t)t * a.Hq + h) * (D + 1) + D; }, ln);
+            }
           }
-          p0 = pe;
-        }
+          fold_partition<D>(s, run, mrun, lrun, first, ln);
+          first = false;
+          tile::init(s);
+        };
+        tile::run<D, kTilePD>(st, qreg, hi_row, L, trow + js, js, je - js, nmax, kpool, vhead, kv_row_bytes,
+                                   block_bytes, vtile, scale_log2e, lane, PB, flush);
+        flush(st, je);
+        load_running<D>(st, run, mrun, lrun, lane);
       } else {
-        tile::State<D> st;
-        tile::init(st);
-        tile::run<D, PD>(st, qreg, hi_row, L, trow + js, js, je - js, nmax, kpool, vhead, kv_row_bytes, block_bytes,
-                         vtiles, scale_log2e, lane);
-        float* slot = va.part + (size_t)(rng + b) * slot_floats;
-        emit_rows<D>(st, a, b, kv, G, R, direct,
-                     [&](int t, int h) { return slot + ((size_t)t * a.Hq + h) * (D + 1); },
-                     [&](int t, int h) { return slot + ((size_t)t * a.Hq + h) * (D + 1) + D; }, lane);
+        tile::run<D, kTilePD>(st, qreg, hi_row, L, trow + js, js, je - js, nmax, kpool, vhead, kv_row_bytes,
+                                   block_bytes, vtile, scale_log2e, lane);
       }
+      emit_rows<D>(st, a, b, kv, G, R, direct,
+                   [&](int t, int h) { return piece + ((size_t)t * a.Hq + h) * (D + 1); },
+                   [&](int t, int h) { return piece + ((size_t)t * a.Hq + h) * (D + 1) + D; }, lane);
     }
     if (pstart + plen >= F1) break;
     ++b;
@@ -320,12 +387,10 @@ __global__ __launch_bounds__(64 * kMaxWpg) void verify_mfma_kernel(VerifyArgs va
 // (sequence, query token, 4 heads); 16 lanes per head.  A sequence inside one
 // range was written directly.
 template <int D>
-__global__ __launch_bounds__(256) void verify_merge_kernel(VerifyArgs va) {
+__device__ __forceinline__ void merge_pieces(const VerifyArgs& va, int gidx, int lane) {
   constexpr int EPL = D / 16;
   constexpr int BATCH = 16;   // pieces whose loads are issued together
   const DecodeArgs& a = va.a;
-  const int lane = threadIdx.x & 63;
-  const int gidx = blockIdx.x * 4 + (threadIdx.x >> 6);     // ((b * T + t) * Hq/4 + hq)
   const int HG = a.Hq / 4;
   if (gidx >= a.B * a.T * HG) return;
   const int per = va.hdr[1];
@@ -395,104 +460,66 @@ __device__ __forceinline__ void lse_pair(float& l, float (&o)[N], float l2, cons
   l = m + logf(w1 + w2);
 }
 
-// Merge of the split-KV partitions, one wave per output row (b, t, h): lane
-// group g (16 lanes, D/16 elements each) takes partitions g, g + 4, ... in
-// batches whose loads are issued together, and the four groups' running
-// states are combined at the end.  A partition cut by range boundaries is
-// first rebuilt from its pieces (the range holding its first block wrote slot
-// 1, every later range slot 0) and, when the sequence has several
-// partitions, written back to the documented partial layout.  Sequences with
-// one partition inside one range were written directly and are skipped.
+// The partial of a partition cut by range boundaries, rebuilt from its pieces
+// and written to the documented layout: one wave per (range boundary r >= 1,
+// query token, 4 heads).  The partition cut by boundary r, if any, is handled
+// at the first boundary that cuts it; the range holding its first block wrote
+// the piece to slot 1, every later range to slot 0.  Sequences with a single
+// partition have no partials.
 template <int D>
-__global__ __launch_bounds__(256) void partition_merge_kernel(VerifyArgs va) {
+__device__ __forceinline__ void rebuild_cut_partition(const VerifyArgs& va, int gidx, int lane) {
   constexpr int EPL = D / 16;
-  constexpr int NB = 4;   // partitions per group whose loads are issued together
   const DecodeArgs& a = va.a;
-  const int lane = threadIdx.x & 63, grp = lane >> 4, d0 = (lane & 15) * EPL;
-  const int rowi = blockIdx.x * 4 + (threadIdx.x >> 6);   // (b * T + t) * Hq + h
-  if (rowi >= a.B * a.T * a.Hq) return;
-  const int h = rowi % a.Hq, bt = rowi / a.Hq;
-  const int b = bt / a.T, t = bt - b * a.T;
-  const int per = va.hdr[1], PB = va.PB;
+  const int HG = a.Hq / 4;
+  if (gidx >= (va.ranges - 1) * a.T * HG) return;
+  const int hq = gidx % HG, rt = gidx / HG;
+  const int t = rt % a.T, r = rt / a.T + 1;
+  const int total = va.hdr[0], per = va.hdr[1], PB = va.PB;
+  const int F = r * per;
+  if (F >= total) return;
+  int lo = 0, hi = a.B;   // the sequence holding block F: prefix[lo] <= F < prefix[lo + 1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (va.prefix[mid] <= F) lo = mid; else hi = mid;
+  }
+  const int b = lo;
   const int pstart = va.prefix[b], plen = va.prefix[b + 1] - pstart;
-  const int Pb = (plen + PB - 1) / PB;
-  uint16_t* out = static_cast<uint16_t*>(a.out) + (size_t)rowi * D + d0;
-  float* lse_out = a.lse_out ? a.lse_out + rowi : nullptr;
-  if (plen > 0 && Pb == 1 && pstart / per == (pstart + plen - 1) / per) return;   // written by the tile
+  const int off = F - pstart;
+  if (off % PB == 0 || plen <= PB) return;   // no partition cut here, or a single partition
+  const int p = off / PB;
+  const int r0 = (pstart + p * PB) / per;
+  if (r != r0 + 1) return;
+  const int r1 = (pstart + min(plen, (p + 1) * PB) - 1) / per;
+  const int h = hq * 4 + (lane >> 4), d0 = (lane & 15) * EPL;
   const size_t slot_floats = (size_t)a.T * a.Hq * (D + 1);
   const size_t srow = ((size_t)t * a.Hq + h) * (D + 1);
-  float* po = a.part_out + (size_t)rowi * a.P_max * D + d0;
-  float* pl = a.part_lse + (size_t)rowi * a.P_max;
+  const float* src = va.cut + (size_t)(2 * r0 + 1) * slot_floats + srow;
+  float l = src[D], o[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) o[e] = src[d0 + e];
+  for (int rr = r0 + 1; rr <= r1; ++rr) {
+    const float* s2 = va.cut + (size_t)(2 * rr) * slot_floats + srow;
+    float o2[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o2[e] = s2[d0 + e];
+    lse_pair<EPL>(l, o, s2[D], o2);
+  }
+  const size_t prow = ((size_t)b * a.T + t) * a.Hq + h;
+  float* po = a.part_out + (prow * a.P_max + p) * D + d0;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) po[e] = l == kNegInf ? 0.f : o[e];
+  if ((lane & 15) == 0) a.part_lse[prow * a.P_max + p] = l;
+}
 
-  float m = kNegInf, ssum = 0.f, acc[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  for (int p0 = grp; p0 < Pb; p0 += 4 * NB) {
-    float lv[NB], ov[NB][EPL];
-    int cut_lo[NB], cut_hi[NB];   // ranges of a cut partition (cut_lo < cut_hi), else equal
-#pragma unroll
-    for (int k = 0; k < NB; ++k) {
-      const int p = p0 + 4 * k;
-      lv[k] = kNegInf;
-      cut_lo[k] = cut_hi[k] = 0;
-      if (p < Pb) {
-        const int s0 = pstart + p * PB, e0 = pstart + min(plen, (p + 1) * PB);
-        const int r0 = s0 / per, r1 = (e0 - 1) / per;
-        const float* src = r0 == r1 ? nullptr : va.part + (size_t)(2 * r0 + 1) * slot_floats + srow;
-        lv[k] = src ? src[D] : pl[p];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) ov[k][e] = src ? src[d0 + e] : po[(size_t)p * D + e];
-        cut_lo[k] = r0;
-        cut_hi[k] = r1;
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < NB; ++k) {
-      if (cut_lo[k] == cut_hi[k]) continue;
-      for (int r = cut_lo[k] + 1; r <= cut_hi[k]; ++r) {   // the later pieces (slot 0 of each later range)
-        const float* src = va.part + (size_t)(2 * r) * slot_floats + srow;
-        float o2[EPL];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) o2[e] = src[d0 + e];
-        lse_pair<EPL>(lv[k], ov[k], src[D], o2);
-      }
-      if (Pb > 1) {   // the partition's partial, in the documented layout
-        const int p = p0 + 4 * k;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) po[(size_t)p * D + e] = lv[k] == kNegInf ? 0.f : ov[k][e];
-        if ((lane & 15) == 0) pl[p] = lv[k];
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < NB; ++k) {
-      if (lv[k] == kNegInf) continue;   // absent or empty partition: its o is not read
-      const float nm = fmaxf(m, lv[k]);
-      const float sa = __builtin_amdgcn_exp2f((m - nm) * kLog2e);
-      const float sb = __builtin_amdgcn_exp2f((lv[k] - nm) * kLog2e);
-      ssum = ssum * sa + sb;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = acc[e] * sa + sb * ov[k][e];
-      m = nm;
-    }
-  }
-  // combine the four groups (partners 16 and 32 lanes away)
-#pragma unroll
-  for (int off = 16; off < 64; off <<= 1) {
-    const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(ssum, off);
-    const float nm = fmaxf(m, m2);
-    const float sa = m == kNegInf ? 0.f : __builtin_amdgcn_exp2f((m - nm) * kLog2e);
-    const float sb = m2 == kNegInf ? 0.f : __builtin_amdgcn_exp2f((m2 - nm) * kLog2e);
-    ssum = ssum * sa + s2 * sb;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = acc[e] * sa + __shfl_xor(acc[e], off) * sb;
-    m = nm;
-  }
-  if (grp == 0) {
-    const float inv = ssum != 0.f ? 1.f / ssum : 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) out[e] = f32_to_bf16_rne(acc[e] * inv);
-    if (lse_out && lane == 0) *lse_out = ssum != 0.f ? m + logf(ssum) : kNegInf;
-  }
+// After the tile: workgroups [0, merge_blocks) merge range pieces into `out`,
+// the rest (partitions only) rebuild cut partitions.  Four waves per workgroup.
+template <int D>
+__global__ __launch_bounds__(256) void verify_finish_kernel(VerifyArgs va, int merge_blocks) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if ((int)blockIdx.x < merge_blocks)
+    merge_pieces<D>(va, blockIdx.x * 4 + wave, lane);
+  else
+    rebuild_cut_partition<D>(va, (blockIdx.x - merge_blocks) * 4 + wave, lane);
 }
 
 int verify_ranges(int Hkv) { return kStreamWaves / Hkv; }   // one wave per KV head and range
@@ -542,10 +569,10 @@ size_t verify_workspace_bytes(int B, int T, int Hq, int D) {
   return plan_layout(B).end + rows * (D + 1) * 4;
 }
 
-// Beyond the documented partials: the plan and two piece slots per range.
+// Beyond the documented partials: the plan, the range-piece slots of the
+// single pass, then two slots per range for pieces of cut partitions.
 size_t verify_partition_extra_bytes(int B, int T, int Hq, int D) {
-  const size_t rows = (size_t)kStreamWaves * (T * Hq < 16 ? T * Hq : 16);
-  return plan_layout(B).end + 2 * rows * (D + 1) * 4;
+  return verify_workspace_bytes(B, T, Hq, D) + 2 * (size_t)kStreamWaves * (T * Hq < 16 ? T * Hq : 16) * (D + 1) * 4;
 }
 
 hipError_t launch_verify_mfma(const DecodeArgs& a, void* workspace, hipStream_t stream) {
@@ -567,10 +594,11 @@ hipError_t launch_verify_mfma(const DecodeArgs& a, void* workspace, hipStream_t 
   int4* udesc = reinterpret_cast<int4*>(ws + pl.udesc);
   va.hdr = hdr; va.prefix = prefix; va.first = first; va.udesc = udesc;
   va.part = reinterpret_cast<float*>(ws + pl.end);
-  // the V tiles of every wave of a workgroup share its LDS: fewer waves per
-  // workgroup where they would not fit (the grid then has more workgroups)
-  const size_t tile_bytes = a.D == 64 ? tile::run_tile_bytes<64, kTilePD>() : tile::run_tile_bytes<128, kTilePD>();
-  const size_t stage_bytes = part ? (a.D == 64 ? kStageFloats<64> : kStageFloats<128>) * 4 : 0;
+  va.cut = va.part + ((size_t)va.ranges + a.B) * a.T * a.Hq * (a.D + 1);
+  // the per-wave LDS of a workgroup: fewer waves per workgroup where it
+  // would not fit (the grid then has more workgroups)
+  const size_t wave_lds = a.D == 64 ? (part ? verify_wave_lds<64, true>() : verify_wave_lds<64, false>())
+                                    : (part ? verify_wave_lds<128, true>() : verify_wave_lds<128, false>());
   int wpg = a.Hkv < kMaxWpg ? a.Hkv : kMaxWpg;
   // At D = 64, workgroups of at most 4 waves (twice as many per CU, the same
   // waves per SIMD) measured faster: 1B decode batch 51.4 against 53.0 us.
@@ -579,9 +607,9 @@ hipError_t launch_verify_mfma(const DecodeArgs& a, void* workspace, hipStream_t 
   if (a.D == 64)
     while (wpg > 4 && wpg % 2 == 0) wpg /= 2;
   const size_t lds_cap = (size_t)device_lds_per_block() - 64;
-  while (wpg % 2 == 0 && (size_t)wpg * (tile_bytes + stage_bytes) > lds_cap) wpg /= 2;
-  const size_t tiles = (size_t)wpg * tile_bytes;
-  const size_t lds_inl = tiles + (size_t)kInlinePerWave * wpg * 4 + (size_t)wpg * stage_bytes;
+  while (wpg % 2 == 0 && (size_t)wpg * wave_lds > lds_cap) wpg /= 2;
+  const size_t lds_waves = (size_t)wpg * wave_lds;
+  const size_t lds_inl = lds_waves + (size_t)kInlinePerWave * wpg * 4;
   const bool inl = a.B + 1 <= kInlinePerWave * wpg && lds_inl <= lds_cap;
   hipError_t e = hipSuccess;
   // one unit per sequence: blocks = ceil(L / 16)
@@ -589,9 +617,9 @@ hipError_t launch_verify_mfma(const DecodeArgs& a, void* workspace, hipStream_t 
   if (e != hipSuccess) return e;
   const float sl2 = a.scale * kLog2e;
   const dim3 grid(va.ranges * (a.Hkv / wpg)), block(64 * wpg);
-  const size_t lds = inl ? lds_inl : tiles + (size_t)wpg * stage_bytes;
+  const size_t lds = inl ? lds_inl : lds_waves;
 #define PKV_VERIFY_LAUNCH(DD, INLV, PARTV) \
-  hipLaunchKernelGGL((verify_mfma_kernel<DD, kTilePD, INLV, PARTV>), grid, block, lds, stream, va, sl2)
+  hipLaunchKernelGGL((verify_mfma_kernel<DD, INLV, PARTV>), grid, block, lds, stream, va, sl2)
   if (a.D == 64) {
     if (part) { if (inl) PKV_VERIFY_LAUNCH(64, true, true); else PKV_VERIFY_LAUNCH(64, false, true); }
     else { if (inl) PKV_VERIFY_LAUNCH(64, true, false); else PKV_VERIFY_LAUNCH(64, false, false); }
@@ -601,19 +629,14 @@ hipError_t launch_verify_mfma(const DecodeArgs& a, void* workspace, hipStream_t 
   }
 #undef PKV_VERIFY_LAUNCH
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (part) {
-    const int rows = a.B * a.T * a.Hq;
-    if (a.D == 64)
-      hipLaunchKernelGGL((partition_merge_kernel<64>), dim3((rows + 3) / 4), dim3(256), 0, stream, va);
-    else
-      hipLaunchKernelGGL((partition_merge_kernel<128>), dim3((rows + 3) / 4), dim3(256), 0, stream, va);
-    return hipGetLastError();
-  }
-  const int waves = a.B * a.T * (a.Hq / 4);
+  const int merge_blocks = (a.B * a.T * (a.Hq / 4) + 3) / 4;
+  const int fix_blocks = part ? ((va.ranges - 1) * a.T * (a.Hq / 4) + 3) / 4 : 0;
+  if (merge_blocks + fix_blocks == 0) return hipSuccess;
+  const dim3 fgrid(merge_blocks + fix_blocks);
   if (a.D == 64)
-    hipLaunchKernelGGL((verify_merge_kernel<64>), dim3((waves + 3) / 4), dim3(256), 0, stream, va);
+    hipLaunchKernelGGL((verify_finish_kernel<64>), fgrid, dim3(256), 0, stream, va, merge_blocks);
   else
-    hipLaunchKernelGGL((verify_merge_kernel<128>), dim3((waves + 3) / 4), dim3(256), 0, stream, va);
+    hipLaunchKernelGGL((verify_finish_kernel<128>), fgrid, dim3(256), 0, stream, va, merge_blocks);
   return hipGetLastError();
 }
 

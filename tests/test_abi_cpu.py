@@ -37,12 +37,15 @@ def test_workspace_sizing():
     def partitioned(B, T, Hq, D, P):
         """The documented partials (offset 0), rounded up to 256 bytes, then
         the tile's plan (a header, B + 1 prefix sums, 2048 range starts,
-        B + 1 descriptors, each area rounded to 256 bytes) and two piece slots
-        of min(16, T * Hq) rows per range for the 2048 ranges of Hkv = 1."""
+        B + 1 descriptors, each area rounded to 256 bytes), one piece slot of
+        T * Hq rows per (range, sequence) -- at most 2048 * min(16, T * Hq)
+        + B * T * Hq rows -- and two slots of min(16, T * Hq) rows per range
+        for the 2048 ranges of Hkv = 1."""
         r = lambda n: -(-n // 256) * 256
         partials = r(B * T * Hq * P * (D + 1) * 4)
         plan = 256 + r((B + 1) * 4) + r(2048 * 4) + r((B + 1) * 16)
-        return partials + plan + 2 * 2048 * min(16, T * Hq) * (D + 1) * 4
+        pieces = (2048 * min(16, T * Hq) + B * T * Hq) * (D + 1) * 4
+        return partials + plan + pieces + 2 * 2048 * min(16, T * Hq) * (D + 1) * 4
     # P_max = ceil(64*16/256) = 4 partitions
     assert f(4, 1, 32, 128, 64, 16, 256) == partitioned(4, 1, 32, 128, 4)
     assert f(16, 4, 32, 128, 4096, 16, 512) == partitioned(16, 4, 32, 128, 128)
