@@ -16,7 +16,7 @@ import torch
 import oracle
 import paged_kv_cache_attention_amd as pkv
 from paged_kv_cache_attention_amd.serve import PagedExecutor
-from gpu_util import check_attention, host
+from gpu_util import check_attention, check_attention_pbf16, host
 
 pytestmark = pytest.mark.gpu
 
@@ -84,14 +84,19 @@ def test_engine_serves_16_requests_with_preemption(prefix_cache):
             Q = oracle.round_to_bf16(oracle.rope_rotate(Eq[hist[s:L]], pos[s:], THETA))
             got = host(outputs[i]).reshape(L - s, HQ, D)
             ref = np.zeros_like(got)
+            abs_ref = np.zeros_like(got)
             for r in range(L - s):
                 for h in range(HQ):
                     kh = h // (HQ // HKV)
                     ref[r, h], _ = oracle.softmax_attention_row(Q[r, h], K[: s + r + 1, kh], Vv[: s + r + 1, kh],
                                                                 1.0 / D ** 0.5)
+                    abs_ref[r, h], _ = oracle.softmax_attention_row(Q[r, h], K[: s + r + 1, kh],
+                                                                    np.abs(Vv[: s + r + 1, kh]), 1.0 / D ** 0.5)
             kind = "prefill" if plan.kind[i] == pkv.PKV_ENGINE_PREFILL else "decode"
-            floor = 2.0 ** -16 * float(np.abs(Ev).max()) + 1e-5 if kind == "prefill" else 1e-5
-            check_attention(got, ref, "bf16", f"request {rid} {kind} at {s}..{L}", floor=floor)
+            if kind == "prefill":   # the prefill tile rounds P to bf16 once
+                check_attention_pbf16(got, ref, abs_ref, f"request {rid} prefill at {s}..{L}")
+            else:
+                check_attention(got, ref, "bf16", f"request {rid} decode at {s}..{L}")
             checked["rows"] += L - s
             toks.append(next_token(rid, len(hist)))
         return np.array(toks, dtype=np.int32)

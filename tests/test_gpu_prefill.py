@@ -15,7 +15,8 @@ import torch
 import oracle
 import workload
 import paged_kv_cache_attention_amd as pkv
-from gpu_util import appended_oracle_pools, check_attention, check_lse, host, mfma_floor, oracle_inputs, upload
+from gpu_util import (appended_oracle_pools, check_attention, check_attention_pbf16, check_lse, host, oracle_inputs,
+                      upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -33,10 +34,18 @@ def prefill(w, d, lse=True, piece_tokens=0):
     return host(out), (host(lse_t) if lse else None)
 
 
+def oracle_with_abs(q, kp, vp, tables, lens, scale, block_size):
+    """The oracle's (out, lse) and its attention over |V| (the scale of the
+    P-rounding bound of the prefill tile)."""
+    ref, ref_lse = oracle.paged_attention(q, kp, vp, tables, lens, scale, block_size)
+    abs_ref, _ = oracle.paged_attention(q, kp, np.abs(vp), tables, lens, scale, block_size)
+    return ref, ref_lse, abs_ref
+
+
 def check_vs_oracle(w, out, lse, where, seqs=None):
-    ref, ref_lse = oracle.paged_attention(*oracle_inputs(w, seqs), w.scale, w.block_size)
+    ref, ref_lse, abs_ref = oracle_with_abs(*oracle_inputs(w, seqs), w.scale, w.block_size)
     sel = slice(None) if seqs is None else list(seqs)
-    check_attention(out[sel], ref, "bf16", where, floor=mfma_floor(w))
+    check_attention_pbf16(out[sel], ref, abs_ref, where)
     if lse is not None:
         check_lse(lse[sel], ref_lse, where)
 
@@ -111,9 +120,9 @@ def test_prefill_rows_equal_decode_rows():
         dec = pkv.paged_attention_decode(d["q"][:, t:t + 1].contiguous(), d["k"], d["v"], d["tables"], lens_t,
                                          scale=float(w.scale))
         torch.cuda.synchronize()
-        ref, _ = oracle.paged_attention(w.values(w.q)[:, t:t + 1], w.values(w.k_pool), w.values(w.v_pool),
-                                        w.block_tables, w.context_lens - T + t + 1, w.scale, w.block_size)
-        check_attention(out[:, t:t + 1], ref, "bf16", f"prefill row {t}", floor=mfma_floor(w))
+        ref, _, abs_ref = oracle_with_abs(w.values(w.q)[:, t:t + 1], w.values(w.k_pool), w.values(w.v_pool),
+                                          w.block_tables, w.context_lens - T + t + 1, w.scale, w.block_size)
+        check_attention_pbf16(out[:, t:t + 1], ref, abs_ref, f"prefill row {t}")
         check_attention(host(dec), ref, "bf16", f"decode row {t}")
 
 
@@ -128,9 +137,9 @@ def test_llama8b_chunked_prefill_full():
     out, lse = prefill(w, d)
     kp, vp = appended_oracle_pools(w)
     for b in (int(np.argmax(w.context_lens)), int(np.argmin(w.context_lens))):
-        ref, ref_lse = oracle.paged_attention(w.values(w.q)[b:b + 1], kp, vp, w.block_tables[b:b + 1],
-                                              w.context_lens[b:b + 1], w.scale, w.block_size)
-        check_attention(out[b:b + 1], ref, "bf16", f"8B prefill seq {b}", floor=mfma_floor(w))
+        ref, ref_lse, abs_ref = oracle_with_abs(w.values(w.q)[b:b + 1], kp, vp, w.block_tables[b:b + 1],
+                                                w.context_lens[b:b + 1], w.scale, w.block_size)
+        check_attention_pbf16(out[b:b + 1], ref, abs_ref, f"8B prefill seq {b}")
         check_lse(lse[b:b + 1], ref_lse, f"8B prefill seq {b}")
 
 
@@ -169,9 +178,9 @@ def test_prefill_maximum_chunk_sampled_rows():
     rows = sorted({0, 1, 15, 16, 127, 128, 4095, 8191 - pre % 16, T - 2, T - 1, *rng.integers(0, T, size=6).tolist()})
     L = int(w.context_lens[0])
     for t in rows:
-        ref, ref_lse = oracle.paged_attention(w.values(w.q)[:, t:t + 1], w.values(w.k_pool), w.values(w.v_pool),
-                                              w.block_tables, np.array([L - T + t + 1]), w.scale, w.block_size)
-        check_attention(out[:, t:t + 1], ref, "bf16", f"max chunk row {t}", floor=mfma_floor(w))
+        ref, ref_lse, abs_ref = oracle_with_abs(w.values(w.q)[:, t:t + 1], w.values(w.k_pool), w.values(w.v_pool),
+                                                w.block_tables, np.array([L - T + t + 1]), w.scale, w.block_size)
+        check_attention_pbf16(out[:, t:t + 1], ref, abs_ref, f"max chunk row {t}")
         check_lse(lse[:, t:t + 1], ref_lse, f"max chunk row {t}")
 
 
@@ -193,8 +202,9 @@ PIECE_CASES = [  # (D, Hq, Hkv, T, lens, piece_tokens)
 @pytest.mark.parametrize("D,Hq,Hkv,T,lens,piece_tokens", PIECE_CASES)
 def test_prefill_key_pieces(D, Hq, Hkv, T, lens, piece_tokens):
     """Items split into key pieces of piece_tokens tokens, one workgroup each,
-    merged by log-sum-exp: the oracle's result, the unsplit call's within
-    rounding, and the same bits on a second call."""
+    merged by log-sum-exp: the oracle's result (and the unsplit call's, each
+    within the P-rounding bound of the oracle), the unsplit call's LSE, and
+    the same bits on a second call."""
     w = workload.uniform_batch("pieces", seed=151 + T, B=len(lens), T=T, Hq=Hq, Hkv=Hkv, D=D, dtype="bf16",
                                lens=lens)
     say("prefill pieces", D, Hq, Hkv, T, lens, piece_tokens)
@@ -202,8 +212,7 @@ def test_prefill_key_pieces(D, Hq, Hkv, T, lens, piece_tokens):
     out, lse = prefill(w, d, piece_tokens=piece_tokens)
     check_vs_oracle(w, out, lse, f"prefill pieces of {piece_tokens} D={D} T={T}")
     out0, lse0 = prefill(w, d, piece_tokens=0)
-    ref_ulp = oracle.bf16_ulp(out0)
-    assert (np.abs(out - out0) <= 2 * ref_ulp + mfma_floor(w)).all(), "split and unsplit results differ"
+    check_vs_oracle(w, out0, lse0, f"prefill unsplit D={D} T={T}")
     assert np.allclose(lse, lse0, atol=1e-4, rtol=0)
     out2, lse2 = prefill(w, d, piece_tokens=piece_tokens)
     assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
@@ -233,7 +242,7 @@ def test_prefill_one_sequence_long_prefix_suggested_pieces():
     L = int(w.context_lens[0])
     rng = np.random.default_rng(3)
     for t in sorted({0, 1, 127, 128, 255, T - 1, *rng.integers(0, T, size=4).tolist()}):
-        ref, ref_lse = oracle.paged_attention(w.values(w.q)[:, t:t + 1], w.values(w.k_pool), w.values(w.v_pool),
-                                              w.block_tables, np.array([L - T + t + 1]), w.scale, w.block_size)
-        check_attention(out[:, t:t + 1], ref, "bf16", f"one long sequence row {t}", floor=mfma_floor(w))
+        ref, ref_lse, abs_ref = oracle_with_abs(w.values(w.q)[:, t:t + 1], w.values(w.k_pool), w.values(w.v_pool),
+                                                w.block_tables, np.array([L - T + t + 1]), w.scale, w.block_size)
+        check_attention_pbf16(out[:, t:t + 1], ref, abs_ref, f"one long sequence row {t}")
         check_lse(lse[:, t:t + 1], ref_lse, f"one long sequence row {t}")
