@@ -48,8 +48,12 @@ def live_slots(w):
     return int(live.sum())
 
 
-def algorithmic_bytes(w):
-    """Bytes the decode call must move (unique), and the logical KV bytes (each sequence in full)."""
+def algorithmic_bytes(w, part=0):
+    """Bytes the decode call must move (unique), and the logical KV bytes
+    (each sequence in full).  With split-KV partitions of `part` tokens the
+    call also writes each partition's normalised partial and lse (fp32, D + 1
+    values per row) for every sequence of more than one partition; the
+    reduce folds them on chip, so they are not read back."""
     e = w.elem_bytes
     row = w.Hkv * w.D * e                      # one token, all KV heads, K or V
     kv_unique = 2 * row * live_slots(w)
@@ -57,8 +61,12 @@ def algorithmic_bytes(w):
     qo = 2 * w.B * w.T * w.Hq * w.D * e        # q read + out written
     tables = 4 * int(np.sum(-(-w.context_lens // w.block_size))) + 4 * w.B
     append = 2 * 2 * w.B * w.T * row if w.lens_pre is not None else 0   # k_new+v_new read and written
-    return dict(decode=kv_unique + qo + tables, logical=kv_logical + qo + tables, append=append,
-                kv_unique=kv_unique, kv_logical=kv_logical)
+    partials = 0
+    if part:
+        pb = -(-w.context_lens.astype(np.int64) // part)
+        partials = int(np.sum(np.where(pb > 1, pb, 0))) * w.T * w.Hq * (w.D + 1) * 4
+    return dict(decode=kv_unique + qo + tables + partials, logical=kv_logical + qo + tables + partials,
+                append=append, kv_unique=kv_unique, kv_logical=kv_logical, partials=partials)
 
 
 # Decode-kernel sources whose hash guards the committed traffic figures (both
@@ -75,13 +83,15 @@ def decode_uses_tile(w):
             and w.B <= 8192)
 
 
-def measured_traffic(workload_name):
+def measured_traffic(workload_name, part=0):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
     counter summary (FETCH_SIZE + WRITE_SIZE, calibrated), or None when there
-    is none for this workload or the kernel sources changed since."""
+    is none for this workload and partition size or the kernel sources
+    changed since."""
     import hashlib
     import re
-    prof = os.path.join(ROOT, "profiles", f"paged_decode_{workload_name}.md")
+    suffix = f"_partitions_{part}" if part else ""
+    prof = os.path.join(ROOT, "profiles", f"paged_decode_{workload_name}{suffix}.md")
     if not os.path.exists(prof):
         return None
     m = re.search(r"traffic-bytes: fetch=(\d+) write=(\d+) source-sha256=([0-9a-f]+)", open(prof).read())
@@ -435,7 +445,7 @@ def main():
         cold = np.array([a.elapsed_time(b) for a, b in cev])
         del flush
 
-    nb = algorithmic_bytes(w)
+    nb = algorithmic_bytes(w, part)
     achieved = nb["decode"] / (decode_ms * 1e-3) / 1e9
     seq_steps = w.B / (ms_step * 1e-3)
     result = {
@@ -447,11 +457,14 @@ def main():
                    "append": has_append},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(w.name) if part == 0 else None,
-                     "kernel": ("paged_attention_decode call (partition kernel + lse merge)" if part
+                     "traffic": measured_traffic(w.name, part),
+                     "kernel": (("paged_attention_decode call (balanced MFMA tile with split-KV partitions"
+                                 " + piece merge)" if decode_uses_tile(w) else
+                                 "paged_attention_decode call (fixed partitions + lse merge)") if part
                                 else "paged_attention_decode call (balanced MFMA tile + piece merge)" if decode_uses_tile(w)
                                 else "paged_attention_decode call (plan + balanced decode + boundary merge)"),
-                     "bytes_per_launch": nb["decode"], "launch_ms": round(decode_ms, 5),
+                     "bytes_per_launch": nb["decode"], "partial_bytes": nb["partials"],
+                     "launch_ms": round(decode_ms, 5),
                      "launch_ms_p10_p50_p90": [round(float(np.percentile(warm, p)), 5) for p in (10, 50, 90)],
                      "logical_GBps": round(nb["logical"] / (decode_ms * 1e-3) / 1e9, 1)},
     }
