@@ -82,6 +82,36 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
   return u;
 }
 
+// V^T operands of four column tiles: two ds_read_b64_tr_b16 each, at ad[i]
+// (keys 4 quad .. +3 of a 32-key chunk) and HI bytes further (16 keys on),
+// issued together in one asm block that waits for them (lgkmcnt(0)) before
+// it ends.  As builtins, these reads got an s_waitcnt vmcnt(0) from the
+// compiler (it cannot tell the staged step from the one being loaded by
+// global_load_lds), which waited for the next step's loads, just issued:
+// every step then ran with its prefetch drained.
+typedef uint32_t u32x2_v __attribute__((ext_vector_type(2)));
+template <int HI>
+__device__ __forceinline__ void vt_reads4(u32x2_v (&lo)[4], u32x2_v (&hi)[4], const uint32_t (&ad)[4]) {
+  static_assert(HI == 4096, "16 staged rows of 2 D bytes, D = 128");
+#define PKV_VT_READS4(OFF)                                                                                        \
+  __asm__ volatile(                                                                                               \
+      "ds_read_b64_tr_b16 %0, %8\n\t"                                                                           \
+      "ds_read_b64_tr_b16 %4, %8 offset:" OFF "\n\t"                                                           \
+      "ds_read_b64_tr_b16 %1, %9\n\t"                                                                           \
+      "ds_read_b64_tr_b16 %5, %9 offset:" OFF "\n\t"                                                           \
+      "ds_read_b64_tr_b16 %2, %10\n\t"                                                                          \
+      "ds_read_b64_tr_b16 %6, %10 offset:" OFF "\n\t"                                                          \
+      "ds_read_b64_tr_b16 %3, %11\n\t"                                                                          \
+      "ds_read_b64_tr_b16 %7, %11 offset:" OFF "\n\t"                                                          \
+      "s_waitcnt lgkmcnt(0)"                                                                                      \
+      : "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3]), "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(hi[2]),       \
+        "=&v"(hi[3])                                                                                              \
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])                                                            \
+      : "memory")
+  PKV_VT_READS4("4096");
+#undef PKV_VT_READS4
+}
+
 // TPW 16-row tiles per wave, STEP keys per staged step.
 template <int D, int TPW, int STEP>
 struct PGeo {
@@ -447,49 +477,65 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
         kc[h][c] = *reinterpret_cast<const u32x4_t*>(ks + (16 * h + row) * PG::ROWB +
                                                      ((quad + 4 * c) ^ PG::swz_k(16 * h + row)) * 16);
     __builtin_amdgcn_sched_barrier(0);
-    // tile by tile, so that tile 0's scores are ready while tile 1's
-    // products still run
 #pragma unroll
-    for (int j = 0; j < TPW; ++j)
+    for (int c = 0; c < KS; ++c)
 #pragma unroll
-      for (int c = 0; c < KS; ++c)
+      for (int h = 0; h < NQ; ++h)
 #pragma unroll
-        for (int h = 0; h < NQ; ++h)
+        for (int j = 0; j < TPW; ++j)
           sacc[j][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kc[h][c]), as_bf16x8(qreg[j][c]), sacc[j][h],
                                                                0, 0, 0);
-    // the step's V^T chunks, in flight during the softmax
+    // the step's V^T chunks, read while the QK^T products run: keys
+    // 32 kk + 4 quad .. +3, then 16 keys further, for column 16 d + row, two
+    // transposing reads each (ds_read_b64_tr_b16: lane i of each 16-lane group
+    // receives element i % 4 of the 8-byte chunk that lane 4 k + i / 4 of the
+    // group addresses, k = 0..3).  At D = 128 four column tiles go per asm
+    // block (vt_reads4); at D = 64 the asm blocks spilled at the 128-VGPR
+    // budget of four waves per SIMD, so the reads stay builtins there.
     bf16x8_v vb[NK][DT];
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk)
+    for (int kk = 0; kk < NK; ++kk) {
+      const int vrow = 32 * kk + 4 * quad + (row >> 2);
+      auto vaddr = [&](int d) {
+        return vs + vrow * PG::ROWB + (((2 * d + ((row & 3) >> 1)) ^ PG::swz_v(vrow)) * 16) + 8 * (row & 1);
+      };
+      if constexpr (D == 128) {
 #pragma unroll
-      for (int d = 0; d < DT; ++d) {
-        // keys 32 kk + 4 quad .. +3, then 16 keys further, for column
-        // 16 d + row: two transposing reads (ds_read_b64_tr_b16: lane i of
-        // each 16-lane group receives element i % 4 of the 8-byte chunk that
-        // lane 4 k + i / 4 of the group addresses, k = 0..3)
-        const int vrow = 32 * kk + 4 * quad + (row >> 2);
-        const unsigned char* vr = vs + vrow * PG::ROWB + (((2 * d + ((row & 3) >> 1)) ^ PG::swz_v(vrow)) * 16) +
-                                  8 * (row & 1);
-        const i16x4_v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4_v*)(const_cast<unsigned char*>(vr)));
-        const i16x4_v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4_v*)(const_cast<unsigned char*>(vr + 16 * PG::ROWB)));
-        u32x4_t w;
-        __builtin_memcpy(&w, &lo, 8);
-        __builtin_memcpy(reinterpret_cast<unsigned char*>(&w) + 8, &hi, 8);
-        vb[kk][d] = as_bf16x8(w);
+        for (int d0 = 0; d0 < DT; d0 += 4) {
+          uint32_t ad[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            ad[i] = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)(
+                const_cast<unsigned char*>(vaddr(d0 + i)));
+          u32x2_v lo[4], hi[4];
+          vt_reads4<16 * PG::ROWB>(lo, hi, ad);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vb[kk][d0 + i] = as_bf16x8(u32x4_t{lo[i].x, lo[i].y, hi[i].x, hi[i].y});
+        }
+      } else {
+#pragma unroll
+        for (int d = 0; d < DT; ++d) {
+          const unsigned char* vr = vaddr(d);
+          const i16x4_v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_v*)(const_cast<unsigned char*>(vr)));
+          const i16x4_v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_v*)(const_cast<unsigned char*>(vr + 16 * PG::ROWB)));
+          u32x4_t w;
+          __builtin_memcpy(&w, &lo, 8);
+          __builtin_memcpy(reinterpret_cast<unsigned char*>(&w) + 8, &hi, 8);
+          vb[kk][d] = as_bf16x8(w);
+        }
       }
+    }
     __builtin_amdgcn_sched_barrier(0);
     // softmax.  Score i of the lane (i = 4 h + k) is key 16 h + 4 quad + k of
     // the step; k-slot 8 quad + e of P chunk kk holds score 8 kk + e.  The
     // running max m is kept in scaled base-2 units; since the scale is
     // positive, max(score) * scale is the max of the scaled scores, and each
-    // p is exp2(score * scale - m) with one rounding (an fma).  Each tile's
-    // P.V products are issued right after its softmax: the matrix unit runs
-    // them while the next tile's softmax (VALU) proceeds.
+    // p is exp2(score * scale - m) with one rounding (an fma).
+    u32x4_t pb[TPW][NK];
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
-      u32x4_t pb[NK];
       float sv[4 * NQ];   // raw scores, masked ones -inf
 #pragma unroll
       for (int i = 0; i < 4 * NQ; ++i) {
@@ -533,15 +579,17 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
         uint32_t h4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) h4[e] = cvt_pk_bf16(pv[8 * kk + 2 * e], pv[8 * kk + 2 * e + 1]);
-        pb[kk] = u32x4_t{h4[0], h4[1], h4[2], h4[3]};
+        pb[j][kk] = u32x4_t{h4[0], h4[1], h4[2], h4[3]};
       }
-      // O += P V: B operand = V^T[d][keys 32 kk + 4 quad .. +3 and 32 kk + 16 + 4 quad .. +3]
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk)
-#pragma unroll
-        for (int d = 0; d < DT; ++d)
-          acc[j][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pb[kk]), vb[kk][d], acc[j][d], 0, 0, 0);
     }
+    // O += P V: B operand = V^T[d][keys 32 kk + 4 quad .. +3 and 32 kk + 16 + 4 quad .. +3]
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+      for (int d = 0; d < DT; ++d)
+#pragma unroll
+        for (int j = 0; j < TPW; ++j)
+          acc[j][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pb[j][kk]), vb[kk][d], acc[j][d], 0, 0, 0);
   };
 
   constexpr int kStepsPerWin = kTblWin * kBS / STEP;
