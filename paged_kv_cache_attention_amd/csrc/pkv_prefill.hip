@@ -51,10 +51,12 @@ constexpr int kTblWin = 512;   // block-table entries cached in LDS at a time
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kSlack = 8.f;
-// K/V steps staged in LDS at once: loads run kStages - 1 steps ahead of the
-// tiles (straight into LDS, so deeper staging costs no registers).  Three
-// stages measured slower than two on the Llama-3-8B-shaped chunked batch
-// (235.3 against 222.6 us) and on one long prompt (123.0 against 117.7 us).
+// K/V steps staged in LDS at once: the loads of the next step are in flight
+// while the tiles work on this one.  Three stages measured no faster than two
+// on the Llama-3-8B-shaped chunked batch and on one long prompt (the staging
+// loads cost their issue and LDS writes, not their latency).  The step loop
+// runs two steps per iteration, so that each step's stage is a constant and
+// its LDS offsets fold into the read instructions.
 constexpr int kStages = 2;
 
 typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
@@ -89,26 +91,31 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
 // compiler (it cannot tell the staged step from the one being loaded by
 // global_load_lds), which waited for the next step's loads, just issued:
 // every step then ran with its prefetch drained.
+// ad[i] addresses stage 0; BUF picks the stage through the instructions'
+// offset field (a V stage is 8 KB at D = 128), so the addresses stay the same
+// from step to step.
 typedef uint32_t u32x2_v __attribute__((ext_vector_type(2)));
-template <int HI>
+template <int HI, int BUF>
 __device__ __forceinline__ void vt_reads4(u32x2_v (&lo)[4], u32x2_v (&hi)[4], const uint32_t (&ad)[4]) {
   static_assert(HI == 4096, "16 staged rows of 2 D bytes, D = 128");
-#define PKV_VT_READS4(OFF)                                                                                        \
+  static_assert(BUF == 0 || BUF == 1, "two stages");
+#define PKV_VT_READS4(OFF0, OFF1)                                                                                 \
   __asm__ volatile(                                                                                               \
-      "ds_read_b64_tr_b16 %0, %8\n\t"                                                                           \
-      "ds_read_b64_tr_b16 %4, %8 offset:" OFF "\n\t"                                                           \
-      "ds_read_b64_tr_b16 %1, %9\n\t"                                                                           \
-      "ds_read_b64_tr_b16 %5, %9 offset:" OFF "\n\t"                                                           \
-      "ds_read_b64_tr_b16 %2, %10\n\t"                                                                          \
-      "ds_read_b64_tr_b16 %6, %10 offset:" OFF "\n\t"                                                          \
-      "ds_read_b64_tr_b16 %3, %11\n\t"                                                                          \
-      "ds_read_b64_tr_b16 %7, %11 offset:" OFF "\n\t"                                                          \
+      "ds_read_b64_tr_b16 %0, %8 offset:" OFF0 "\n\t"                                                          \
+      "ds_read_b64_tr_b16 %4, %8 offset:" OFF1 "\n\t"                                                          \
+      "ds_read_b64_tr_b16 %1, %9 offset:" OFF0 "\n\t"                                                          \
+      "ds_read_b64_tr_b16 %5, %9 offset:" OFF1 "\n\t"                                                          \
+      "ds_read_b64_tr_b16 %2, %10 offset:" OFF0 "\n\t"                                                         \
+      "ds_read_b64_tr_b16 %6, %10 offset:" OFF1 "\n\t"                                                         \
+      "ds_read_b64_tr_b16 %3, %11 offset:" OFF0 "\n\t"                                                         \
+      "ds_read_b64_tr_b16 %7, %11 offset:" OFF1 "\n\t"                                                         \
       "s_waitcnt lgkmcnt(0)"                                                                                      \
       : "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3]), "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(hi[2]),       \
         "=&v"(hi[3])                                                                                              \
       : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])                                                            \
       : "memory")
-  PKV_VT_READS4("4096");
+  if constexpr (BUF == 0) PKV_VT_READS4("0", "4096");
+  else PKV_VT_READS4("8192", "12288");
 #undef PKV_VT_READS4
 }
 
@@ -347,7 +354,7 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
   const int t_last = (min(R, r0 + PG::ROWS) - 1) / G;
   const int kv_len = clampi(L - a.T + t_last + 1, 0, L);   // keys any row of the group sees
   const int nsteps = (kv_len + STEP - 1) / STEP;
-  const int nblk = (kv_len + kBS - 1) / kBS;
+  const int nblk = __builtin_amdgcn_readfirstlane((kv_len + kBS - 1) / kBS);
   // This workgroup's steps [s0, s1): the whole item, or piece `piece` of
   // npc = ceil(nsteps / piece_steps) near-equal pieces.  An item of npc > 1
   // pieces leaves normalised partials.
@@ -418,15 +425,20 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
   };
   // Per thread and staged chunk k: the block of the step it reads (relative
   // to the step's first block) and its byte offset inside a physical block;
-  // only the physical id changes from step to step.
+  // only the physical id changes from step to step.  The 64 lanes of a wave
+  // stage 64 / RC consecutive keys of one row-aligned run (4 keys at D = 128,
+  // 8 at D = 64), never across a block boundary, so the block is the same
+  // for the whole wave: its base address is formed in scalar registers and
+  // the lanes add only their 32-bit offset.
   constexpr int NB = STEP / kBS;                      // blocks per step
+  static_assert(kBS % (64 / RC) == 0 && (kThreads / RC) % kBS == 0, "a wave's staged keys stay in one block");
   int kblk[PER_T];
   uint32_t koff[PER_T], voff[PER_T];
 #pragma unroll
   for (int k = 0; k < PER_T; ++k) {
     const int i = tid + k * kThreads;
     const int key = i / RC, slot = i % RC;
-    kblk[k] = key / kBS;
+    kblk[k] = __builtin_amdgcn_readfirstlane(key / kBS);
     koff[k] = (uint32_t)((key % kBS) * kv_row_bytes + (slot ^ PG::swz_k(key)) * 16);
     voff[k] = (uint32_t)((key % kBS) * kv_row_bytes + (slot ^ PG::swz_v(key)) * 16);
   }
@@ -434,19 +446,24 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
     const int b0 = s * NB;
 #pragma unroll
     for (int k = 0; k < PER_T; ++k) {
-      const uint32_t ph = (uint32_t)stbl[(uint32_t)min(b0 + kblk[k], nblk - 1) % kTblWin];
+      const int te = __builtin_amdgcn_readfirstlane(min(b0 + kblk[k], nblk - 1)) % kTblWin;
+      const uint32_t ph = (uint32_t)__builtin_amdgcn_readfirstlane(stbl[te]);
+      uint64_t kb = (uint64_t)(uintptr_t)kpool + (uint64_t)ph * block_bytes;
+      uint64_t vb = (uint64_t)(uintptr_t)vpool + (uint64_t)ph * block_bytes;
+      uint32_t ko = koff[k], vo = voff[k];
+      // opaque to the optimiser, so that neither the pool base is folded into
+      // the lanes' offsets nor the offsets widened out of the loop: the loads
+      // then take the scalar-base + 32-bit-offset form
+      __asm__ volatile("" : "+s"(kb), "+s"(vb), "+v"(ko), "+v"(vo));
       const int run = (k * kThreads + 64 * wave) * 16;   // this wave's 1 KB run of the tile
-      load_lds16(kpool + (uint64_t)ph * block_bytes + koff[k], kst(buf) + run);
-      load_lds16(vpool + (uint64_t)ph * block_bytes + voff[k], vst(buf) + run);
+      load_lds16(reinterpret_cast<const unsigned char*>(kb) + ko, kst(buf) + run);
+      load_lds16(reinterpret_cast<const unsigned char*>(vb) + vo, vst(buf) + run);
     }
   };
   // After this the step's K and V are in LDS as far as this wave's loads go
-  // (the barrier that follows covers the other waves).  `later`: steps whose
-  // loads were issued after this one's (1 or 0 with three stages): their
-  // 2 * PER_T loads may stay in flight (vmcnt counts in issue order).
-  auto land = [&](int s, int buf, int later) {
-    if (later > 0) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * PER_T));   // vmcnt <= 2 PER_T; no exp/lgkm wait
-    else __builtin_amdgcn_s_waitcnt(0);
+  // (the barrier that follows covers the other waves).
+  auto land = [&](int s, int buf) {
+    __builtin_amdgcn_s_waitcnt(0);
     if ((s + 1) * STEP > kv_len) {   // the step holds keys past the group's last visible one:
 #pragma unroll                      // they may hold anything, so zero their V (each lane its own chunk)
       for (int k = 0; k < PER_T; ++k) {
@@ -458,10 +475,14 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
 
   // One step for this wave's tiles.  MASKED: some key of the step is at or
   // past the causal limit of one of the wave's rows.
-  auto compute = [&](int s, int buf, auto masked_tag) {
+  auto compute = [&](int s, auto buf_tag, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    const unsigned char* ks = kst(buf);
-    const unsigned char* vs = vst(buf);
+    constexpr int BUF = decltype(buf_tag)::value;
+    const unsigned char* ks = kst(BUF);
+    // at D = 128 the V^T reads address stage 0 and add the stage in their
+    // offset field
+    const unsigned char* vs = vst(D == 128 ? 0 : BUF);
+    static_assert(D != 128 || PG::VBYTES == 8192, "V stage size in vt_reads4's offsets");
     floatx4_t sacc[TPW][NQ];
 #pragma unroll
     for (int j = 0; j < TPW; ++j)
@@ -508,7 +529,7 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
             ad[i] = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)(
                 const_cast<unsigned char*>(vaddr(d0 + i)));
           u32x2_v lo[4], hi[4];
-          vt_reads4<16 * PG::ROWB>(lo, hi, ad);
+          vt_reads4<16 * PG::ROWB, BUF>(lo, hi, ad);
 #pragma unroll
           for (int i = 0; i < 4; ++i) vb[kk][d0 + i] = as_bf16x8(u32x4_t{lo[i].x, lo[i].y, hi[i].x, hi[i].y});
         }
@@ -594,38 +615,50 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
 
   constexpr int kStepsPerWin = kTblWin * kBS / STEP;
   if (s1 > s0) {
-    static_assert(kStages == 2 || kStages == 3, "two or three staged steps");
-    static_assert(2 * PER_T < 16, "pending loads fit vmcnt's low bits");
-    // Loads of step sa start kStages - 1 steps before it is computed.  A step
-    // that opens a new table window reloads it first (every load of earlier
-    // steps has its address by then).
-    auto start = [&](int sa) {
+    static_assert(kStages == 2, "two staged steps");
+    using Buf0 = std::integral_constant<int, 0>;
+    using Buf1 = std::integral_constant<int, 1>;
+    // Step s uses stage (s - s0) % 2.  Its loads start one step before it is
+    // computed; a step that opens a new table window reloads the window first
+    // (every load of earlier steps has its address by then).
+    auto start = [&](int sa, int buf) {
       if (sa > s0 && sa % kStepsPerWin == 0) {
         __syncthreads();
         load_window(sa / kStepsPerWin);
         __syncthreads();
       }
-      issue(sa, sa % kStages);
+      issue(sa, buf);
     };
     load_window(s0 / kStepsPerWin);
     __syncthreads();
-    for (int q = 0; q < kStages - 1 && s0 + q < s1; ++q) start(s0 + q);
-    land(s0, s0 % kStages, min(kStages - 2, s1 - 1 - s0));
+    start(s0, 0);
+    land(s0, 0);
     __syncthreads();
-    auto step = [&](int s, auto masked_tag) {
-      const int buf = s % kStages;
-      if (s + kStages - 1 < s1) start(s + kStages - 1);
-      if (wave_active) compute(s, buf, masked_tag);
-      if (s + 1 < s1) land(s + 1, (s + 1) % kStages, min(kStages - 2, s1 - 2 - s));
+    auto step = [&](int s, auto buf_tag, auto masked_tag) {
+      constexpr int BUF = decltype(buf_tag)::value;
+      if (s + 1 < s1) start(s + 1, 1 - BUF);
+      if (wave_active) compute(s, buf_tag, masked_tag);
+      if (s + 1 < s1) land(s + 1, 1 - BUF);
       __syncthreads();
     };
     // Steps before s_mask hold only keys every row of the wave sees; the
-    // rest are masked.  Two loops, one per kind, so each keeps its registers
-    // in place (the barrier count per step is the same for every wave).
+    // rest are masked.  One loop per kind, so each keeps its registers in
+    // place (the barrier count per step is the same for every wave); each
+    // runs two steps per iteration, stage 0 then stage 1, and each step
+    // variant is written once (so that it is inlined).  An odd unmasked step
+    // left over runs in the masked loop, whose code also serves steps that
+    // every row sees.
     const int s_mask = wave_active ? clampi(hi_min / STEP, s0, s1) : s1;
+    const int s_pairs = s0 + ((s_mask - s0) & ~1);
     int s = s0;
-    for (; s < s_mask; ++s) step(s, std::false_type{});
-    for (; s < s1; ++s) step(s, std::true_type{});
+    for (; s < s_pairs; s += 2) {
+      step(s, Buf0{}, std::false_type{});
+      step(s + 1, Buf1{}, std::false_type{});
+    }
+    for (; s < s1; s += 2) {
+      step(s, Buf0{}, std::true_type{});
+      if (s + 1 < s1) step(s + 1, Buf1{}, std::true_type{});
+    }
   }
 
   // ---- epilogue: O / l in bf16 (or, for a piece of a split item, in fp32
