@@ -12,9 +12,10 @@
 // Work item = (row group, sequence, KV head); rows are r = t * G + g
 // (G = Hq/Hkv).  A workgroup of kWaves waves owns one item; each wave holds
 // TPW 16-row MFMA tiles (two in the shipped configuration: 128 rows per item).
-// Keys advance STEP (32) at a time, loaded straight into LDS once per
-// workgroup (global_load_lds_dwordx4, double-buffered: the next step's loads
-// are in flight while the tiles work on the current one), with the item's
+// Keys are staged in LDS once per workgroup, a stage of 64 keys at D = 128
+// (32 at D = 64) per workgroup barrier, computed as 32-key steps
+// (global_load_lds_dwordx4, double-buffered: the next stage's loads are in
+// flight while the tiles work on the current one), with the item's
 // block-table entries cached in LDS 512 at a time:
 //   K[token][d]  row-major, chunks XOR-swizzled by row -> A operand of S^T = K Q^T
 //   V[token][d]  row-major, chunks XOR-swizzled by row, read back transposed
@@ -91,14 +92,15 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
 // compiler (it cannot tell the staged step from the one being loaded by
 // global_load_lds), which waited for the next step's loads, just issued:
 // every step then ran with its prefetch drained.
-// ad[i] addresses stage 0; BUF picks the stage through the instructions'
-// offset field (a V stage is 8 KB at D = 128), so the addresses stay the same
-// from step to step.
+// ad[i] addresses the V staging area's start; OFF (the stage and the
+// 32-key half within it, a multiple of 8 KB at D = 128) goes into the
+// instructions' offset field, so the addresses stay the same from step to
+// step.
 typedef uint32_t u32x2_v __attribute__((ext_vector_type(2)));
-template <int HI, int BUF>
+template <int HI, int OFF>
 __device__ __forceinline__ void vt_reads4(u32x2_v (&lo)[4], u32x2_v (&hi)[4], const uint32_t (&ad)[4]) {
   static_assert(HI == 4096, "16 staged rows of 2 D bytes, D = 128");
-  static_assert(BUF == 0 || BUF == 1, "two stages");
+  static_assert(OFF % 8192 == 0 && OFF + HI < 65536, "offset field");
 #define PKV_VT_READS4(OFF0, OFF1)                                                                                 \
   __asm__ volatile(                                                                                               \
       "ds_read_b64_tr_b16 %0, %8 offset:" OFF0 "\n\t"                                                          \
@@ -114,9 +116,12 @@ __device__ __forceinline__ void vt_reads4(u32x2_v (&lo)[4], u32x2_v (&hi)[4], co
         "=&v"(hi[3])                                                                                              \
       : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])                                                            \
       : "memory")
-  if constexpr (BUF == 0) PKV_VT_READS4("0", "4096");
-  else PKV_VT_READS4("8192", "12288");
+  if constexpr (OFF == 0) PKV_VT_READS4("0", "4096");
+  else if constexpr (OFF == 8192) PKV_VT_READS4("8192", "12288");
+  else if constexpr (OFF == 16384) PKV_VT_READS4("16384", "20480");
+  else PKV_VT_READS4("24576", "28672");
 #undef PKV_VT_READS4
+  static_assert(OFF <= 24576, "two stages of two halves");
 }
 
 // TPW 16-row tiles per wave, STEP keys per staged step.
@@ -127,14 +132,21 @@ struct PGeo {
   static constexpr int NK = STEP / 32;               // 32-key MFMA k-chunks per step (P.V)
   static constexpr int ROWB = 2 * D;                 // staged K or V row bytes (unpadded: loads land
                                                      // in LDS as whole 1 KB runs per wave)
-  static constexpr int KBYTES = STEP * ROWB;
-  static constexpr int VBYTES = STEP * ROWB;
+  // 32-key steps per staged stage (one barrier and one load wait per
+  // stage): two at D = 128 (chunked 8B batch 193.4 -> 183.8 us, one long
+  // prompt 107.8 -> 102.8, interleaved A/B, identical bits); one at D = 64,
+  // where the staging offsets of a second step spilled at the 128-VGPR
+  // budget of four waves per SIMD.
+  static constexpr int SUBS = D == 128 ? 2 : 1;
+  static constexpr int SKEYS = SUBS * STEP;          // keys per staged stage
+  static constexpr int KBYTES = SKEYS * ROWB;
+  static constexpr int VBYTES = SKEYS * ROWB;
   static constexpr int OROW = 2 * D + 16;            // epilogue row bytes (the 4 rows a quad writes sit 16
                                                      // banks apart)
   static constexpr int LDS = kStages * (KBYTES + VBYTES) > ROWS * OROW ? kStages * (KBYTES + VBYTES) : ROWS * OROW;
   static constexpr int RC = D * 2 / 16;              // 16-byte chunks per token row
-  static constexpr int PER_T = STEP * RC / kThreads;  // staged chunks per thread (K, and again V)
-  static_assert(PER_T * kThreads == STEP * RC, "even staging split");
+  static constexpr int PER_T = SKEYS * RC / kThreads;  // staged chunks per thread (K, and again V)
+  static_assert(PER_T * kThreads == SKEYS * RC, "even staging split");
   // Chunk c of staged row r sits in slot c ^ swz(r) of the row (an XOR
   // swizzle instead of padding).  K: the 16 rows a 16-lane group reads at one
   // chunk fall on 16 distinct 4-bank slots.  V: the 4 rows x 2 chunks of one
@@ -299,7 +311,7 @@ __device__ __forceinline__ void piece_of_rank(const int32_t* lens, int B, int T,
 }
 
 // Waves per SIMD the register budget is sized for (that many workgroups per
-// CU, 20 or 39 KB of LDS each at 32-key steps): four with one tile per wave,
+// CU, 20 KB of LDS each at D = 64, 66 KB at D = 128): four with one tile per wave,
 // or two tiles at D = 64; two otherwise.
 template <int D, int TPW, int STEP>
 constexpr int prefill_waves_per_eu() { return STEP == 32 && (TPW == 1 || D == 64) ? 4 : 2; }
@@ -312,7 +324,7 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
   constexpr int DT = D / 16;                          // output column tiles
   constexpr int NQ = PG::NQ, NK = PG::NK, RC = PG::RC, PER_T = PG::PER_T;
   __shared__ __attribute__((aligned(16))) unsigned char lds[PG::LDS];
-  __shared__ int stbl[kTblWin];   // physical ids of blocks [win * kTblWin, (win + 1) * kTblWin)
+  __shared__ int stbl[kTblWin];   // physical ids of blocks [win0, win0 + kTblWin)
   auto kst = [&](int buf) { return lds + buf * PG::KBYTES; };
   auto vst = [&](int buf) { return lds + kStages * PG::KBYTES + buf * PG::VBYTES; };
 
@@ -414,18 +426,21 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
   const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks;
   const unsigned char* kpool = static_cast<const unsigned char*>(a.k_pool) + (size_t)kv * D * 2;
   const unsigned char* vpool = static_cast<const unsigned char*>(a.v_pool) + (size_t)kv * D * 2;
-  // The table window holding step s: entries are loaded once per kTblWin
-  // blocks instead of once per step, so the K/V loads of a step depend on no
-  // global load of their own.
-  auto load_window = [&](int win) {
+  // The block-table window: kTblWin entries from block win0 on, loaded once
+  // per kTblWin blocks instead of once per stage, so the K/V loads of a stage
+  // depend on no global load of their own.  It slides to a stage's first
+  // block when the stage's last one is past it.
+  int win0 = 0;
+  auto load_window = [&](int first) {
+    win0 = first;
     for (int e = tid; e < kTblWin; e += kThreads) {
-      const int blk = min(win * kTblWin + e, nblk - 1);
+      const int blk = min(first + e, nblk - 1);
       stbl[e] = clampi(trow[blk], 0, nmax);
     }
   };
-  // Per thread and staged chunk k: the block of the step it reads (relative
-  // to the step's first block) and its byte offset inside a physical block;
-  // only the physical id changes from step to step.  The 64 lanes of a wave
+  // Per thread and staged chunk k: the block of the stage it reads (relative
+  // to the stage's first block) and its byte offset inside a physical block;
+  // only the physical id changes from stage to stage.  The 64 lanes of a wave
   // stage 64 / RC consecutive keys of one row-aligned run (4 keys at D = 128,
   // 8 at D = 64), never across a block boundary, so the block is the same
   // for the whole wave: its base address is formed in scalar registers and
@@ -446,7 +461,7 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
     const int b0 = s * NB;
 #pragma unroll
     for (int k = 0; k < PER_T; ++k) {
-      const int te = __builtin_amdgcn_readfirstlane(min(b0 + kblk[k], nblk - 1)) % kTblWin;
+      const int te = __builtin_amdgcn_readfirstlane(min(b0 + kblk[k], nblk - 1) - win0);
       const uint32_t ph = (uint32_t)__builtin_amdgcn_readfirstlane(stbl[te]);
       uint64_t kb = (uint64_t)(uintptr_t)kpool + (uint64_t)ph * block_bytes;
       uint64_t vb = (uint64_t)(uintptr_t)vpool + (uint64_t)ph * block_bytes;
@@ -460,12 +475,12 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
       load_lds16(reinterpret_cast<const unsigned char*>(vb) + vo, vst(buf) + run);
     }
   };
-  // After this the step's K and V are in LDS as far as this wave's loads go
-  // (the barrier that follows covers the other waves).
+  // After this the stage starting at step s has its K and V in LDS as far as
+  // this wave's loads go (the barrier that follows covers the other waves).
   auto land = [&](int s, int buf) {
     __builtin_amdgcn_s_waitcnt(0);
-    if ((s + 1) * STEP > kv_len) {   // the step holds keys past the group's last visible one:
-#pragma unroll                      // they may hold anything, so zero their V (each lane its own chunk)
+    if (s * STEP + PG::SKEYS > kv_len) {   // the stage holds keys past the group's last visible one:
+#pragma unroll                            // they may hold anything, so zero their V (each lane its own chunk)
       for (int k = 0; k < PER_T; ++k) {
         const int i = tid + k * kThreads;
         if (s * STEP + i / RC >= kv_len) store16(vst(buf) + i * 16, u32x4_t{0u, 0u, 0u, 0u});
@@ -473,16 +488,19 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
     }
   };
 
-  // One step for this wave's tiles.  MASKED: some key of the step is at or
-  // past the causal limit of one of the wave's rows.
-  auto compute = [&](int s, auto buf_tag, auto masked_tag) {
+  // One 32-key step for this wave's tiles: half HALF of the stage in buffer
+  // BUF.  MASKED: some key of the step is at or past the causal limit of one
+  // of the wave's rows.
+  auto compute = [&](int s, auto buf_tag, auto half_tag, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    constexpr int BUF = decltype(buf_tag)::value;
+    constexpr int BUF = decltype(buf_tag)::value, HALF = decltype(half_tag)::value;
+    constexpr int R0 = HALF * STEP;   // the step's first row in the stage
     const unsigned char* ks = kst(BUF);
-    // at D = 128 the V^T reads address stage 0 and add the stage in their
-    // offset field
-    const unsigned char* vs = vst(D == 128 ? 0 : BUF);
-    static_assert(D != 128 || PG::VBYTES == 8192, "V stage size in vt_reads4's offsets");
+    // at D = 128 the V^T reads address the V area's start and add the stage
+    // and half in their offset field
+    const unsigned char* vs = D == 128 ? vst(0) : vst(BUF) + R0 * PG::ROWB;
+    constexpr int kVtOff = BUF * PG::VBYTES + R0 * PG::ROWB;
+    static_assert(D != 128 || PG::VBYTES == 16384, "V stage size in vt_reads4's offsets");
     floatx4_t sacc[TPW][NQ];
 #pragma unroll
     for (int j = 0; j < TPW; ++j)
@@ -495,8 +513,8 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
     for (int h = 0; h < NQ; ++h)
 #pragma unroll
       for (int c = 0; c < KS; ++c)
-        kc[h][c] = *reinterpret_cast<const u32x4_t*>(ks + (16 * h + row) * PG::ROWB +
-                                                     ((quad + 4 * c) ^ PG::swz_k(16 * h + row)) * 16);
+        kc[h][c] = *reinterpret_cast<const u32x4_t*>(ks + (R0 + 16 * h + row) * PG::ROWB +
+                                                     ((quad + 4 * c) ^ PG::swz_k(R0 + 16 * h + row)) * 16);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < KS; ++c)
@@ -516,9 +534,9 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
     bf16x8_v vb[NK][DT];
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      const int vrow = 32 * kk + 4 * quad + (row >> 2);
+      const int vrow = 32 * kk + 4 * quad + (row >> 2);   // row in the step; R0 + vrow in the stage
       auto vaddr = [&](int d) {
-        return vs + vrow * PG::ROWB + (((2 * d + ((row & 3) >> 1)) ^ PG::swz_v(vrow)) * 16) + 8 * (row & 1);
+        return vs + vrow * PG::ROWB + (((2 * d + ((row & 3) >> 1)) ^ PG::swz_v(R0 + vrow)) * 16) + 8 * (row & 1);
       };
       if constexpr (D == 128) {
 #pragma unroll
@@ -529,7 +547,7 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
             ad[i] = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)(
                 const_cast<unsigned char*>(vaddr(d0 + i)));
           u32x2_v lo[4], hi[4];
-          vt_reads4<16 * PG::ROWB, BUF>(lo, hi, ad);
+          vt_reads4<16 * PG::ROWB, kVtOff>(lo, hi, ad);
 #pragma unroll
           for (int i = 0; i < 4; ++i) vb[kk][d0 + i] = as_bf16x8(u32x4_t{lo[i].x, lo[i].y, hi[i].x, hi[i].y});
         }
@@ -613,51 +631,59 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
           acc[j][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pb[j][kk]), vb[kk][d], acc[j][d], 0, 0, 0);
   };
 
-  constexpr int kStepsPerWin = kTblWin * kBS / STEP;
   if (s1 > s0) {
-    static_assert(kStages == 2, "two staged steps");
+    static_assert(kStages == 2, "two stages");
+    constexpr int SUBS = PG::SUBS;
     using Buf0 = std::integral_constant<int, 0>;
     using Buf1 = std::integral_constant<int, 1>;
-    // Step s uses stage (s - s0) % 2.  Its loads start one step before it is
-    // computed; a step that opens a new table window reloads the window first
-    // (every load of earlier steps has its address by then).
+    using Half0 = std::integral_constant<int, 0>;
+    using Half1 = std::integral_constant<int, 1>;
+    // Stages of SUBS steps from s0 on, alternating the two buffers.  A
+    // stage's loads start one stage before it is computed; if its last block
+    // is past the table window, the window slides to its first block first
+    // (every load of earlier stages has its address by then).
     auto start = [&](int sa, int buf) {
-      if (sa > s0 && sa % kStepsPerWin == 0) {
+      if ((sa + SUBS) * NB - 1 >= win0 + kTblWin) {
         __syncthreads();
-        load_window(sa / kStepsPerWin);
+        load_window(sa * NB);
         __syncthreads();
       }
       issue(sa, buf);
     };
-    load_window(s0 / kStepsPerWin);
+    load_window(s0 * NB);
     __syncthreads();
     start(s0, 0);
     land(s0, 0);
     __syncthreads();
-    auto step = [&](int s, auto buf_tag, auto masked_tag) {
+    // One stage: step s and (SUBS = 2, when `two`) step s + 1.
+    auto stage = [&](int s, auto buf_tag, auto masked_tag, bool two) {
       constexpr int BUF = decltype(buf_tag)::value;
-      if (s + 1 < s1) start(s + 1, 1 - BUF);
-      if (wave_active) compute(s, buf_tag, masked_tag);
-      if (s + 1 < s1) land(s + 1, 1 - BUF);
+      if (s + SUBS < s1) start(s + SUBS, 1 - BUF);
+      if (wave_active) {
+        compute(s, buf_tag, Half0{}, masked_tag);
+        if constexpr (SUBS == 2)
+          if (two) compute(s + 1, buf_tag, Half1{}, masked_tag);
+      }
+      if (s + SUBS < s1) land(s + SUBS, 1 - BUF);
       __syncthreads();
     };
     // Steps before s_mask hold only keys every row of the wave sees; the
     // rest are masked.  One loop per kind, so each keeps its registers in
-    // place (the barrier count per step is the same for every wave); each
-    // runs two steps per iteration, stage 0 then stage 1, and each step
-    // variant is written once (so that it is inlined).  An odd unmasked step
-    // left over runs in the masked loop, whose code also serves steps that
-    // every row sees.
+    // place (the barrier count per stage is the same for every wave); each
+    // runs two stages per iteration, buffer 0 then buffer 1, and each step
+    // variant is written once (so that it is inlined).  Unmasked steps left
+    // over from whole iterations run in the masked loop, whose code also
+    // serves steps that every row sees.
     const int s_mask = wave_active ? clampi(hi_min / STEP, s0, s1) : s1;
-    const int s_pairs = s0 + ((s_mask - s0) & ~1);
+    const int s_whole = s0 + ((s_mask - s0) / (2 * SUBS)) * (2 * SUBS);
     int s = s0;
-    for (; s < s_pairs; s += 2) {
-      step(s, Buf0{}, std::false_type{});
-      step(s + 1, Buf1{}, std::false_type{});
+    for (; s < s_whole; s += 2 * SUBS) {
+      stage(s, Buf0{}, std::false_type{}, true);
+      stage(s + SUBS, Buf1{}, std::false_type{}, true);
     }
-    for (; s < s1; s += 2) {
-      step(s, Buf0{}, std::true_type{});
-      if (s + 1 < s1) step(s + 1, Buf1{}, std::true_type{});
+    for (; s < s1; s += 2 * SUBS) {
+      stage(s, Buf0{}, std::true_type{}, s + 1 < s1);
+      if (s + SUBS < s1) stage(s + SUBS, Buf1{}, std::true_type{}, s + SUBS + 1 < s1);
     }
   }
 
