@@ -588,7 +588,10 @@ void prefill_kernel(PrefillArgs pa, float scale_log2e) {
       float mx = sv[0];
 #pragma unroll
       for (int i = 1; i < 4 * NQ; ++i) mx = fmaxf(mx, sv[i]);
-      if (__builtin_amdgcn_ballot_w64(mx * scale_log2e > m_thr[j])) {
+      // rare (the running max rises by more than the slack): marked
+      // unlikely, the rescale is laid out after the loop (chunked 8B batch
+      // 187.2 -> 181.5 us, interleaved A/B, identical bits)
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(mx * scale_log2e > m_thr[j]) != 0, 0)) {
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(m_row[j], mx * scale_log2e);
