@@ -179,23 +179,13 @@ def cpu_baseline(w, budget_s, repeats=3):
                       f"median of {repeats} passes"}
 
 
-def hipcc_version():
-    """hipcc's version line (a child process; taken before the GPU is touched)."""
-    import subprocess
-    try:
-        out = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True, timeout=60).stdout
-        return next((l.strip() for l in out.splitlines() if "version" in l.lower()), None)
-    except (OSError, subprocess.SubprocessError):
-        return None
-
-
-def provenance(torch, w, hipcc):
+def provenance(torch, w):
     """What produced the numbers: device, ROCm and hipcc versions, commit, seed, host CPU."""
     from paged_kv_cache_attention_amd import build as pkv_build
     props = torch.cuda.get_device_properties(0)
     info = {"gpu": torch.cuda.get_device_name(0), "gpu_arch": getattr(props, "gcnArchName", None),
             "gpu_cus": props.multi_processor_count, "torch": torch.__version__, "torch_hip": torch.version.hip,
-            "hipcc": hipcc, "seed": workload.WORKLOAD_SEEDS.get(w.name), "host_cpu": cpu_model(),
+            "hipcc": None, "seed": workload.WORKLOAD_SEEDS.get(w.name), "host_cpu": cpu_model(),
             "host_cores": host_cores()}
     try:
         info["rocm"] = open("/opt/rocm/.info/version").read().strip()
@@ -203,10 +193,11 @@ def provenance(torch, w, hipcc):
         info["rocm"] = None
     info["sources_sha256"] = pkv_build.sources_sha256()
     info["commit"] = None
-    try:   # the commit the library was built from, recorded by the build while the sources still match
+    try:   # the commit and hipcc the library was built with, recorded by the build while the sources still match
         bi = json.loads(pkv_build.BUILD_INFO.read_text())
         if bi.get("sources_sha256") == info["sources_sha256"]:
             info["commit"] = bi.get("commit")
+            info["hipcc"] = bi.get("hipcc")
     except (OSError, ValueError):
         pass
     return info
@@ -345,7 +336,6 @@ def main():
         print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
-    hipcc = hipcc_version()
     import torch
     import paged_kv_cache_attention_amd as pkv
 
@@ -503,7 +493,7 @@ def main():
     # decode kernels' access pattern, no arithmetic) and a plain device copy
     result["read_ceiling"] = read_ceiling(torch, dev)
     result["copy_ceiling"] = copy_ceiling(torch, dev)
-    result["provenance"] = provenance(torch, w, hipcc)
+    result["provenance"] = provenance(torch, w)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)

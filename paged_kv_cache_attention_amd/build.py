@@ -74,7 +74,13 @@ def _write_build_info():
             commit = head.stdout.strip() + ("-dirty" if dirty else "")
     except OSError:
         pass
-    BUILD_INFO.write_text(json.dumps({"commit": commit, "sources_sha256": sources_sha256()}) + "\n")
+    version = None
+    try:
+        out = subprocess.run([hipcc(), "--version"], capture_output=True, text=True, timeout=60).stdout
+        version = next((l.strip() for l in out.splitlines() if "version" in l.lower()), None)
+    except (OSError, subprocess.SubprocessError):
+        pass
+    BUILD_INFO.write_text(json.dumps({"commit": commit, "sources_sha256": sources_sha256(), "hipcc": version}) + "\n")
 
 
 def _compile(cmd, verbose):

@@ -49,10 +49,16 @@ constexpr int run_tile_bytes() { return kBS * 2 * D; }
 
 // The V tile: 16 unpadded token rows of 2 D bytes, 16-byte chunk c
 // of row r in slot c ^ vswz(r), so that the 4 rows x 2 chunks of one
-// transposing read of a 16-lane group sit on 8 distinct 4-bank slots (at
-// D = 64 a row covers half the banks and its parity picks the half).
+// transposing read of a 16-lane group sit on 8 distinct 4-bank slots, and at
+// D = 128 (a row is exactly the 64 banks) the neighbouring group, 4 rows
+// further, on the other half of the banks (8B decode batch: 3.04 M LDS bank
+// conflict cycles per call without that bit, 0.01 M with it; the call time
+// is set by memory and did not move).  At D = 64 a row covers half the banks
+// and its parity picks the half.
 template <int D>
-__device__ __forceinline__ int vswz(int r) { return D == 128 ? 2 * (r & 3) : 2 * ((r >> 1) & 1); }
+__device__ __forceinline__ int vswz(int r) {
+  return D == 128 ? (2 * (r & 3)) | (8 * ((r >> 2) & 1)) : 2 * ((r >> 1) & 1);
+}
 
 // All D/16 V operands of one block (column tiles d = 0 .. D/16 - 1), read
 // back to back in one asm block that also waits for them (lgkmcnt(0)) before
