@@ -329,6 +329,9 @@ def main():
                     help="append workloads: fused RoPE append (paged_kv_append_rope, queries rotated too)")
     ap.add_argument("--serve", action="store_true",
                     help="measure the host runtime (engine) and a 16-request serving run instead of one batch")
+    ap.add_argument("--piece-tokens", type=int, default=None,
+                    help="prefill workloads: piece_tokens for the call (0: no key pieces; default: the library's "
+                         "suggestion for the shape)")
     ap.add_argument("--cold-reps", type=int, default=20,
                     help="extra untimed-region reps, each after a 1 GiB cache flush, for the cold-cache figure")
     args = ap.parse_args()
@@ -374,7 +377,8 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     prefill = w.T > 16   # a chunked-prefill workload: paged_attention_prefill
     if prefill:   # the library's key-piece choice for this shape, workspace allocated up front
-        pieces = pkv.pkv_prefill_piece_tokens(w.B, w.T, w.Hq, w.Hkv, w.D, w.block_size, w.max_blocks)
+        pieces = (pkv.pkv_prefill_piece_tokens(w.B, w.T, w.Hq, w.Hkv, w.D, w.block_size, w.max_blocks)
+                  if args.piece_tokens is None else args.piece_tokens)
         pneed = pkv.pkv_prefill_workspace_bytes(w.B, w.T, w.Hq, w.Hkv, w.D, w.block_size, w.max_blocks, pieces)
         pws = torch.empty(max(pneed, 16), dtype=torch.uint8, device=dev)
 
