@@ -256,8 +256,9 @@ pkv_status paged_attention_decode_noalloc(const void* q, const void* k_pool, con
  * Supported: bf16 only (PKV_EUNSUPPORTED for fp32), D in {64, 128},
  * Hq / Hkv in {1, 2, 4, 8}, 1 <= T <= 8192, block_size 16.  The device-side
  * contract T <= L <= max_blocks * block_size is the decode one (checked under
- * PKV_DEBUG=1).  Work is split into items of 128 query rows of one KV head;
- * K and V of the item's visible keys are read once per item.
+ * PKV_DEBUG=1).  Work is split into items of 128 query rows of one KV head
+ * (256 at D = 128 when keys are split into pieces); K and V of the item's
+ * visible keys are read once per item.
  *
  * piece_tokens = 0: every item is finished by the workgroup that owns it; the
  * workspace is not used (may be NULL).  piece_tokens > 0 (a multiple of 32)

@@ -40,6 +40,7 @@ hipError_t launch_decode_stream(const DecodeArgs& a, void* workspace, hipStream_
 constexpr int kPrefillMaxT = 8192;
 constexpr int kPrefillTPW = 2;                  // 16-row MFMA tiles per wave
 constexpr int kPrefillRows = 16 * kPrefillTPW * 4;   // query rows per work item (4 waves)
+constexpr int kPrefillRowsWide = 16 * kPrefillTPW * 8;   // with key pieces at D = 128 (8 waves)
 constexpr int kPrefillStep = 32;                // keys per staged step; pieces are multiples of it
 constexpr int kPrefillMinPiece = 512;           // smallest piece the policy picks
 // Key pieces per item for piece_tokens (1: no split).

@@ -10,8 +10,9 @@
 // T * Hq/Hkv query rows against the same keys.
 //
 // Work item = (row group, sequence, KV head); rows are r = t * G + g
-// (G = Hq/Hkv).  A workgroup of kWaves waves owns one item; each wave holds
-// TPW 16-row MFMA tiles (two in the shipped configuration: 128 rows per item).
+// (G = Hq/Hkv).  A workgroup of WAVES waves owns one item; each wave holds
+// TPW 16-row MFMA tiles (two in the shipped configuration: 128 rows per item
+// with 4 waves, 256 with the 8 waves of a key-piece launch at D = 128).
 // Keys are staged in LDS once per workgroup, a stage of 64 keys at D = 128
 // (32 at D = 64) per workgroup barrier, computed as 32-key steps
 // (global_load_lds_dwordx4, double-buffered: the next stage's loads are in
@@ -49,8 +50,6 @@ namespace {
 
 constexpr int kBS = 16;
 constexpr int kTblWin = 512;   // block-table entries cached in LDS at a time
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr float kSlack = 8.f;
 // K/V steps staged in LDS at once: the loads of the next step are in flight
 // while the tiles work on this one.  Three stages measured no faster than two
@@ -124,10 +123,12 @@ __device__ __forceinline__ void vt_reads4(u32x2_v (&lo)[4], u32x2_v (&hi)[4], co
   static_assert(OFF <= 24576, "two stages of two halves");
 }
 
-// TPW 16-row tiles per wave, STEP keys per staged step.
-template <int D, int TPW, int STEP>
+// TPW 16-row tiles per wave, STEP keys per staged step, WAVES waves per
+// workgroup (one item).
+template <int D, int TPW, int STEP, int WAVES = 4>
 struct PGeo {
-  static constexpr int ROWS = 16 * TPW * kWaves;     // query rows per item
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int ROWS = 16 * TPW * WAVES;      // query rows per item
   static constexpr int NQ = STEP / 16;               // 16-key quarters per step (S^T tiles)
   static constexpr int NK = STEP / 32;               // 32-key MFMA k-chunks per step (P.V)
   static constexpr int ROWB = 2 * D;                 // staged K or V row bytes (unpadded: loads land
@@ -145,8 +146,8 @@ struct PGeo {
                                                      // banks apart)
   static constexpr int LDS = kStages * (KBYTES + VBYTES) > ROWS * OROW ? kStages * (KBYTES + VBYTES) : ROWS * OROW;
   static constexpr int RC = D * 2 / 16;              // 16-byte chunks per token row
-  static constexpr int PER_T = SKEYS * RC / kThreads;  // staged chunks per thread (K, and again V)
-  static_assert(PER_T * kThreads == SKEYS * RC, "even staging split");
+  static constexpr int PER_T = SKEYS * RC / THREADS;  // staged chunks per thread (K, and again V)
+  static_assert(PER_T * THREADS == SKEYS * RC, "even staging split");
   // Chunk c of staged row r sits in slot c ^ swz(r) of the row (an XOR
   // swizzle instead of padding).  K: the 16 rows a 16-lane group reads at one
   // chunk fall on 16 distinct 4-bank slots.  V: the 4 rows x 2 chunks of one
@@ -163,7 +164,8 @@ struct PGeo {
 };
 
 static_assert(PGeo<64, kPrefillTPW, kPrefillStep>::ROWS == kPrefillRows &&
-                  PGeo<128, kPrefillTPW, kPrefillStep>::ROWS == kPrefillRows,
+                  PGeo<128, kPrefillTPW, kPrefillStep>::ROWS == kPrefillRows &&
+                  PGeo<128, kPrefillTPW, kPrefillStep, 8>::ROWS == kPrefillRowsWide,
               "work item rows shared with the host-side sizing");
 
 struct PrefillArgs {
@@ -322,10 +324,11 @@ __device__ __forceinline__ void piece_of_rank(const int32_t* lens, int B, int T,
 template <int D, int TPW, int STEP>
 constexpr int prefill_waves_per_eu() { return STEP == 32 && (TPW == 1 || D == 64) ? 4 : 2; }
 
-template <int D, int TPW, int STEP>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(prefill_waves_per_eu<D, TPW, STEP>())))
+template <int D, int TPW, int STEP, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(prefill_waves_per_eu<D, TPW, STEP>())))
 void prefill_kernel(PrefillArgs pa, float scale_log2e) {
-  using PG = PGeo<D, TPW, STEP>;
+  using PG = PGeo<D, TPW, STEP, WAVES>;
+  constexpr int kThreads = PG::THREADS;
   constexpr int KS = D / 32;                          // k-steps of QK^T
   constexpr int DT = D / 16;                          // output column tiles
   constexpr int NQ = PG::NQ, NK = PG::NK, RC = PG::RC, PER_T = PG::PER_T;
@@ -810,9 +813,9 @@ __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArg
   if (c == 0 && a.lse_out) a.lse_out[orow] = wsum != 0.f ? M + logf(wsum) : kNegInf;
 }
 
-template <int D, int TPW, int STEP>
+template <int D, int TPW, int STEP, int WAVES>
 hipError_t launch_pf(const PrefillArgs& pa0, int piece_tokens, hipStream_t stream) {
-  using PG = PGeo<D, TPW, STEP>;
+  using PG = PGeo<D, TPW, STEP, WAVES>;
   PrefillArgs pa = pa0;
   const int G = pa.a.Hq / pa.a.Hkv;
   pa.groups = (pa.a.T * G + PG::ROWS - 1) / PG::ROWS;
@@ -821,8 +824,8 @@ hipError_t launch_pf(const PrefillArgs& pa0, int piece_tokens, hipStream_t strea
   pa.pieces = prefill_pieces(pa.a.max_blocks, piece_tokens);
   pa.piece_steps = pa.pieces > 1 ? piece_tokens / STEP : 0;
   if (items * pa.pieces > 0x7fffffff || items * PG::ROWS > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<D, TPW, STEP>), dim3((unsigned)(items * pa.pieces)), dim3(kThreads), 0, stream,
-                     pa, pa.a.scale * kLog2e);
+  hipLaunchKernelGGL((prefill_kernel<D, TPW, STEP, WAVES>), dim3((unsigned)(items * pa.pieces)), dim3(PG::THREADS), 0,
+                     stream, pa, pa.a.scale * kLog2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pa.pieces <= 1) return e;
   constexpr int kChunks = PG::ROWS / (kMergeThreads / (D / 4));
@@ -836,9 +839,18 @@ hipError_t launch_pf(const PrefillArgs& pa0, int piece_tokens, hipStream_t strea
 // V read from LDS, which outweighs the occupancy given up at D = 128 (two
 // workgroups per CU instead of four with one tile: 312 against 346 us);
 // 64-key steps and 8-wave workgroups of one tile per wave were slower.
+// Items of 4 waves (128 rows) normally; with key pieces at D = 128, items of
+// 8 waves (256 rows), which stage each key once for twice the rows: one long
+// prompt chunk 100.2 -> 95.6 us per call (interleaved A/B), where the pieces
+// already give every CU work, while the unsplit 8-sequence chunked batch
+// schedules its coarser items worse (187.7 -> 194.5 us).  At D = 64 a
+// second step per stage, which 8-wave staging needs, spills.
 template <int D>
 hipError_t launch_pf_d(const PrefillArgs& pa, int piece_tokens, hipStream_t stream) {
-  return launch_pf<D, kPrefillTPW, kPrefillStep>(pa, piece_tokens, stream);
+  if constexpr (D == 128)
+    if (prefill_pieces(pa.a.max_blocks, piece_tokens) > 1)
+      return launch_pf<D, kPrefillTPW, kPrefillStep, 8>(pa, piece_tokens, stream);
+  return launch_pf<D, kPrefillTPW, kPrefillStep, 4>(pa, piece_tokens, stream);
 }
 
 }  // namespace
@@ -852,8 +864,9 @@ int prefill_pieces(int max_blocks, int piece_tokens) {
 size_t prefill_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int max_blocks, int piece_tokens) {
   const int pieces = prefill_pieces(max_blocks, piece_tokens);
   if (pieces <= 1 || B <= 0 || T <= 0 || Hkv <= 0) return 0;
-  const long long groups = ((long long)T * (Hq / Hkv) + kPrefillRows - 1) / kPrefillRows;
-  return (size_t)B * groups * Hkv * pieces * kPrefillRows * (D + 1) * sizeof(float);
+  const int rows = D == 128 ? kPrefillRowsWide : kPrefillRows;   // items of the split launch (launch_pf_d)
+  const long long groups = ((long long)T * (Hq / Hkv) + rows - 1) / rows;
+  return (size_t)B * groups * Hkv * pieces * rows * (D + 1) * sizeof(float);
 }
 
 int prefill_piece_tokens(int B, int T, int Hq, int Hkv, int D, int max_blocks, int cus) {

@@ -191,6 +191,7 @@ PIECE_CASES = [  # (D, Hq, Hkv, T, lens, piece_tokens)
     (128, 16, 8, 37, [37, 38, 500], 160),               # some items in one piece, written directly
     (64, 32, 4, 17, [17, 40, 1000], 32),                # G = 8
     (128, 32, 8, 1, [1, 30, 300], 64),                  # T = 1: one row group, decode rows in pieces
+    (128, 8, 8, 300, [300, 301, 700], 64),              # MHA: 300 rows, a full 256-row item and a partial one
     # grids of several waves of workgroups, pieces of mixed-length items ranked
     # ahead of the unsplit items: 40 and 70 sequences (the latter past 64, the
     # lengths in more than one register per lane)
@@ -202,9 +203,10 @@ PIECE_CASES = [  # (D, Hq, Hkv, T, lens, piece_tokens)
 @pytest.mark.parametrize("D,Hq,Hkv,T,lens,piece_tokens", PIECE_CASES)
 def test_prefill_key_pieces(D, Hq, Hkv, T, lens, piece_tokens):
     """Items split into key pieces of piece_tokens tokens, one workgroup each,
-    merged by log-sum-exp: the oracle's result (and the unsplit call's, each
-    within the P-rounding bound of the oracle), the unsplit call's LSE, and
-    the same bits on a second call."""
+    merged by log-sum-exp (at D = 128 the split launch runs 256-row items of
+    8 waves): the oracle's result (and the unsplit call's, each within the
+    P-rounding bound of the oracle), the unsplit call's LSE, and the same
+    bits on a second call."""
     w = workload.uniform_batch("pieces", seed=151 + T, B=len(lens), T=T, Hq=Hq, Hkv=Hkv, D=D, dtype="bf16",
                                lens=lens)
     say("prefill pieces", D, Hq, Hkv, T, lens, piece_tokens)
