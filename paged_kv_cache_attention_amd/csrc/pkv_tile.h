@@ -148,6 +148,14 @@ __device__ __forceinline__ void load_q(u32x4_t (&qreg)[D / 32], const uint16_t* 
 // the 8B shared-prefix decode batch, 431.6 against 441.3 us on the
 // long-context verify batch.
 //
+// stream_v: V of a block is loaded with the non-temporal hint unless one of
+// the neighbouring sequences in the batch (tables tprev, tnext: their rows at
+// the same logical block, or nullptr) lists the same physical block.  K
+// keeps the default policy.  Measured (interleaved A/B, us per call): 8B
+// shared-prefix batch 215.8 -> 211.3, long-context verify 431.1 -> 386.0, a
+// D = 64 batch of 64 sequences of 4000-8000 tokens 153.0 -> 136.5; the
+// hint on every block instead cost the 8B batch its cached prefix re-reads
+// (216.9 -> 248.6), and on K as well as V it was slower there (224.4).
 // With pblocks > 0 the walk also cuts at every multiple of pblocks logical
 // blocks: after the block that ends such a partition (if more blocks of the
 // walk follow) it calls flush(st, kb_end), kb_end being the logical block the
@@ -164,7 +172,8 @@ __device__ __forceinline__ void run(State<D>& st, const u32x4_t (&qreg)[D / 32],
                                          const int32_t* trow, int kb0, int nb, int nmax, const unsigned char* kpool,
                                          const unsigned char* vhead, size_t kv_row_bytes, size_t block_bytes,
                                          unsigned char* vtile, float scale_log2e, int lane, int pblocks = 0,
-                                         Flush flush = Flush()) {
+                                         Flush flush = Flush(), bool stream_v = false,
+                                         const int32_t* tprev = nullptr, const int32_t* tnext = nullptr) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   const int row = lane & 15, quad = lane >> 4;
@@ -182,20 +191,33 @@ __device__ __forceinline__ void run(State<D>& st, const u32x4_t (&qreg)[D / 32],
     vr[c] = pos / (2 * D);
     voff[c] = (uint32_t)(vr[c] * kv_row_bytes + (((pos % (2 * D)) / 16) ^ vswz<D>(vr[c])) * 16);
   }
-  auto load_kv = [&](u32x4_t (&kd)[KS], u32x4_t (&vd)[KS], int ph) {
+  uint64_t keep = 0;   // blocks of the table chunk whose V keeps the default cache policy
+  // the loads of entry i of the table chunk (the last one past its end)
+  auto load_kv = [&](u32x4_t (&kd)[KS], u32x4_t (&vd)[KS], int i) {
+    const int e = i < cn ? i : cn - 1;
+    const int ph = __builtin_amdgcn_readlane(tbl, e);
     const unsigned char* kb = kpool + (size_t)ph * block_bytes;
     const unsigned char* vb = vhead + (size_t)ph * block_bytes;
     __builtin_amdgcn_sched_barrier(0);
+    if ((keep >> e) & 1) {
 #pragma unroll
-    for (int c = 0; c < KS; ++c) kd[c] = load16(kb + c * 64);
+      for (int c = 0; c < KS; ++c) kd[c] = load16(kb + c * 64);
 #pragma unroll
-    for (int c = 0; c < KS; ++c) vd[c] = load16(vb + voff[c]);
+      for (int c = 0; c < KS; ++c) vd[c] = load16(vb + voff[c]);
+    } else {
+      // the empty asm keeps the two arms apart: merged, the loads lost the
+      // non-temporal hint
+      __asm__ volatile("" ::: "memory");
+#pragma unroll
+      for (int c = 0; c < KS; ++c) kd[c] = load16(kb + c * 64);
+#pragma unroll
+      for (int c = 0; c < KS; ++c) vd[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vb + voff[c]));
+      __asm__ volatile("" ::: "memory");
+    }
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto phys = [&](int i) { return __builtin_amdgcn_readlane(tbl, i < cn ? i : cn - 1); };
 
   auto body = [&](u32x4_t (&kcur)[KS], u32x4_t (&vcur)[KS], int kb, int i) {
-    const int ph_ahead = phys(i + PD);
     floatx4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < KS; ++c) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kcur[c]), as_bf16x8(qreg[c]), s, 0, 0, 0);
@@ -208,7 +230,7 @@ __device__ __forceinline__ void run(State<D>& st, const u32x4_t (&qreg)[D / 32],
       const bool dead = kb * kBS + vr[c] >= vlimit;
       store16(vtile + 1024 * c + 16 * lane, dead ? u32x4_t{0u, 0u, 0u, 0u} : vcur[c]);
     }
-    load_kv(kcur, vcur, ph_ahead);
+    load_kv(kcur, vcur, i + PD);
     const int tok0 = kb * kBS + 4 * quad;
     float sv[4];
     bool need = false;
@@ -259,9 +281,14 @@ __device__ __forceinline__ void run(State<D>& st, const u32x4_t (&qreg)[D / 32],
 
   for (int c0 = 0; c0 < nb; c0 += 64) {
     cn = min(64, nb - c0);
-    tbl = lane < cn ? clampi(trow[c0 + lane], 0, nmax) : 0;
+    const int raw = lane < cn ? trow[c0 + lane] : -1;
+    tbl = lane < cn ? clampi(raw, 0, nmax) : 0;
+    bool kp = !stream_v;
+    if (tprev) kp |= lane < cn && tprev[c0 + lane] == raw;
+    if (tnext) kp |= lane < cn && tnext[c0 + lane] == raw;
+    keep = __builtin_amdgcn_ballot_w64(kp);
 #pragma unroll
-    for (int s = 0; s < PD; ++s) load_kv(kbuf[s], vbuf[s], phys(s));
+    for (int s = 0; s < PD; ++s) load_kv(kbuf[s], vbuf[s], s);
     for (int i = 0; i < cn; i += PD) {
 #pragma unroll
       for (int s = 0; s < PD; ++s) body(kbuf[s], vbuf[s], kb0 + c0 + i + s, i + s);

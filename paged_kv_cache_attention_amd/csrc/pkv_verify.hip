@@ -62,6 +62,11 @@ static_assert(2 * tile::run_tile_bytes<64>() == 16 * 64 * 4 && 2 * tile::run_til
 constexpr int kInlinePerWave = 512;            // LDS prefix entries per wave
 constexpr int kInlinePT = kInlinePerWave / 64;  // sequences per thread
 constexpr int kMinBlocksPerRange = 16;
+// V is streamed (non-temporal loads, tile::run) when the call's K and V
+// exceed twice the device's 256 MB last-level cache; a batch that fits keeps
+// its rows cached from one decode step to the next (Llama-3.2-1B batch, 257
+// MB: 53.0 us per call with the default policy, 54.0 streamed).
+constexpr long long kStreamVBytes = 512ll << 20;
 
 struct VerifyArgs {
   DecodeArgs a;       // with partitions: a.part_out [B, T, Hq, P_max, D], a.part_lse [B, T, Hq, P_max]
@@ -286,6 +291,7 @@ __global__ __launch_bounds__(64 * kMaxWpg) void verify_mfma_kernel(VerifyArgs va
   const int F0 = rng * per;
   if (F0 >= total) return;
   const int F1 = min(total, F0 + per);
+  const bool stream_v = (long long)total * kBS * a.Hkv * D * 4 > kStreamVBytes;
   int b;
   if constexpr (INL) {
     // the sequence holding block F0: largest b < B with prefix[b] <= F0
@@ -328,6 +334,10 @@ __global__ __launch_bounds__(64 * kMaxWpg) void verify_mfma_kernel(VerifyArgs va
                                 ((size_t)(b * a.T + t_row) * a.Hq + kv * G + (rq - t_row * G)) * D,
                       row_ok, lane);
       const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks;
+      // the neighbours' table entries at the same logical blocks (within
+      // their rows: js .. je - 1 < max_blocks); equal ids mark shared blocks
+      const int32_t* tprev = b > 0 ? trow - a.max_blocks + js : nullptr;
+      const int32_t* tnext = b + 1 < a.B ? trow + a.max_blocks + js : nullptr;
       float* piece = va.part + (size_t)(rng + b) * slot_floats;
       tile::State<D> st;
       tile::init(st);
@@ -367,12 +377,12 @@ __global__ __launch_bounds__(64 * kMaxWpg) void verify_mfma_kernel(VerifyArgs va
           tile::init(s);
         };
         tile::run<D, kTilePD>(st, qreg, hi_row, L, trow + js, js, je - js, nmax, kpool, vhead, kv_row_bytes,
-                                   block_bytes, vtile, scale_log2e, lane, PB, flush);
+                                   block_bytes, vtile, scale_log2e, lane, PB, flush, stream_v, tprev, tnext);
         flush(st, je);
         load_running<D>(st, run, mrun, lrun, lane);
       } else {
         tile::run<D, kTilePD>(st, qreg, hi_row, L, trow + js, js, je - js, nmax, kpool, vhead, kv_row_bytes,
-                                   block_bytes, vtile, scale_log2e, lane);
+                                   block_bytes, vtile, scale_log2e, lane, 0, tile::NoFlush(), stream_v, tprev, tnext);
       }
       emit_rows<D>(st, a, b, kv, G, R, direct,
                    [&](int t, int h) { return piece + ((size_t)t * a.Hq + h) * (D + 1); },
