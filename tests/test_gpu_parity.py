@@ -151,6 +151,23 @@ def test_llama8b_prefix_share_full(c4, part):
     check_lse(host(lse), ref_lse, f"llama8b part={part}")
 
 
+def test_llama8b_prefix_share_groups_not_adjacent(c4):
+    """The same batch with its sequences reordered so that the members of a
+    prefix group are 16 places apart: no sequence shares a block with its
+    neighbours, so the tile streams V of the shared prefixes too (a cache
+    hint only).  Every sequence against the oracle."""
+    w, d, (ref, ref_lse) = c4
+    perm = np.array([(i % 16) * 16 + i // 16 for i in range(w.B)])
+    assert len(set(perm.tolist())) == w.B
+    idx = torch.from_numpy(perm).cuda()
+    dp = dict(q=d["q"].index_select(0, idx).contiguous(), k=d["k"], v=d["v"],
+              tables=d["tables"].index_select(0, idx).contiguous(), lens=d["lens"].index_select(0, idx).contiguous())
+    say("decode llama8b_prefix_share, groups spread over the batch")
+    out, lse = run_decode(w, dp, partition_size=0)
+    check_attention(host(out), ref[perm], "bf16", "llama8b groups not adjacent", floor=mfma_floor(w))
+    check_lse(host(lse), ref_lse[perm], "llama8b groups not adjacent")
+
+
 @pytest.fixture(scope="module")
 def c5():
     """The long-context verify batch (16 sequences of 16K-64K tokens, T = 4),
