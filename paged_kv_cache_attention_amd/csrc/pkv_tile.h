@@ -283,9 +283,10 @@ __device__ __forceinline__ void run(State<D>& st, const u32x4_t (&qreg)[D / 32],
     cn = min(64, nb - c0);
     const int raw = lane < cn ? trow[c0 + lane] : -1;
     tbl = lane < cn ? clampi(raw, 0, nmax) : 0;
-    bool kp = !stream_v;
-    if (tprev) kp |= lane < cn && tprev[c0 + lane] == raw;
-    if (tnext) kp |= lane < cn && tnext[c0 + lane] == raw;
+    bool kp = true;
+    if (stream_v) {
+      kp = (tprev && lane < cn && tprev[c0 + lane] == raw) || (tnext && lane < cn && tnext[c0 + lane] == raw);
+    }
     keep = __builtin_amdgcn_ballot_w64(kp);
 #pragma unroll
     for (int s = 0; s < PD; ++s) load_kv(kbuf[s], vbuf[s], s);
