@@ -82,16 +82,21 @@ struct VerifyArgs {
 
 // Prefix sums over n counts (count(i) for i < n) into sp[0..n] by the whole
 // workgroup, kInlinePT consecutive entries per thread; returns the total.
-template <typename CountFn>
-__device__ __forceinline__ int inline_scan(int n, CountFn count, int* sp, int* wsc) {
+// count(i, raw) turns raw = load(min(i, n - 1)) into the count of entry i;
+// every thread loads its kInlinePT raw values first, unconditionally (n >= 1),
+// so that the loads are in flight together rather than one at a time.
+template <typename LoadFn, typename CountFn>
+__device__ __forceinline__ int inline_scan(int n, LoadFn load, CountFn count, int* sp, int* wsc) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), nw = blockDim.x >> 6;
   int nb[kInlinePT];
   int sum = 0;
 #pragma unroll
+  for (int j = 0; j < kInlinePT; ++j) nb[j] = load(min(tid * kInlinePT + j, n - 1));
+#pragma unroll
   for (int j = 0; j < kInlinePT; ++j) {
     const int i = tid * kInlinePT + j;
-    nb[j] = i < n ? count(i) : 0;
+    nb[j] = i < n ? count(i, nb[j]) : 0;
     sum += nb[j];
   }
   int is = sum;
@@ -127,8 +132,8 @@ __device__ __forceinline__ int verify_inline_plan(const VerifyArgs& va, int* sp,
   const DecodeArgs& a = va.a;
   const int tid = threadIdx.x;
   const int max_tokens = a.max_blocks * kBS;
-  const int total = inline_scan(a.B, [&](int b) { return (clampi(a.context_lens[b], 0, max_tokens) + kBS - 1) / kBS; },
-                                sp, wsc);
+  const int total = inline_scan(a.B, [&](int b) { return a.context_lens[b]; },
+                                [&](int, int L) { return (clampi(L, 0, max_tokens) + kBS - 1) / kBS; }, sp, wsc);
   for (int k = blockIdx.x * blockDim.x + tid; k <= a.B; k += gridDim.x * blockDim.x) va.prefix[k] = sp[k];
   if (blockIdx.x == 0 && tid == 0) {
     va.hdr[0] = total;
